@@ -1,0 +1,125 @@
+"""CPU checks of the seeded workloads and the roofline accounting, pinned to the pages' worked numbers."""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+from attention_paged_kv_amd import accounting as A
+from attention_paged_kv_amd import workloads as W
+
+GOLD = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "page_figures.json")))
+
+
+def test_kv_bytes_per_token_matches_page_examples():
+    for key in ("kv_bytes_per_token_32L_32kv_128d_fp16", "kv_bytes_per_token_32L_8kv_128d_fp16"):
+        g = GOLD[key]
+        assert A.kv_bytes_per_token(**g["args"]) == g["value"]
+    per_tok = A.kv_bytes_per_token(32, 8, 128, 2)
+    assert per_tok * 4096 == GOLD["kv_bytes_4k_context_8kv"]["value_bytes"]
+    assert per_tok * 128 * 1024 == GOLD["kv_bytes_128k_context_8kv"]["value_bytes"]
+    g = GOLD["kv_bytes_4096_ctx_batch32_32kv"]
+    per32 = A.kv_bytes_per_token(32, 32, 128, 2)
+    assert per32 * 4096 == g["printed_gb_per_request"] * 2 ** 30
+    assert per32 * 4096 * 32 == g["printed_gb_batch32"] * 2 ** 30
+
+
+def test_dense_attention_flops_match_page_examples():
+    for key in ("dense_attention_flops_7b_s2048", "dense_attention_flops_7b_s32768"):
+        g = GOLD[key]
+        got = A.dense_prefill_attention_flops(**g["args"])
+        assert abs(got - g["value"]) / g["value"] <= g["rel_tol"], (key, got)
+
+
+def test_causal_count_is_half_plus_diagonal_of_dense():
+    S, H, d = 8192, 32, 128
+    causal = A.attention_flops([S], [S], H, d)
+    assert causal == 4 * d * H * S * (S + 1) // 2
+    assert causal == 549_822_922_752      # 5.498e11 for the 8k prefill workload
+    # brute-force visible pair count on a tiny chunked case
+    q, s = 5, 12
+    brute = sum(1 for r in range(q) for j in range(s) if j <= s - q + r)
+    assert A.visible_pairs([q], [s]) == brute
+
+
+def test_block_and_chunk_arithmetic():
+    g = GOLD["blocks_for_4096_tokens"]
+    assert A.blocks_needed(g["args"]["num_tokens"], g["args"]["block_size"]) == g["value"]
+    g = GOLD["chunks_for_30k_prompt"]
+    assert math.ceil(g["args"]["prompt"] / g["args"]["chunk"]) == g["value"]
+    g = GOLD["cached_before_chunk_15"]
+    assert (g["args"]["chunk_index"] - 1) * g["args"]["chunk"] == g["value"]
+
+
+def test_config_shapes_without_values():
+    c2 = W.config2(values=False)
+    st = c2.steps[0]
+    assert st.num_seqs == 32 and np.all(st.q_lens == 1)
+    assert st.seq_lens.min() >= 512 and st.seq_lens.max() <= 4096
+    assert c2.num_blocks == 16384 and st.block_tables.shape == (32, 256)
+    c4 = W.config4(values=False)
+    st = c4.steps[0]
+    assert st.num_seqs == 31 and int(st.query_start_loc[-1]) == 2078
+    assert list(st.q_lens[:30]) == [1] * 30 and st.q_lens[30] == 2048
+    assert st.seq_lens[30] == 30720 and st.seq_lens[30] - st.q_lens[30] == GOLD["cached_before_chunk_15"]["value"]
+    assert st.block_tables.shape == (31, 1920)
+    c5 = W.config5(values=False)
+    st = c5.steps[0]
+    assert st.num_seqs == 16 and st.seq_lens.min() >= 3277 and st.seq_lens.max() <= 32768
+    assert st.block_tables.shape == (16, 2048)
+    c3 = W.config3(values=False)
+    assert c3.steps[0].block_tables.shape == (1, 512) and c3.num_blocks == 512
+
+
+@pytest.mark.parametrize("cfg", ["c2", "c4", "c5"])
+def test_slots_injective_and_tables_valid(cfg):
+    w = W.CONFIGS[cfg](values=False)
+    st = w.steps[0]
+    used = []
+    for b in range(st.num_seqs):
+        n = -(-int(st.seq_lens[b]) // 16)
+        row = st.block_tables[b]
+        assert np.all(row[:n] >= 0) and np.all(row[:n] < w.num_blocks)
+        assert np.all(row[n:] == -1)
+        used.append(row[:n])
+    used = np.concatenate(used)
+    assert len(np.unique(used)) == len(used)            # no physical block shared between requests
+    assert len(np.unique(st.slot_mapping)) == len(st.slot_mapping)
+
+
+def test_generation_is_deterministic_and_seeded():
+    a = W.make_batch(3, [40, 17], [40, 1], 2, 1, 64, "bf16")
+    b = W.make_batch(3, [40, 17], [40, 1], 2, 1, 64, "bf16")
+    c = W.make_batch(4, [40, 17], [40, 1], 2, 1, 64, "bf16")
+    assert np.array_equal(a.steps[0].q, b.steps[0].q) and np.array_equal(a.k_cache0, b.k_cache0)
+    assert not np.array_equal(a.steps[0].q, c.steps[0].q)
+
+
+def test_values_are_standard_normal_rounded_to_bf16():
+    w = W.make_batch(0, [4096], [4096], 4, 4, 128, "bf16", num_blocks=256)
+    x = W.to_float(w.steps[0].k_new, "bf16").astype(np.float64)
+    assert abs(x.mean()) < 0.01 and abs(x.std() - 1.0) < 0.01
+    # bf16 values widened then re-rounded are unchanged
+    assert np.array_equal(W.f32_to_bf16_bits(W.to_float(w.steps[0].k_new, "bf16")), w.steps[0].k_new)
+
+
+def test_poison_everywhere_but_live_context():
+    w = W.make_batch(1, [20, 35], [3, 35], 1, 1, 64, "f32", num_blocks=6)
+    st = w.steps[0]
+    live = set()
+    for b in range(2):
+        ctx = int(st.seq_lens[b] - st.q_lens[b])
+        live.update(W.slots_for(st.block_tables, b, np.arange(ctx)).tolist())
+    flat_v = w.v_cache0.reshape(-1, 64)
+    for s in range(flat_v.shape[0]):
+        assert np.isnan(flat_v[s]).all() != (s in live)
+
+
+def test_c1_steps():
+    w = W.config1()
+    assert len(w.steps) == 17 and w.dtype == "f32" and w.scale == 1.0 / 8
+    assert w.steps[0].num_tokens == 128 and int(w.steps[0].seq_lens[0]) == 128
+    for t in range(1, 17):
+        assert w.steps[t].num_tokens == 1 and int(w.steps[t].seq_lens[0]) == 128 + t
+    assert sorted(w.steps[0].block_tables[0].tolist()) == list(range(9))
