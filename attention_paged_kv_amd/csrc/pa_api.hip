@@ -1,0 +1,431 @@
+// pa_api.hip -- the C ABI declared in include/pa.h: argument validation on the host, workspace
+// layout, launch sequencing on the caller's stream, check mode, kernel timing and error text.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <mutex>
+#include <string>
+#include <unordered_map>
+#include <vector>
+
+#include "pa.h"
+#include "pa_internal.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+int device_fail(hipError_t e, const char* what) {
+  return fail(PA_ERR_DEVICE, "%s: %s", what, hipGetErrorString(e));
+}
+
+std::atomic<int> g_check{-1};
+bool check_on() {
+  int v = g_check.load();
+  if (v < 0) {
+    const char* e = std::getenv("PA_CHECK");
+    v = (e && e[0] == '1') ? 1 : 0;
+    int expected = -1;
+    g_check.compare_exchange_strong(expected, v);
+    v = g_check.load();
+  }
+  return v == 1;
+}
+
+int split_tokens() {
+  static int v = [] {
+    const char* e = std::getenv("PA_SPLIT_TOKENS");
+    int s = e ? std::atoi(e) : pa::kDefaultSplitTokens;
+    if (s < 16 || s % 16 != 0) s = pa::kDefaultSplitTokens;
+    return s;
+  }();
+  return v;
+}
+
+// ---- per-device state: library-owned workspace and the check-mode result slot ----
+struct DevState {
+  void* ws = nullptr;
+  size_t ws_bytes = 0;
+  int* check = nullptr;
+};
+std::mutex g_dev_mu;
+std::unordered_map<int, DevState> g_dev;
+
+// ---- kernel timing ----
+struct TimedLaunch {
+  std::string name;
+  hipEvent_t a, b;
+};
+std::mutex g_t_mu;
+bool g_timing = false;
+std::vector<TimedLaunch> g_pending;
+std::vector<hipEvent_t> g_event_pool;
+std::unordered_map<std::string, std::pair<double, int64_t>> g_t_acc;
+
+hipEvent_t take_event() {
+  if (!g_event_pool.empty()) {
+    hipEvent_t e = g_event_pool.back();
+    g_event_pool.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+template <class F>
+hipError_t timed(const char* name, hipStream_t s, F&& launch) {
+  std::unique_lock<std::mutex> lk(g_t_mu);
+  if (!g_timing) {
+    lk.unlock();
+    return launch();
+  }
+  hipEvent_t a = take_event(), b = take_event();
+  if (!a || !b) return hipErrorOutOfMemory;
+  hipEventRecord(a, s);
+  hipError_t e = launch();
+  hipEventRecord(b, s);
+  g_pending.push_back({name, a, b});
+  return e;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+// Where each piece of an attention call lives in the workspace, and what runs.
+struct Plan {
+  bool bf16 = false;
+  int head_dim = 0, group = 0, heads_per_wg = 0;
+  bool run_decode = false, run_tiles = false;
+  int rows = 0, per_token = 0, split = 0, max_splits = 0;
+  int pos_per_tile = 0, num_slots = 0;
+  size_t off_o = 0, off_ml = 0, off_tiles = 0, off_ntiles = 0, total = 0;
+};
+
+int validate_desc(const pa_cache_desc* c) {
+  if (!c) return fail(PA_ERR_INVALID_ARG, "cache descriptor is NULL");
+  if (c->block_size != PA_BLOCK_SIZE) return fail(PA_ERR_INVALID_ARG, "block_size must be 16 (got %d)", c->block_size);
+  if (c->num_blocks < 1) return fail(PA_ERR_INVALID_ARG, "num_blocks must be >= 1 (got %d)", c->num_blocks);
+  if (c->num_kv_heads < 1) return fail(PA_ERR_INVALID_ARG, "num_kv_heads must be >= 1 (got %d)", c->num_kv_heads);
+  if (c->dtype != PA_DTYPE_F32 && c->dtype != PA_DTYPE_BF16) return fail(PA_ERR_UNSUPPORTED, "unsupported dtype %d", c->dtype);
+  if (c->head_dim != 64 && c->head_dim != 128) return fail(PA_ERR_UNSUPPORTED, "head_dim must be 64 or 128 (got %d)", c->head_dim);
+  return PA_OK;
+}
+
+int make_plan(int32_t B, int32_t T, int32_t MB, int32_t Hq, const pa_cache_desc* c, Plan& p) {
+  int rc = validate_desc(c);
+  if (rc) return rc;
+  if (B < 1) return fail(PA_ERR_INVALID_ARG, "num_seqs must be >= 1 (got %d)", B);
+  if (T < B) return fail(PA_ERR_INVALID_ARG, "num_q_tokens (%d) < num_seqs (%d): every request needs q_len >= 1", T, B);
+  if (MB < 1) return fail(PA_ERR_INVALID_ARG, "max_blocks_per_seq must be >= 1 (got %d)", MB);
+  if ((int64_t)MB * PA_BLOCK_SIZE > (1 << 30)) return fail(PA_ERR_INVALID_ARG, "max_blocks_per_seq too large");
+  if (Hq < 1 || Hq % c->num_kv_heads != 0)
+    return fail(PA_ERR_INVALID_ARG, "num_q_heads (%d) must be a positive multiple of num_kv_heads (%d)", Hq, c->num_kv_heads);
+  p.bf16 = c->dtype == PA_DTYPE_BF16;
+  p.head_dim = c->head_dim;
+  p.group = Hq / c->num_kv_heads;
+  p.heads_per_wg = (p.group % 8 == 0) ? 8 : (p.group % 4 == 0) ? 4 : (p.group % 2 == 0) ? 2 : 1;
+  if (p.bf16 && p.group > pa::kTileRows)
+    return fail(PA_ERR_UNSUPPORTED, "query heads per KV head (%d) above %d", p.group, pa::kTileRows);
+  p.split = split_tokens();
+  p.max_splits = (int)(((int64_t)MB * PA_BLOCK_SIZE + p.split - 1) / p.split);
+  if (p.bf16) {
+    p.per_token = 0;
+    p.rows = B;
+    p.run_decode = !(B == 1 && T >= 2);          // some request may have q_len == 1
+    p.run_tiles = T > B;                         // some request has q_len >= 2
+    p.pos_per_tile = pa::kTileRows / p.group;
+    p.num_slots = (T + p.pos_per_tile - 1) / p.pos_per_tile + B;
+  } else {
+    p.per_token = 1;
+    p.rows = T;
+    p.run_decode = true;
+    p.run_tiles = false;
+  }
+  size_t off = 0;
+  if (p.run_decode && p.max_splits > 1) {
+    const size_t units = (size_t)p.rows * p.max_splits * Hq;
+    p.off_o = off;
+    off = align256(off + units * p.head_dim * sizeof(float));
+    p.off_ml = off;
+    off = align256(off + units * 2 * sizeof(float));
+  }
+  if (p.run_tiles) {
+    p.off_tiles = off;
+    off = align256(off + (size_t)p.num_slots * sizeof(int4));
+    p.off_ntiles = off;
+    off = align256(off + sizeof(int));
+  }
+  p.total = off;
+  const int64_t dec_grid = (int64_t)c->num_kv_heads * (p.group / p.heads_per_wg) * p.max_splits * p.rows;
+  if (p.run_decode && dec_grid > 0x7FFFFFFF) return fail(PA_ERR_UNSUPPORTED, "batch too large for one launch");
+  return PA_OK;
+}
+
+int get_device(int& dev) {
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return device_fail(e, "hipGetDevice");
+  return PA_OK;
+}
+
+int ensure_check_slot(int dev, int*& slot) {
+  std::lock_guard<std::mutex> lk(g_dev_mu);
+  DevState& st = g_dev[dev];
+  if (!st.check) {
+    hipError_t e = hipMalloc(&st.check, 4 * sizeof(int));
+    if (e != hipSuccess) return device_fail(e, "hipMalloc(check)");
+  }
+  slot = st.check;
+  return PA_OK;
+}
+
+int run_check(const pa::CheckArgs& base, hipStream_t s) {
+  int dev = 0;
+  int rc = get_device(dev);
+  if (rc) return rc;
+  int* slot = nullptr;
+  rc = ensure_check_slot(dev, slot);
+  if (rc) return rc;
+  pa::CheckArgs a = base;
+  a.result = slot;
+  hipError_t e = hipMemsetAsync(slot, 0, 4 * sizeof(int), s);
+  if (e != hipSuccess) return device_fail(e, "hipMemsetAsync(check)");
+  e = timed("check", s, [&] { return pa::launch_check(a, s); });
+  if (e != hipSuccess) return device_fail(e, "check kernel");
+  int host[4] = {0, 0, 0, 0};
+  e = hipMemcpyAsync(host, slot, sizeof host, hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return device_fail(e, "check readback");
+  if (!host[0]) return PA_OK;
+  static const char* what[] = {"", "slot outside the pool", "slot written twice", "query_start_loc[0] != 0",
+                               "query_start_loc[num_seqs] != num_q_tokens", "q_len < 1", "seq_len < q_len",
+                               "seq_len > max_blocks_per_seq*16", "block id outside [0, num_blocks)"};
+  const int code = host[1] >= 1 && host[1] <= 8 ? host[1] : 0;
+  return fail(PA_ERR_CHECK_FAILED, "check mode: %s (index %d, value %d)", what[code], host[2], host[3]);
+}
+
+}  // namespace
+
+extern "C" {
+
+int pa_abi_version(void) { return PA_ABI_VERSION; }
+
+const char* pa_last_error(void) { return g_err.c_str(); }
+
+void pa_set_check(int on) { g_check.store(on ? 1 : 0); }
+
+void pa_release(void) {
+  std::lock_guard<std::mutex> lk(g_dev_mu);
+  int cur = 0;
+  hipGetDevice(&cur);
+  for (auto& kv : g_dev) {
+    hipSetDevice(kv.first);
+    hipDeviceSynchronize();
+    if (kv.second.ws) hipFree(kv.second.ws);
+    if (kv.second.check) hipFree(kv.second.check);
+    kv.second = DevState{};
+  }
+  g_dev.clear();
+  hipSetDevice(cur);
+}
+
+int pa_append_kv(const void* k, const void* v, const int32_t* slot_mapping, int32_t num_tokens, void* k_cache,
+                 void* v_cache, const pa_cache_desc* cache, void* stream) {
+  g_err.clear();
+  int rc = validate_desc(cache);
+  if (rc) return rc;
+  if (num_tokens < 0) return fail(PA_ERR_INVALID_ARG, "num_tokens must be >= 0 (got %d)", num_tokens);
+  if (num_tokens == 0) return PA_OK;
+  if (!k || !v || !slot_mapping || !k_cache || !v_cache) return fail(PA_ERR_INVALID_ARG, "null pointer argument");
+  if (k_cache == v_cache) return fail(PA_ERR_INVALID_ARG, "k_cache and v_cache must differ");
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const int64_t esz = cache->dtype == PA_DTYPE_BF16 ? 2 : 4;
+  if (check_on()) {
+    pa::CheckArgs c{};
+    c.slot_mapping = slot_mapping;
+    c.num_tokens = num_tokens;
+    c.num_slots = (int64_t)cache->num_blocks * PA_BLOCK_SIZE;
+    rc = run_check(c, s);
+    if (rc) return rc;
+  }
+  pa::AppendArgs a{k, v, slot_mapping, k_cache, v_cache, num_tokens, (int64_t)cache->num_kv_heads * cache->head_dim * esz};
+  hipError_t e = timed("append", s, [&] { return pa::launch_append(a, s); });
+  if (e != hipSuccess) return device_fail(e, "append launch");
+  return PA_OK;
+}
+
+size_t pa_attention_workspace_size(int32_t num_seqs, int32_t num_q_tokens, int32_t max_blocks_per_seq,
+                                   int32_t num_q_heads, const pa_cache_desc* cache) {
+  Plan p;
+  std::string keep = g_err;
+  if (make_plan(num_seqs, num_q_tokens, max_blocks_per_seq, num_q_heads, cache, p) != PA_OK) {
+    g_err = keep;
+    return 0;
+  }
+  return p.total > 0 ? p.total : 256;
+}
+
+int pa_attention(const void* q, int32_t num_q_tokens, int32_t num_q_heads, const void* k_cache, const void* v_cache,
+                 const pa_cache_desc* cache, const int32_t* block_tables, int32_t num_seqs, int32_t max_blocks_per_seq,
+                 const int32_t* seq_lens, const int32_t* query_start_loc, float scale, void* out, void* workspace,
+                 size_t workspace_bytes, void* stream) {
+  g_err.clear();
+  Plan p;
+  int rc = make_plan(num_seqs, num_q_tokens, max_blocks_per_seq, num_q_heads, cache, p);
+  if (rc) return rc;
+  if (!q || !k_cache || !v_cache || !block_tables || !seq_lens || !query_start_loc || !out)
+    return fail(PA_ERR_INVALID_ARG, "null pointer argument");
+  if (out == q || out == k_cache || out == v_cache) return fail(PA_ERR_INVALID_ARG, "out must not alias inputs");
+  if (!std::isfinite(scale)) return fail(PA_ERR_INVALID_ARG, "scale must be finite");
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+
+  char* ws = static_cast<char*>(workspace);
+  if (p.total > 0) {
+    if (ws) {
+      if (workspace_bytes < p.total)
+        return fail(PA_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu needed", workspace_bytes, p.total);
+    } else {
+      int dev = 0;
+      rc = get_device(dev);
+      if (rc) return rc;
+      std::lock_guard<std::mutex> lk(g_dev_mu);
+      DevState& st = g_dev[dev];
+      if (st.ws_bytes < p.total) {
+        if (st.ws) {
+          hipDeviceSynchronize();
+          hipFree(st.ws);
+          st.ws = nullptr;
+          st.ws_bytes = 0;
+        }
+        hipError_t e = hipMalloc(&st.ws, p.total);
+        if (e != hipSuccess) return device_fail(e, "hipMalloc(workspace)");
+        st.ws_bytes = p.total;
+      }
+      ws = static_cast<char*>(st.ws);
+    }
+  }
+
+  if (check_on()) {
+    pa::CheckArgs c{};
+    c.block_tables = block_tables;
+    c.seq_lens = seq_lens;
+    c.qsl = query_start_loc;
+    c.num_seqs = num_seqs;
+    c.max_blocks = max_blocks_per_seq;
+    c.num_blocks = cache->num_blocks;
+    c.num_q_tokens = num_q_tokens;
+    rc = run_check(c, s);
+    if (rc) return rc;
+  }
+
+  const float scale_log2 = scale * 1.4426950408889634f;
+  if (p.run_decode) {
+    pa::DecodeArgs d{};
+    d.q = q;
+    d.k_cache = k_cache;
+    d.v_cache = v_cache;
+    d.block_tables = block_tables;
+    d.seq_lens = seq_lens;
+    d.qsl = query_start_loc;
+    d.out = out;
+    d.part_o = p.max_splits > 1 ? reinterpret_cast<float*>(ws + p.off_o) : nullptr;
+    d.part_ml = p.max_splits > 1 ? reinterpret_cast<float*>(ws + p.off_ml) : nullptr;
+    d.num_seqs = num_seqs;
+    d.num_rows = p.rows;
+    d.per_token = p.per_token;
+    d.num_q_heads = num_q_heads;
+    d.num_kv_heads = cache->num_kv_heads;
+    d.group = p.group;
+    d.heads_per_wg = p.heads_per_wg;
+    d.max_blocks = max_blocks_per_seq;
+    d.split = p.split;
+    d.max_splits = p.max_splits;
+    d.scale_log2 = scale_log2;
+    hipError_t e = timed("decode_split", s, [&] { return pa::launch_decode_split(d, p.head_dim, p.bf16, s); });
+    if (e != hipSuccess) return device_fail(e, "decode split launch");
+    if (p.max_splits > 1) {
+      e = timed("decode_merge", s, [&] { return pa::launch_decode_merge(d, p.head_dim, p.bf16, s); });
+      if (e != hipSuccess) return device_fail(e, "decode merge launch");
+    }
+  }
+  if (p.run_tiles) {
+    int4* tiles = reinterpret_cast<int4*>(ws + p.off_tiles);
+    int* ntiles = reinterpret_cast<int*>(ws + p.off_ntiles);
+    hipError_t e = timed("plan", s, [&] {
+      return pa::launch_plan_tiles(query_start_loc, num_seqs, p.pos_per_tile, tiles, ntiles, s);
+    });
+    if (e != hipSuccess) return device_fail(e, "plan launch");
+    pa::TileArgs t{};
+    t.q = q;
+    t.k_cache = k_cache;
+    t.v_cache = v_cache;
+    t.block_tables = block_tables;
+    t.seq_lens = seq_lens;
+    t.qsl = query_start_loc;
+    t.out = out;
+    t.tiles = tiles;
+    t.num_tiles = ntiles;
+    t.num_slots = p.num_slots;
+    t.num_q_heads = num_q_heads;
+    t.num_kv_heads = cache->num_kv_heads;
+    t.group = p.group;
+    t.pos_per_tile = p.pos_per_tile;
+    t.max_blocks = max_blocks_per_seq;
+    t.scale_log2 = scale_log2;
+    e = timed("prefill_tile", s, [&] { return pa::launch_prefill_tile(t, p.head_dim, s); });
+    if (e != hipSuccess) return device_fail(e, "prefill tile launch");
+  }
+  return PA_OK;
+}
+
+int pa_timing_enable(int on) {
+  std::lock_guard<std::mutex> lk(g_t_mu);
+  g_timing = on != 0;
+  return PA_OK;
+}
+
+int pa_timing_read(const char* name, double* total_ms, int64_t* launches) {
+  std::lock_guard<std::mutex> lk(g_t_mu);
+  for (auto& t : g_pending) {
+    hipError_t e = hipEventSynchronize(t.b);
+    float ms = 0.f;
+    if (e == hipSuccess) e = hipEventElapsedTime(&ms, t.a, t.b);
+    if (e != hipSuccess) return device_fail(e, "timing event");
+    auto& acc = g_t_acc[t.name];
+    acc.first += ms;
+    acc.second += 1;
+    g_event_pool.push_back(t.a);
+    g_event_pool.push_back(t.b);
+  }
+  g_pending.clear();
+  auto it = g_t_acc.find(name ? name : "");
+  if (total_ms) *total_ms = it == g_t_acc.end() ? 0.0 : it->second.first;
+  if (launches) *launches = it == g_t_acc.end() ? 0 : it->second.second;
+  return PA_OK;
+}
+
+void pa_timing_reset(void) {
+  std::lock_guard<std::mutex> lk(g_t_mu);
+  for (auto& t : g_pending) {
+    hipEventSynchronize(t.b);
+    g_event_pool.push_back(t.a);
+    g_event_pool.push_back(t.b);
+  }
+  g_pending.clear();
+  g_t_acc.clear();
+}
+
+}  // extern "C"

@@ -1,0 +1,104 @@
+// pa_append.hip -- KV append into the paged cache, and the check-mode index validator.
+//
+// Append: each new token's K and V rows (Hkv*d elements each) are copied bit for bit to the
+// cache slot given for it (P3 §2.3: only K and V are cached; P1 §2.2: written at the page
+// index).  With the position-major cache layout a token's row is contiguous in the cache, so
+// the scatter is a coalesced 16-byte-per-lane copy: consecutive lanes move consecutive 16-byte
+// pieces of the same row.
+#include "pa_common.h"
+#include "pa_internal.h"
+
+namespace pa {
+
+__global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
+  const int64_t per_row = a.row_bytes >> 4;                 // 16-byte pieces per token row
+  const int64_t total = a.num_tokens * per_row;
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; c < total; c += stride) {
+    const int64_t tok = c / per_row;
+    const int64_t piece = c - tok * per_row;
+    const int32_t slot = a.slot_mapping[tok];
+    if (slot < 0) continue;                                  // padding token
+    const int64_t src = tok * per_row + piece;
+    const int64_t dst = (int64_t)slot * per_row + piece;
+    const uint4 kv = reinterpret_cast<const uint4*>(a.k)[src];
+    const uint4 vv = reinterpret_cast<const uint4*>(a.v)[src];
+    reinterpret_cast<uint4*>(a.k_cache)[dst] = kv;
+    reinterpret_cast<uint4*>(a.v_cache)[dst] = vv;
+  }
+}
+
+hipError_t launch_append(const AppendArgs& a, hipStream_t s) {
+  const int64_t total = a.num_tokens * (a.row_bytes >> 4);
+  int64_t blocks = (total + 255) / 256;
+  if (blocks > 65536) blocks = 65536;
+  if (blocks < 1) blocks = 1;
+  append_kernel<<<dim3((unsigned)blocks), dim3(256), 0, s>>>(a);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------------------------------------
+// Check mode: validates the index arguments on the device before any data kernel runs.
+// result[0] = 1 once an error is recorded; result[1] = code; result[2] = index; result[3] = value.
+// ------------------------------------------------------------------------------------------
+__device__ void report(int* r, int code, int index, int value) {
+  if (atomicCAS(&r[0], 0, 1) == 0) {
+    r[1] = code;
+    r[2] = index;
+    r[3] = value;
+  }
+}
+
+__global__ __launch_bounds__(256) void check_kernel(CheckArgs a, unsigned* bitmap) {
+  const int tid = threadIdx.x + blockIdx.x * blockDim.x;
+  const int nthr = blockDim.x * gridDim.x;
+  if (a.slot_mapping) {
+    for (int i = tid; i < a.num_tokens; i += nthr) {
+      const int s = a.slot_mapping[i];
+      if (s < 0) continue;
+      if ((int64_t)s >= a.num_slots) { report(a.result, 1, i, s); continue; }
+      const unsigned bit = 1u << (s & 31);
+      const unsigned old = atomicOr(&bitmap[s >> 5], bit);
+      if (old & bit) report(a.result, 2, i, s);
+    }
+  }
+  if (a.block_tables) {
+    if (tid == 0) {
+      if (a.qsl[0] != 0) report(a.result, 3, 0, a.qsl[0]);
+      if (a.qsl[a.num_seqs] != a.num_q_tokens) report(a.result, 4, a.num_seqs, a.qsl[a.num_seqs]);
+    }
+    for (int b = tid; b < a.num_seqs; b += nthr) {
+      const int ql = a.qsl[b + 1] - a.qsl[b];
+      const int sl = a.seq_lens[b];
+      if (ql < 1) { report(a.result, 5, b, ql); continue; }
+      if (sl < ql) { report(a.result, 6, b, sl); continue; }
+      if (sl > a.max_blocks * kBlock) { report(a.result, 7, b, sl); continue; }
+      const int nb = (sl + kBlock - 1) / kBlock;
+      for (int j = 0; j < nb; ++j) {
+        const int blk = a.block_tables[(int64_t)b * a.max_blocks + j];
+        if (blk < 0 || blk >= a.num_blocks) { report(a.result, 8, b * a.max_blocks + j, blk); break; }
+      }
+    }
+  }
+}
+
+hipError_t launch_check(const CheckArgs& a, hipStream_t s) {
+  unsigned* bitmap = nullptr;
+  if (a.slot_mapping) {
+    const size_t words = (size_t)((a.num_slots + 31) / 32);
+    hipError_t e = hipMalloc(&bitmap, words * sizeof(unsigned));
+    if (e != hipSuccess) return e;
+    e = hipMemsetAsync(bitmap, 0, words * sizeof(unsigned), s);
+    if (e != hipSuccess) { hipFree(bitmap); return e; }
+  }
+  check_kernel<<<dim3(64), dim3(256), 0, s>>>(a, bitmap);
+  hipError_t e = hipGetLastError();
+  if (bitmap) {
+    hipError_t e2 = hipStreamSynchronize(s);
+    hipFree(bitmap);
+    if (e == hipSuccess) e = e2;
+  }
+  return e;
+}
+
+}  // namespace pa

@@ -1,0 +1,89 @@
+// pa_internal.h -- host-side launch interface between the C ABI layer and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pa {
+
+// Query rows with q_len == 1 (and, for fp32 caches, every query row) run on the split-KV
+// decode kernels; bf16 requests with q_len >= 2 run on the MFMA tile kernel.
+constexpr int kDefaultSplitTokens = 256;   // keys per decode split (multiple of 64)
+constexpr int kTileRows = 128;             // query rows (position x head-in-group) per MFMA tile
+constexpr int kTileKeys = 64;              // keys per MFMA K/V tile
+
+struct AppendArgs {
+  const void* k;
+  const void* v;
+  const int32_t* slot_mapping;
+  void* k_cache;
+  void* v_cache;
+  int64_t num_tokens;
+  int64_t row_bytes;      // Hkv * d * esz
+};
+
+struct DecodeArgs {
+  const void* q;
+  const void* k_cache;
+  const void* v_cache;
+  const int32_t* block_tables;
+  const int32_t* seq_lens;
+  const int32_t* qsl;
+  void* out;
+  float* part_o;          // [rows][max_splits][Hq][d]   unnormalised partial outputs
+  float* part_ml;         // [rows][max_splits][Hq][2]   (running max in log2 units, sum)
+  int num_seqs;
+  int num_rows;           // row slots: requests (bf16) or tokens (fp32)
+  int per_token;          // 1: row slot = token index; 0: row slot = request with q_len == 1
+  int num_q_heads;
+  int num_kv_heads;
+  int group;              // Hq / Hkv
+  int heads_per_wg;       // query heads of one group handled by one workgroup
+  int max_blocks;
+  int split;              // keys per split
+  int max_splits;
+  float scale_log2;       // scale * log2(e)
+};
+
+struct TileArgs {
+  const void* q;
+  const void* k_cache;
+  const void* v_cache;
+  const int32_t* block_tables;
+  const int32_t* seq_lens;
+  const int32_t* qsl;
+  void* out;
+  const int4* tiles;      // (request, first local row, rows in tile, unused)
+  const int* num_tiles;
+  int num_slots;          // upper bound on tiles launched per KV head
+  int num_q_heads;
+  int num_kv_heads;
+  int group;
+  int pos_per_tile;       // kTileRows / group
+  int max_blocks;
+  float scale_log2;
+};
+
+struct CheckArgs {
+  const int32_t* slot_mapping;   // append check (nullptr for attention)
+  int num_tokens;
+  int64_t num_slots;
+  const int32_t* block_tables;   // attention check (nullptr for append)
+  const int32_t* seq_lens;
+  const int32_t* qsl;
+  int num_seqs;
+  int max_blocks;
+  int num_blocks;
+  int num_q_tokens;
+  int* result;                   // [4]: flag, code, index, value (device, zeroed by caller)
+};
+
+hipError_t launch_append(const AppendArgs& a, hipStream_t s);
+hipError_t launch_decode_split(const DecodeArgs& a, int head_dim, bool bf16, hipStream_t s);
+hipError_t launch_decode_merge(const DecodeArgs& a, int head_dim, bool bf16, hipStream_t s);
+hipError_t launch_plan_tiles(const int32_t* qsl, int num_seqs, int pos_per_tile, int4* tiles, int* num_tiles,
+                             hipStream_t s);
+hipError_t launch_prefill_tile(const TileArgs& a, int head_dim, hipStream_t s);
+hipError_t launch_check(const CheckArgs& a, hipStream_t s);
+
+}  // namespace pa

@@ -43,7 +43,7 @@ def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
     """Round float32 values to bfloat16 (nearest, ties to even); returns uint16 bit patterns."""
     x = np.ascontiguousarray(x, dtype=np.float32)
     u = x.view(np.uint32)
-    r = ((u + np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))) >> np.uint32(16)).astype(np.uint16)
+    r = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
     nan = np.isnan(x)
     if nan.any():
         r[nan] = np.uint16(0x7FC0)
@@ -52,7 +52,7 @@ def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
 
 def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
     """Widen bfloat16 bit patterns to float32 (exact)."""
-    return (np.asarray(b, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
+    return (np.asarray(b, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
 
 
 def esize(dtype: str) -> int:
@@ -67,22 +67,40 @@ def to_storage(x: np.ndarray, dtype: str) -> np.ndarray:
     return np.ascontiguousarray(x, dtype=np.float32) if dtype == "f32" else f32_to_bf16_bits(x)
 
 
+_CHUNK = 1 << 24
+
+
+def normal_storage(rng: np.random.Generator, shape, dtype: str) -> np.ndarray:
+    """N(0,1) float32 draws in storage dtype.  Drawn in chunks (the stream is the same as one
+    draw of the whole array) so that bf16 rounding never touches full-size temporaries."""
+    n = int(np.prod(shape))
+    if dtype == "f32":
+        return rng.standard_normal(n, dtype=np.float32).reshape(shape)
+    out = np.empty(n, dtype=np.uint16)
+    for i in range(0, n, _CHUNK):
+        m = min(_CHUNK, n - i)
+        out[i:i + m] = f32_to_bf16_bits(rng.standard_normal(m, dtype=np.float32))
+    return out.reshape(shape)
+
+
 def to_float(x: np.ndarray, dtype: str) -> np.ndarray:
     """Storage array -> float32 view of the values it holds."""
     return np.asarray(x, dtype=np.float32) if dtype == "f32" else bf16_bits_to_f32(x)
 
 
 def poison_cache(shape, dtype: str, rng_sign: Optional[np.random.Generator] = None):
-    """Fresh K and V caches filled with poison: K = +-3e38 (alternating sign), V = NaN."""
-    n = int(np.prod(shape))
-    sign = np.where(np.arange(n, dtype=np.int64) % 2 == 0, 1.0, -1.0).astype(np.float32)
-    kpo = (sign * np.float32(K_POISON)).reshape(shape)
+    """Fresh K and V caches filled with poison: K = +-3e38 (sign alternating along d), V = NaN."""
+    d = shape[-1]
+    sign = np.where(np.arange(d) % 2 == 0, 1.0, -1.0).astype(np.float32)
+    krow = (sign * np.float32(K_POISON)).astype(np.float32)
+    kc = np.empty(shape, dtype=np_storage_dtype(dtype))
+    vc = np.empty(shape, dtype=np_storage_dtype(dtype))
     if dtype == "f32":
-        kc = kpo
-        vc = np.full(shape, np.nan, dtype=np.float32)
+        kc[...] = krow
+        vc[...] = np.float32(np.nan)
     else:
-        kc = f32_to_bf16_bits(kpo)
-        vc = np.full(shape, 0x7FC0, dtype=np.uint16)
+        kc[...] = f32_to_bf16_bits(krow)
+        vc[...] = np.uint16(0x7FC0)
     return kc, vc
 
 
@@ -196,9 +214,9 @@ def make_batch(seed: int, seq_lens: Sequence[int], q_lens: Sequence[int], num_q_
         return Workload(name=name, dtype=dtype, num_q_heads=Hq, num_kv_heads=Hkv, head_dim=d, num_blocks=NB,
                         scale=float(scale) if scale is not None else 1.0 / math.sqrt(d),
                         k_cache0=empty, v_cache0=empty, steps=[step], seed=seed, description=description)
-    q = to_storage(rng.standard_normal((T, Hq, d), dtype=np.float32), dtype)
-    K = to_storage(rng.standard_normal((L, Hkv, d), dtype=np.float32), dtype)
-    V = to_storage(rng.standard_normal((L, Hkv, d), dtype=np.float32), dtype)
+    q = normal_storage(rng, (T, Hq, d), dtype)
+    K = normal_storage(rng, (L, Hkv, d), dtype)
+    V = normal_storage(rng, (L, Hkv, d), dtype)
 
     kc, vc = poison_cache((NB, BLOCK_SIZE, Hkv, d), dtype)
     kc2 = kc.reshape(NB * BLOCK_SIZE, Hkv, d)

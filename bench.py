@@ -1,0 +1,239 @@
+#!/usr/bin/env python3
+"""Benchmark of the paged-attention hot path on one MI355X.
+
+A step is one pass of the whole path over one batch: append this step's K/V into the paged cache,
+then causal attention of every query row (decode splits + merge, and prefill/chunk tiles where
+the batch has them).  Inputs are seeded synthetic tensors already resident in HBM.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config c2|c3|c4|c5|c1] [--no-cpu-baseline]
+
+Prints one JSON line.  The default workload is the 32-request bf16 decode batch (32/32 heads,
+d=128, contexts U[512, 4096], 16384-block pool); its metric is KV-read GB/s.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "attn throughput: decode KV-read GB/s, prefill TFLOPS, % of roofline"
+HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2516.6
+FP32_VEC_PEAK_TFLOPS = 157.3
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def cpu_baseline(w, steps, is_decode, kv_bytes):
+    """Time the fp64 CPU oracle on the host cores over a bounded sample of the same workload.
+
+    Decode workloads (and the tiny fp32 sequence) run whole steps, repeated until ~10 s; prefill
+    workloads run a strided sample of query rows (all decode rows of a mixed batch are kept), and
+    the rate is the algorithmic FLOPs of the sampled rows over the oracle's time."""
+    import oracle
+    from attention_paged_kv_amd import accounting as A
+    threads = oracle.default_threads()
+    kcs, vcs = w.k_cache0.copy(), w.v_cache0.copy()
+    if is_decode or w.dtype == "f32":
+        reps, t_cpu = 0, 0.0
+        while t_cpu < 10.0 and reps < 50:
+            for st in steps:
+                ta = time.perf_counter()
+                oracle.run_step(w, st, kcs, vcs, num_threads=threads)
+                t_cpu += time.perf_counter() - ta
+            reps += 1
+        per = t_cpu / reps
+        if is_decode:
+            val, unit = kv_bytes / per / 1e9, "GB/s"
+        else:
+            fl = sum(A.attention_flops(st.q_lens, st.seq_lens, w.num_q_heads, w.head_dim) for st in steps)
+            val, unit = fl / per / 1e12, "TFLOP/s"
+        sample = f"whole {w.name} step (append + attention of every row), {reps} run(s), {per:.3f} s per step"
+    else:
+        st = steps[0]
+        ql = st.q_lens
+        rows, pos = [], []
+        for b in range(st.num_seqs):
+            q0, n = int(st.query_start_loc[b]), int(ql[b])
+            ctx = int(st.seq_lens[b]) - n
+            stride = 1 if n == 1 else 64
+            for r in range(0, n, stride):
+                rows.append(q0 + r)
+                pos.append(ctx + r)
+        rows = np.array(rows, np.int32)
+        fl = 4 * w.head_dim * w.num_q_heads * int(np.sum(np.array(pos, np.int64) + 1))
+        oracle.append(st.k_new, st.v_new, st.slot_mapping, kcs, vcs)
+        ta = time.perf_counter()
+        oracle.attention(st.q, kcs, vcs, st.block_tables, st.seq_lens, st.query_start_loc, w.scale, rows=rows,
+                         num_threads=threads)
+        per = time.perf_counter() - ta
+        val, unit = fl / per / 1e12, "TFLOP/s"
+        sample = (f"{len(rows)} of {st.num_tokens} query rows of {w.name} (every 64th prefill row, every decode "
+                  f"row), all heads, {per:.2f} s")
+    return {"value": round(val, 6), "unit": unit, "cores": threads, "kind": "oracle", "sample": sample}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", default="c2", choices=["c1", "c2", "c3", "c4", "c5"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on exactly one GPU: the hot path here is single-GPU (no collectives); "
+              "use --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import attention_paged_kv_amd as pa
+    from attention_paged_kv_amd import accounting as A
+    from attention_paged_kv_amd import workloads as W
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    pa.load_library()
+    dev = torch.device("cuda:0")
+
+    t0 = time.time()
+    w = W.CONFIGS[args.config]()
+    log(f"generated {w.name} in {time.time() - t0:.1f}s")
+    tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+
+    def to_dev(a):
+        a = np.ascontiguousarray(a)
+        if w.dtype == "bf16" and a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+        if a.dtype == np.int32:
+            return torch.from_numpy(a).to(dev)
+        return torch.from_numpy(a).to(dev)
+
+    # c1 is a 17-step sequence; its "step" is the whole sequence.  Others are one step.
+    steps = w.steps
+    kc = to_dev(w.k_cache0)
+    vc = to_dev(w.v_cache0)
+    dsteps = []
+    for st in steps:
+        dsteps.append(dict(q=to_dev(st.q), k=to_dev(st.k_new), v=to_dev(st.v_new),
+                           slots=to_dev(st.slot_mapping.astype(np.int32)), bt=to_dev(st.block_tables),
+                           sl=to_dev(st.seq_lens), qsl=to_dev(st.query_start_loc),
+                           out=torch.empty(st.q.shape, dtype=tdt, device=dev)))
+    ws_need = max(pa.workspace_size(st.num_seqs, st.num_tokens, st.block_tables.shape[1], w.num_q_heads, kc)
+                  for st in steps)
+    ws = torch.empty(max(ws_need, 256), dtype=torch.uint8, device=dev)
+
+    def run_step():
+        for d in dsteps:
+            pa.append_kv(d["k"], d["v"], d["slots"], kc, vc)
+            pa.attention(d["q"], kc, vc, d["bt"], d["sl"], d["qsl"], w.scale, d["out"], workspace=ws)
+
+    # algorithmic work of one step
+    kv_bytes = sum(A.kv_read_bytes(st.seq_lens, w.num_kv_heads, w.head_dim, w.esz) for st in steps)
+    flops = sum(A.attention_flops(st.q_lens, st.seq_lens, w.num_q_heads, w.head_dim) for st in steps)
+    decode_bytes = sum(A.kv_read_bytes(st.seq_lens[st.q_lens == 1], w.num_kv_heads, w.head_dim, w.esz)
+                       for st in steps)
+    tile_flops = sum(A.attention_flops(st.q_lens[st.q_lens > 1], st.seq_lens[st.q_lens > 1], w.num_q_heads,
+                                       w.head_dim) for st in steps)
+
+    for _ in range(args.warmup):
+        run_step()
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream(dev)
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        run_step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    gpu_ms = ev0.elapsed_time(ev1)
+    ms_per_step = 1e3 * wall / args.steps
+
+    # per-kernel durations from hipEvents the library records around its own launches (same stream)
+    pa.timing_reset()
+    pa.timing_enable(True)
+    for _ in range(args.steps):
+        run_step()
+    torch.cuda.synchronize()
+    kern = {}
+    for name in ("append", "decode_split", "decode_merge", "plan", "prefill_tile"):
+        ms, n = pa.timing_read(name)
+        if n:
+            kern[name] = {"avg_us": 1e3 * ms / n, "launches_per_step": n / args.steps}
+    pa.timing_enable(False)
+    pa.timing_reset()
+
+    is_decode = args.config in ("c2", "c5")
+    if is_decode:
+        unit = "GB/s"
+        value = kv_bytes / (ms_per_step * 1e-3) / 1e9
+        dk = kern["decode_split"]
+        per_launch = kv_bytes / dk["launches_per_step"]
+        achieved = per_launch / (dk["avg_us"] * 1e-6) / 1e9
+        roof = {"bound": "hbm", "kernel": "decode_split", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                "algorithmic_bytes_per_launch": int(per_launch)}
+    elif w.dtype == "f32":
+        unit = "TFLOP/s"
+        value = flops / (ms_per_step * 1e-3) / 1e12
+        dk = kern["decode_split"]
+        per_launch = flops / dk["launches_per_step"]
+        achieved = per_launch / (dk["avg_us"] * 1e-6) / 1e12
+        roof = {"bound": "alu", "kernel": "decode_split", "achieved": round(achieved, 4),
+                "peak": FP32_VEC_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / FP32_VEC_PEAK_TFLOPS, 6),
+                "traffic": None, "algorithmic_flops_per_launch": int(per_launch)}
+    else:
+        unit = "TFLOP/s"
+        value = flops / (ms_per_step * 1e-3) / 1e12
+        tk = kern["prefill_tile"]
+        per_launch = tile_flops / tk["launches_per_step"]
+        achieved = per_launch / (tk["avg_us"] * 1e-6) / 1e12
+        roof = {"bound": "mfma", "kernel": "prefill_tile", "achieved": round(achieved, 1),
+                "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / BF16_PEAK_TFLOPS, 4),
+                "traffic": None, "algorithmic_flops_per_launch": int(per_launch)}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(w, steps, is_decode, kv_bytes)
+
+    res = {
+        "metric": METRIC,
+        "value": round(value, 2 if unit == "GB/s" else 3),
+        "unit": unit,
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "gpu_ms_per_step": round(gpu_ms / args.steps, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": w.name, "description": w.description, "num_seqs": int(steps[0].num_seqs),
+                   "q_tokens": int(sum(st.num_tokens for st in steps)),
+                   "kv_read_bytes": int(kv_bytes), "flops": int(flops), "parallelism": "single-gpu"},
+        "kernels": {k: {kk: round(vv, 3) for kk, vv in v.items()} for k, v in kern.items()},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

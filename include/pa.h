@@ -1,0 +1,154 @@
+/*
+ * pa.h -- C ABI of libpa: causal self-attention over a 16-token-block paged KV cache on
+ * AMD MI355X (gfx950).  One call family serves decode, one-shot prefill and chunked prefill
+ * as a single varlen batch in which each request advances q_len tokens over its context.
+ *
+ * Sources, cited by page and section:
+ *   P1  "Prefill 和 Decode 不是两个步骤..." (lshu.cn/news/11576)
+ *   P2  "大模型推理性能优化：Prefill与Decode瓶颈及KV缓存显存管理" (wmrh.cn/news/64708)
+ *   P3  prefill/decode article on the page titled "企业官网建设流程全解析" (hotelren.com/news/6181127)
+ *   P4  "11. 分块预填充与统一调度" (niuwancheng.cn, llm-inference/11-chunked-prefill)
+ *
+ * Conventions for every entry point
+ *   - Pointers named as device pointers must be device memory of the current HIP device;
+ *     the library never frees or keeps them past the call (work already queued on `stream`
+ *     aside).  Host-struct pointers (pa_cache_desc) are read during the call only.
+ *   - `stream` is a hipStream_t passed as void*; NULL means the default stream.  Every call is
+ *     asynchronous on that stream and makes no host synchronisation, except in check mode.
+ *   - Return value: PA_OK (0) or a pa_status code.  On an error detected on the host nothing
+ *     is launched and no output is touched; pa_last_error() then describes it.  No C++
+ *     exception crosses this boundary.
+ *   - Cache layout (both caches, same descriptor):  [num_blocks][16][num_kv_heads][head_dim],
+ *     contiguous, element type `dtype`.  Token slot s lives at block s/16, offset s%16; one
+ *     token's K (or V) for all KV heads is one contiguous row of num_kv_heads*head_dim
+ *     elements.  Position-major rows are the layout P1 §3.2 reports as the faster one for
+ *     decode reads; they also make the append a contiguous row copy.
+ *   - Byte offsets are computed in 64 bits: a cache may exceed 2^31 bytes.
+ */
+#ifndef PA_H_
+#define PA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PA_ABI_VERSION 1
+#define PA_BLOCK_SIZE 16
+
+typedef enum {
+  PA_OK = 0,
+  PA_ERR_INVALID_ARG = 1,   /* null pointer, bad size or descriptor                        */
+  PA_ERR_UNSUPPORTED = 2,   /* valid but not implemented (head_dim, dtype, group size)     */
+  PA_ERR_DEVICE = 3,        /* a HIP call or launch failed; pa_last_error() has its text    */
+  PA_ERR_WORKSPACE = 4,     /* caller workspace smaller than pa_attention_workspace_size()  */
+  PA_ERR_CHECK_FAILED = 5   /* check mode found an invalid index in device-side arguments   */
+} pa_status;
+
+typedef enum { PA_DTYPE_F32 = 0, PA_DTYPE_BF16 = 1 } pa_dtype;
+
+/* Describes both caches.  block_size must be 16 (P1 §2.3: 16 tokens per block, a 4096-token
+ * prompt takes 256 blocks).  head_dim must be 64 or 128.  The same dtype is used for q, k, v,
+ * both caches and out. */
+typedef struct {
+  int32_t num_blocks;     /* NB: physical blocks in the pool                                */
+  int32_t block_size;     /* must be PA_BLOCK_SIZE                                          */
+  int32_t num_kv_heads;   /* Hkv                                                            */
+  int32_t head_dim;       /* d: 64 or 128                                                   */
+  int32_t dtype;          /* pa_dtype                                                       */
+} pa_cache_desc;
+
+/* ABI version compiled into the library; a binding must refuse to run if it differs from
+ * PA_ABI_VERSION (P1 §5.1 reports mismatched attention builds that silently return zeros). */
+int pa_abi_version(void);
+
+/* Text of the last error raised on the calling thread; valid until the next pa_* call on
+ * that thread.  Empty string if none. */
+const char* pa_last_error(void);
+
+/* Frees the library-owned workspaces of every device (those used when pa_attention gets a
+ * NULL workspace).  Synchronises the devices that own them. */
+void pa_release(void);
+
+/* Check mode: when on (or when the environment variable PA_CHECK=1 is set at the first call),
+ * pa_attention and pa_append_kv first run a validator kernel over the index arguments,
+ * synchronise `stream`, and return PA_ERR_CHECK_FAILED with the first offending index in
+ * pa_last_error() instead of launching with invalid indices.  Off by default. */
+void pa_set_check(int on);
+
+/*
+ * KV append -- P3 §2.3 (only K and V are cached, never Q), P1 §2.2 (each token's K/V are
+ * written at their page index), P3 §3.1 (a decode step appends its K/V before attending),
+ * P4 "把长输入切成块" (a prefill chunk writes its own K/V after reading the earlier ones).
+ *
+ *   k, v          device, [num_tokens][Hkv][d] contiguous, cache->dtype.  Must not alias the caches.
+ *   slot_mapping  device int32 [num_tokens]: destination slot of each token (block*16 + offset);
+ *                 a negative slot skips that token (padding).  Slots must lie in [0, NB*16) and be
+ *                 distinct; otherwise the result is undefined (check mode reports it).
+ *   k_cache,
+ *   v_cache       device, layout above; row `slot` of each is overwritten bit for bit, all other
+ *                 bytes are left untouched.
+ * num_tokens == 0 is a no-op returning PA_OK.
+ */
+int pa_append_kv(const void* k, const void* v, const int32_t* slot_mapping, int32_t num_tokens,
+                 void* k_cache, void* v_cache, const pa_cache_desc* cache, void* stream);
+
+/* Workspace bytes pa_attention needs for a batch of these sizes (an upper bound computed from
+ * the sizes alone; host-only, no device work).  Returns 0 for invalid sizes. */
+size_t pa_attention_workspace_size(int32_t num_seqs, int32_t num_q_tokens, int32_t max_blocks_per_seq,
+                                   int32_t num_q_heads, const pa_cache_desc* cache);
+
+/*
+ * Causal attention of a varlen batch over the paged cache -- P3 §2.1 (causal mask: position i
+ * sees keys 0..i; softmax over scaled scores; weights multiply V), P3 §3.1 and §5.1 (decode:
+ * q attends over all S+t cached keys after the append), P4 "一步的 token 预算" (each request
+ * advances q_len tokens per step: decode, prefill and chunked prefill are one operation),
+ * P3 §2.3 and §6.3 (grouped-query attention: Hq/Hkv query heads share one KV head).
+ *
+ * For request b: its query tokens are rows query_start_loc[b] .. query_start_loc[b+1]-1 of q;
+ * q_len = their count, ctx = seq_lens[b] - q_len; query row r (0-based within the request) sits
+ * at absolute position ctx + r and attends to keys 0 .. ctx + r, read through block_tables[b].
+ * Query head h uses KV head h / (Hq/Hkv).
+ *   out[t][h][:] = sum_j softmax_j(scale * <q[t][h], K[j][g]>) * V[j][g]
+ *
+ *   q                device [num_q_tokens][num_q_heads][d], cache->dtype.
+ *   k_cache, v_cache device, layout above (already holding this step's appended K/V).
+ *   block_tables     device int32 [num_seqs][max_blocks_per_seq]; entries past ceil(seq_len/16)
+ *                    are never read (any value).
+ *   seq_lens         device int32 [num_seqs]: keys visible to the request's last query token,
+ *                    this step's tokens included; 1 <= q_len <= seq_len <= max_blocks_per_seq*16.
+ *   query_start_loc  device int32 [num_seqs+1]: 0, then nondecreasing, ending at num_q_tokens;
+ *                    every request has q_len >= 1 (so num_q_tokens >= num_seqs).
+ *   scale            softmax scale (1/sqrt(d) for standard attention).
+ *   out              device [num_q_tokens][num_q_heads][d], cache->dtype; must not alias inputs.
+ *                    Accumulation is fp32 for both dtypes; bf16 output is rounded to nearest even.
+ *   workspace        device scratch of at least pa_attention_workspace_size() bytes, owned by
+ *                    the caller and not used concurrently by another call; NULL = use a
+ *                    library-owned per-device buffer (grown with hipMalloc, which synchronises).
+ * Device-side index errors (bad q_len/seq_len, block id outside [0, NB)) are undefined unless
+ * check mode is on.  num_q_heads must be a multiple of Hkv; for bf16, Hq/Hkv <= 128.
+ */
+int pa_attention(const void* q, int32_t num_q_tokens, int32_t num_q_heads,
+                 const void* k_cache, const void* v_cache, const pa_cache_desc* cache,
+                 const int32_t* block_tables, int32_t num_seqs, int32_t max_blocks_per_seq,
+                 const int32_t* seq_lens, const int32_t* query_start_loc, float scale, void* out,
+                 void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Measurement support (not part of the computation).  When timing is on, every kernel the
+ * library launches is bracketed by a pair of hipEvents recorded on the same stream.
+ * pa_timing_read() waits for the recorded events and returns, for the kernel family `name`
+ * ("append", "decode_split", "decode_merge", "plan", "prefill_tile", "check"), the summed
+ * duration in milliseconds and the number of launches since the last reset.
+ */
+int pa_timing_enable(int on);
+int pa_timing_read(const char* name, double* total_ms, int64_t* launches);
+void pa_timing_reset(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PA_H_ */

@@ -37,6 +37,15 @@ def _load():
     return _lib
 
 
+def default_threads() -> int:
+    """Host threads for the oracle: the CPUs this process may run on, at most 16."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except Exception:
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
 def _ptr(a):
     return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
 
@@ -86,7 +95,7 @@ def attention(q, k_cache, v_cache, block_tables, seq_lens, query_start_loc, scal
     out = np.zeros_like(q)
     out64 = np.zeros(q.shape, dtype=np.float64) if want_f64 else None
     rows_a = None if rows is None else np.ascontiguousarray(rows, dtype=np.int32)
-    nt = int(num_threads or os.cpu_count() or 1)
+    nt = int(num_threads or default_threads())
     err = ctypes.create_string_buffer(256)
     rc = lib.pa_oracle_attention(_ptr(q), T, Hq, _ptr(np.ascontiguousarray(k_cache)),
                                  _ptr(np.ascontiguousarray(v_cache)), NB, Hkv, d, dtype, _ptr(block_tables), B, MB,

@@ -1,0 +1,101 @@
+"""CPU checks of the C-ABI library: it loads, exports every symbol pa.h declares, and rejects bad
+arguments on the host before touching any device."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import attention_paged_kv_amd as pa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "pa.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(pa_[a-z_0-9]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(pa.LIB_PATH):
+        from attention_paged_kv_amd import build
+        build.build()
+    return pa.load_library()
+
+
+def test_header_declares_the_two_hot_path_calls():
+    names = declared_functions()
+    assert "pa_append_kv" in names and "pa_attention" in names
+    assert len(names) >= 10
+
+
+def test_library_exports_every_declared_symbol(lib):
+    raw = ctypes.CDLL(pa.LIB_PATH)
+    for name in declared_functions():
+        assert hasattr(raw, name), name
+
+
+def test_abi_version(lib):
+    assert lib.pa_abi_version() == pa.ABI_VERSION
+
+
+def _desc(nb=8, bs=16, hkv=2, d=128, dtype=1):
+    return pa._CacheDesc(nb, bs, hkv, d, dtype)
+
+
+def test_workspace_size_is_host_only_and_bounded(lib):
+    d = _desc()
+    assert lib.pa_attention_workspace_size(4, 4, 16, 8, ctypes.byref(d)) > 0
+    ws = lib.pa_attention_workspace_size(4, 4, 64, 8, ctypes.byref(d))
+    # 64 blocks = 1024 keys = several decode splits: rows x splits x heads x (d + 2) fp32 partials
+    assert ws >= 4 * 2 * 8 * 130 * 4
+    assert lib.pa_attention_workspace_size(0, 4, 16, 8, ctypes.byref(d)) == 0      # no requests
+    assert lib.pa_attention_workspace_size(4, 3, 16, 8, ctypes.byref(d)) == 0      # q_len < 1 somewhere
+    assert lib.pa_attention_workspace_size(4, 4, 16, 7, ctypes.byref(d)) == 0      # Hq % Hkv != 0
+    bad = _desc(bs=32)
+    assert lib.pa_attention_workspace_size(4, 4, 16, 8, ctypes.byref(bad)) == 0
+
+
+@pytest.mark.parametrize("field,val,code", [("block_size", 32, 1), ("head_dim", 96, 2), ("dtype", 7, 2),
+                                            ("num_blocks", 0, 1), ("num_kv_heads", 0, 1)])
+def test_bad_descriptor_rejected_before_launch(lib, field, val, code):
+    d = _desc()
+    setattr(d, field, val)
+    p = ctypes.c_void_p(16)   # never dereferenced: validation fails first
+    rc = lib.pa_attention(p, 4, 8, p, p, ctypes.byref(d), p, 4, 16, p, p, ctypes.c_float(0.1), p, None, 0, None)
+    assert rc == code
+    assert lib.pa_last_error()
+    rc = lib.pa_append_kv(p, p, p, 4, p, p, ctypes.byref(d), None)
+    assert rc == code
+
+
+def test_bad_sizes_rejected_before_launch(lib):
+    d = _desc()
+    p = ctypes.c_void_p(16)
+    assert lib.pa_attention(p, 4, 8, p, p, ctypes.byref(d), p, 0, 16, p, p, ctypes.c_float(1), p, None, 0, None) == 1
+    assert lib.pa_attention(p, 3, 8, p, p, ctypes.byref(d), p, 4, 16, p, p, ctypes.c_float(1), p, None, 0, None) == 1
+    assert lib.pa_attention(p, 4, 6, p, p, ctypes.byref(d), p, 4, 16, p, p, ctypes.c_float(1), p, None, 0, None) == 1
+    assert lib.pa_attention(None, 4, 8, p, p, ctypes.byref(d), p, 4, 16, p, p, ctypes.c_float(1), p, None, 0, None) == 1
+    assert lib.pa_attention(p, 4, 8, p, p, ctypes.byref(d), p, 4, 16, p, p, ctypes.c_float(float("inf")), p, None, 0,
+                            None) == 1
+    small = ctypes.c_void_p(256)
+    o = ctypes.c_void_p(48)
+    assert lib.pa_attention(p, 4, 8, p, p, ctypes.byref(d), p, 4, 16, p, p, ctypes.c_float(1), p, small, 8, None) == 1  # out aliases q
+    # 64 blocks per request -> split partials need workspace; an 8-byte one is refused before any launch
+    assert lib.pa_attention(p, 4, 8, p, p, ctypes.byref(d), p, 4, 64, p, p, ctypes.c_float(1), o, small, 8, None) == 4
+    assert b"workspace" in lib.pa_last_error()
+    assert lib.pa_append_kv(p, p, p, -1, p, p, ctypes.byref(d), None) == 1
+    assert lib.pa_append_kv(None, None, None, 0, None, None, ctypes.byref(d), None) == 0     # empty append
+
+
+def test_binding_fails_loudly_without_library(tmp_path):
+    with pytest.raises(ImportError):
+        saved = pa._lib
+        pa._lib = None
+        try:
+            pa.load_library(str(tmp_path / "missing.so"))
+        finally:
+            pa._lib = saved
