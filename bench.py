@@ -88,6 +88,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", default="c2", choices=["c1", "c2", "c3", "c4", "c5"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-ref-mib", type=int, default=0,
+                    help="instead of the hot path, time a plain device copy of this many MiB "
+                         "(reference kernel for scaling the HBM byte counters)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -106,6 +109,22 @@ def main():
         sys.exit(1)
     pa.load_library()
     dev = torch.device("cuda:0")
+
+    if args.copy_ref_mib:
+        n = args.copy_ref_mib << 20
+        src = torch.ones(n // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(args.warmup):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        dt = (time.perf_counter() - t0) / args.steps
+        print(json.dumps({"copy_ref_bytes_read": n, "copy_ref_bytes_written": n, "ms_per_copy": dt * 1e3,
+                          "GBps_read_plus_write": 2 * n / dt / 1e9}), flush=True)
+        return
 
     t0 = time.time()
     w = W.CONFIGS[args.config]()
