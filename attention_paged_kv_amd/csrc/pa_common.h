@@ -10,6 +10,7 @@ constexpr int kBlock = 16;       // tokens per cache block
 constexpr int kWave = 64;
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 
@@ -44,6 +45,33 @@ __device__ __forceinline__ float group_sum(float v) {
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Combine lane l with lane l ^ 32 (v_permlane32_swap: returns {x[l], x[l ^ 32]} in some order).
+__device__ __forceinline__ float xor32_max(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xor32_sum(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+// Combine lane l with lane l ^ 16 (v_permlane16_swap).
+__device__ __forceinline__ float xor16_max(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xor16_sum(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Transposed LDS read (ds_read_b64_tr_b16).  Within each 16-lane group, input lane 4e + c gives
+// the address of 4 consecutive elements of row e, columns 4c..4c+3 of a 4 x 16 tile; output lane
+// j receives column j of the tile: rows 0..3.
+typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4_t;
+__device__ __forceinline__ bf16x4 lds_read_tr(const uint16_t* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)(const __attribute__((address_space(3))) uint16_t*)p);
+}
 
 constexpr float kLog2e = 1.4426950408889634f;
 

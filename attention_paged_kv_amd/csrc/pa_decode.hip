@@ -1,48 +1,31 @@
 // pa_decode.hip -- split-KV attention for single query rows, and the cross-split merge.
 //
 // A decode step reads every cached key and value of its request once (P3 §3.1-3.2, §6.3): the
-// pass is bound by HBM bandwidth, not arithmetic.  Work unit = (query row, KV head, split of
-// `split` keys).  A workgroup loads each K/V row of its KV head once and uses it for all the
-// query heads of the group it owns (grouped-query sharing, P3 §2.3).  Inside the workgroup every
-// 16-lane row group keeps its own running max / sum / accumulator (online softmax over 16-key
-// blocks); the row groups and the four waves are merged at the end, and splits of one row are
-// merged by a second kernel with the same log-sum-exp rule:
+// pass is bound by HBM bandwidth, not arithmetic.  Work unit = (query row, KV head and a group of
+// its query heads, split of `split` keys).  A workgroup loads each K/V row of its KV head once and
+// uses it for all the query heads it owns (grouped-query sharing, P3 §2.3).  Each wave of the
+// workgroup streams every 4th 16-key block of the split with an online softmax; the four waves are
+// merged at the end, and the splits of one row are merged by a second kernel with
 //   m = max_s m_s,  l = sum_s 2^(m_s - m) l_s,  o = sum_s 2^(m_s - m) o_s / l
 // (scores are kept in log2 units: x * scale * log2 e).  The pages do not describe how partial
-// softmaxes are combined; this is the exact decomposition of the row softmax of P3 §3.1.
+// softmaxes combine; this is the exact decomposition of the row softmax of P3 §3.1.
+//
+// bf16 caches whose KV heads serve several query heads: matrix cores do the arithmetic so that
+// the vector ALUs stay idle however large the group.  Per 16-key block and wave:
+//   S^T (16 keys x 16 query heads) = K (16 x d) . Q^T   -- v_mfma_f32_16x16x32_bf16, K loaded
+//                                                          from HBM straight into A-operand lanes
+//   O^T (d x 16 heads) += V^T (d x 16 keys) . P^T       -- v_mfma_f32_16x16x16_bf16; V is staged
+//       row-major in a per-wave LDS block and read back transposed with ds_read_b64_tr_b16
+// P^T stays in registers: the S^T accumulator layout (lane = head, 4 keys) is exactly the B
+// operand layout of the second product.  Unused head columns are zero.
+// fp32 caches, and bf16 caches with one query head per KV head: vector-ALU kernel (dot products
+// reduced across 16-lane rows with DPP); for fp32 it serves every query row of the batch.
 #include "pa_common.h"
 #include "pa_internal.h"
 
 namespace pa {
 
 namespace {
-
-template <bool BF16>
-struct Io;
-
-template <>
-struct Io<true> {
-  static constexpr int kEsz = 2;
-  static constexpr int kEpl = 8;   // elements per 16-byte load
-  __device__ static void widen(const uint4& u, float* f) {
-    f[0] = bf16_lo(u.x); f[1] = bf16_hi(u.x); f[2] = bf16_lo(u.y); f[3] = bf16_hi(u.y);
-    f[4] = bf16_lo(u.z); f[5] = bf16_hi(u.z); f[6] = bf16_lo(u.w); f[7] = bf16_hi(u.w);
-  }
-  __device__ static void store(void* base, int64_t idx, float v) {
-    reinterpret_cast<uint16_t*>(base)[idx] = f32_to_bf16(v);
-  }
-};
-
-template <>
-struct Io<false> {
-  static constexpr int kEsz = 4;
-  static constexpr int kEpl = 4;
-  __device__ static void widen(const uint4& u, float* f) {
-    f[0] = __uint_as_float(u.x); f[1] = __uint_as_float(u.y);
-    f[2] = __uint_as_float(u.z); f[3] = __uint_as_float(u.w);
-  }
-  __device__ static void store(void* base, int64_t idx, float v) { reinterpret_cast<float*>(base)[idx] = v; }
-};
 
 // Resolve a row slot to (request, token, visible keys).  Returns false if the slot is not a
 // row of this pass (bf16 requests with q_len != 1 go to the tile kernel).
@@ -75,10 +58,241 @@ __device__ __forceinline__ float wave_sum_over_groups(float v, int lpr) {
   return v;
 }
 
+template <bool BF16>
+struct Io;
+
+template <>
+struct Io<true> {
+  static constexpr int kEsz = 2;
+  static constexpr int kEpl = 8;   // elements per 16-byte load
+  __device__ static void widen(const uint4& u, float* f) {
+    f[0] = bf16_lo(u.x); f[1] = bf16_hi(u.x); f[2] = bf16_lo(u.y); f[3] = bf16_hi(u.y);
+    f[4] = bf16_lo(u.z); f[5] = bf16_hi(u.z); f[6] = bf16_lo(u.w); f[7] = bf16_hi(u.w);
+  }
+  __device__ static void store(void* base, int64_t idx, float v) {
+    reinterpret_cast<uint16_t*>(base)[idx] = f32_to_bf16(v);
+  }
+};
+
+template <>
+struct Io<false> {
+  static constexpr int kEsz = 4;
+  static constexpr int kEpl = 4;
+  __device__ static void widen(const uint4& u, float* f) {
+    f[0] = __uint_as_float(u.x); f[1] = __uint_as_float(u.y);
+    f[2] = __uint_as_float(u.z); f[3] = __uint_as_float(u.w);
+  }
+  __device__ static void store(void* base, int64_t idx, float v) { reinterpret_cast<float*>(base)[idx] = v; }
+};
+
+struct Unit {
+  int row, b, t, n_keys, split, k0, k1, n_splits, g, h0, ncols;
+};
+
+// Decode the workgroup index into its unit.  Head-group index is fastest so that neighbouring
+// workgroups read neighbouring runs of the same token rows.
+__device__ __forceinline__ bool get_unit(const DecodeArgs& a, int nzh, Unit& u) {
+  const int nz = a.num_kv_heads * nzh;
+  int i = blockIdx.x;
+  const int z = i % nz;
+  i /= nz;
+  u.split = i % a.max_splits;
+  u.row = i / a.max_splits;
+  if (u.row >= a.num_rows) return false;
+  if (!resolve_row(a, u.row, u.b, u.t, u.n_keys)) return false;
+  u.k0 = u.split * a.split;
+  if (u.k0 >= u.n_keys) return false;
+  u.k1 = min(u.k0 + a.split, u.n_keys);
+  u.n_splits = (u.n_keys + a.split - 1) / a.split;
+  u.g = z / nzh;
+  const int zh = z % nzh;
+  u.h0 = u.g * a.group + zh * a.heads_per_wg;
+  u.ncols = min(a.heads_per_wg, a.group - zh * a.heads_per_wg);
+  return true;
+}
+
 }  // namespace
 
+// ------------------------------------------------------------------------------------------
+// bf16: matrix-core split kernel.  NCOL = query-head columns held (power of two >= ncols).
+// ------------------------------------------------------------------------------------------
+template <int D, int NCOL>
+__global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
+  constexpr int NKK = D / 32;                 // 16x16x32 k-steps over d for S^T
+  constexpr int NT = D / 16;                  // 16-row d tiles of O^T
+  constexpr int VS = D + 16;                  // LDS row stride (elements) of a staged V block
+  constexpr int VBYTES = 4 * kBlock * VS * 2;
+  constexpr int OBYTES = 4 * NCOL * (D + 2) * 4;
+  constexpr int SMEM = VBYTES > OBYTES ? VBYTES : OBYTES;
+  __shared__ __align__(16) char smem[SMEM];
+
+  Unit u;
+  if (!get_unit(a, (a.group + a.heads_per_wg - 1) / a.heads_per_wg, u)) return;
+
+  const int lane = threadIdx.x & (kWave - 1);
+  const int w = threadIdx.x >> 6;
+  const int col = lane & 15;                  // S^T / O^T column = query head; also the K/V row loaded
+  const int grp = lane >> 4;                  // 4-key group of the accumulator layout
+  const float c = a.scale_log2;
+
+  // Q^T as the B operand: lane holds d = 32kk + 8grp .. +8 of head h0 + col
+  bf16x8 qb[NKK];
+  {
+    const bool on = col < u.ncols;
+    const char* qp = reinterpret_cast<const char*>(a.q) +
+                     (((int64_t)u.t * a.num_q_heads + u.h0 + (on ? col : 0)) * D + 8 * grp) * 2;
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) {
+      uint4 v = on ? *reinterpret_cast<const uint4*>(qp + kk * 64) : make_uint4(0, 0, 0, 0);
+      qb[kk] = __builtin_bit_cast(bf16x8, v);
+    }
+  }
+
+  uint16_t* vs = reinterpret_cast<uint16_t*>(smem) + w * kBlock * VS;
+  const int64_t rs = (int64_t)a.num_kv_heads * D;            // elements per cache token row
+  const char* kbase = reinterpret_cast<const char*>(a.k_cache) + ((int64_t)u.g * D + 8 * grp) * 2;
+  const char* vbase = reinterpret_cast<const char*>(a.v_cache) + ((int64_t)u.g * D + 8 * grp) * 2;
+  const int32_t* table = a.block_tables + (int64_t)u.b * a.max_blocks;
+  const int kb0 = u.k0 / kBlock;
+  const int kb1 = (u.k1 + kBlock - 1) / kBlock;
+
+  float m = -INFINITY, lsum = 0.f;
+  floatx4 O[NT];
+#pragma unroll
+  for (int tt = 0; tt < NT; ++tt) O[tt] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+  auto load = [&](int blk, uint4* kr, uint4* vr) {
+    const int64_t off = (((int64_t)table[blk] * kBlock + col) * rs) * 2;
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) {
+      kr[kk] = *reinterpret_cast<const uint4*>(kbase + off + kk * 64);
+      vr[kk] = *reinterpret_cast<const uint4*>(vbase + off + kk * 64);
+    }
+  };
+
+  auto consume = [&](int blk, const uint4* kr, const uint4* vr) {
+    floatx4 s = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk)
+      s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kr[kk]), qb[kk], s, 0, 0, 0);
+    const int kbase_idx = blk * kBlock;
+    const bool partial = kbase_idx + kBlock > u.k1;
+    // stage V (row = key `col`), zeroing rows past the last visible key
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) {
+      uint4 v = vr[kk];
+      if (partial && kbase_idx + col >= u.k1) v = make_uint4(0, 0, 0, 0);
+      *reinterpret_cast<uint4*>(&vs[col * VS + 32 * kk + 8 * grp]) = v;
+    }
+    if (partial) {
+#pragma unroll
+      for (int v = 0; v < 4; ++v)
+        if (kbase_idx + 4 * grp + v >= u.k1) s[v] = -INFINITY;
+    }
+    float bm = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
+    bm = fmaxf(bm, __shfl_xor(bm, 16));
+    bm = fmaxf(bm, __shfl_xor(bm, 32));
+    const float mn = fmaxf(m, bm);
+    const float alpha = (m == -INFINITY) ? 0.f : fast_exp2((m - mn) * c);
+    const float mc = mn * c;
+    float p[4];
+#pragma unroll
+    for (int v = 0; v < 4; ++v) p[v] = fast_exp2(fmaf(s[v], c, -mc));
+    lsum = lsum * alpha + ((p[0] + p[1]) + (p[2] + p[3]));
+    m = mn;
+    bf16x4 pb;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) pb[v] = (__bf16)p[v];
+#pragma unroll
+    for (int tt = 0; tt < NT; ++tt) O[tt] *= alpha;
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    // transpose read: lane (grp, j) addresses row 4grp + j/4, columns 16tt + 4(j%4) .. +4
+    typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+    const __attribute__((address_space(3))) uint16_t* vl =
+        (const __attribute__((address_space(3))) uint16_t*)(vs + (4 * grp + (col >> 2)) * VS + 4 * (col & 3));
+#pragma unroll
+    for (int tt = 0; tt < NT; ++tt) {
+      const bf16x4 vt = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(vl + 16 * tt));
+      O[tt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vt, pb, O[tt], 0, 0, 0);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  };
+
+  {
+    uint4 kA[NKK], vA[NKK], kB[NKK], vB[NKK];
+    int blk = kb0 + w;
+    if (blk < kb1) load(blk, kA, vA);
+    while (blk < kb1) {
+      int nb = blk + 4;
+      if (nb < kb1) load(nb, kB, vB);
+      consume(blk, kA, vA);
+      blk = nb;
+      if (blk >= kb1) break;
+      nb = blk + 4;
+      if (nb < kb1) load(nb, kA, vA);
+      consume(blk, kB, vB);
+      blk = nb;
+    }
+  }
+  lsum += __shfl_xor(lsum, 16);
+  lsum += __shfl_xor(lsum, 32);
+
+  // merge the four waves through LDS (reusing the V staging space)
+  __syncthreads();
+  float* so = reinterpret_cast<float*>(smem);                 // [4][NCOL][D]
+  float* sml = so + 4 * NCOL * D;                             // [4][NCOL][2]
+  if (col < NCOL) {
+#pragma unroll
+    for (int tt = 0; tt < NT; ++tt)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) so[(w * NCOL + col) * D + 16 * tt + 4 * grp + v] = O[tt][v];
+    if (grp == 0) {
+      sml[(w * NCOL + col) * 2] = m;
+      sml[(w * NCOL + col) * 2 + 1] = lsum;
+    }
+  }
+  __syncthreads();
+  for (int idx = threadIdx.x; idx < u.ncols * D; idx += blockDim.x) {
+    const int cc = idx / D;
+    const int dd = idx - cc * D;
+    float mm = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) mm = fmaxf(mm, sml[(i * NCOL + cc) * 2]);
+    float ll = 0.f, o = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float mi = sml[(i * NCOL + cc) * 2];
+      const float f = (mi == -INFINITY) ? 0.f : fast_exp2((mi - mm) * c);
+      ll += sml[(i * NCOL + cc) * 2 + 1] * f;
+      o += so[(i * NCOL + cc) * D + dd] * f;
+    }
+    const int h = u.h0 + cc;
+    if (u.n_splits == 1) {
+      reinterpret_cast<uint16_t*>(a.out)[((int64_t)u.t * a.num_q_heads + h) * D + dd] = f32_to_bf16(o / ll);
+    } else {
+      const int64_t pidx = ((int64_t)u.row * a.max_splits + u.split) * a.num_q_heads + h;
+      a.part_o[pidx * D + dd] = o;
+      if (dd == 0) {
+        a.part_ml[pidx * 2] = mm * c;     // log2 units
+        a.part_ml[pidx * 2 + 1] = ll;
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------------------------------------------
+// Vector-ALU split kernel: fp32 caches, and bf16 caches whose KV heads serve a single query
+// head (no grouped sharing to amortise, so matrix cores would leave 15 of 16 columns idle).
+// GT query heads per workgroup (GT divides the group size).  Each K/V row is read by a 16-lane
+// (bf16, d=128) row group with 16-byte loads; q.k is reduced across the group with DPP, and every
+// row group keeps its own running max / sum / accumulator.
+// ------------------------------------------------------------------------------------------
 template <int D, int GT, bool BF16>
-__global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(256) void decode_valu_kernel(DecodeArgs a) {
   using IO = Io<BF16>;
   constexpr int EPL = IO::kEpl;
   constexpr int LPR = D * IO::kEsz / 16;     // lanes per K/V row
@@ -90,32 +304,17 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
   __shared__ float sm_l[4][GT];
   __shared__ float sm_o[4][GT][D];
 
+  Unit u;
+  if (!get_unit(a, a.group / GT, u)) return;
   const int lane = threadIdx.x & (kWave - 1);
   const int w = threadIdx.x >> 6;
   const int rg = lane / LPR;                 // row group within the wave
   const int cl = lane % LPR;                 // which 16-byte piece of the row
 
-  const int nz = a.num_kv_heads * (a.group / GT);
-  int u = blockIdx.x;
-  const int z = u % nz;
-  u /= nz;
-  const int split = u % a.max_splits;
-  const int row = u / a.max_splits;
-  if (row >= a.num_rows) return;
-  int b, t, n_keys;
-  if (!resolve_row(a, row, b, t, n_keys)) return;
-  const int k0 = split * a.split;
-  if (k0 >= n_keys) return;
-  const int k1 = min(k0 + a.split, n_keys);
-  const int n_splits = (n_keys + a.split - 1) / a.split;
-  const int g = z / (a.group / GT);
-  const int h0 = g * a.group + (z % (a.group / GT)) * GT;
-
-  // query heads of this workgroup, pre-scaled into log2 units
   float qf[GT][EPL];
 #pragma unroll
   for (int hh = 0; hh < GT; ++hh) {
-    const int64_t qoff = ((int64_t)t * a.num_q_heads + h0 + hh) * D + cl * EPL;
+    const int64_t qoff = ((int64_t)u.t * a.num_q_heads + u.h0 + hh) * D + cl * EPL;
     const uint4 qv = *reinterpret_cast<const uint4*>(reinterpret_cast<const char*>(a.q) + qoff * IO::kEsz);
     IO::widen(qv, qf[hh]);
 #pragma unroll
@@ -132,15 +331,14 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
   }
 
   const int64_t rs = (int64_t)a.num_kv_heads * D;          // elements per token row
-  const char* kbase = reinterpret_cast<const char*>(a.k_cache) + ((int64_t)g * D + cl * EPL) * IO::kEsz;
-  const char* vbase = reinterpret_cast<const char*>(a.v_cache) + ((int64_t)g * D + cl * EPL) * IO::kEsz;
-  const int32_t* table = a.block_tables + (int64_t)b * a.max_blocks;
-  const int kb0 = k0 / kBlock;
-  const int kb1 = (k1 + kBlock - 1) / kBlock;
+  const char* kbase = reinterpret_cast<const char*>(a.k_cache) + ((int64_t)u.g * D + cl * EPL) * IO::kEsz;
+  const char* vbase = reinterpret_cast<const char*>(a.v_cache) + ((int64_t)u.g * D + cl * EPL) * IO::kEsz;
+  const int32_t* table = a.block_tables + (int64_t)u.b * a.max_blocks;
+  const int kb0 = u.k0 / kBlock;
+  const int kb1 = (u.k1 + kBlock - 1) / kBlock;
 
   auto load_block = [&](int blk, uint4* kr, uint4* vr) {
-    const int64_t phys = table[blk];
-    const int64_t base = phys * kBlock * rs;
+    const int64_t base = (int64_t)table[blk] * kBlock * rs;
 #pragma unroll
     for (int r = 0; r < LPB; ++r) {
       const int64_t off = (base + (int64_t)(r * RPL + rg) * rs) * IO::kEsz;
@@ -164,12 +362,12 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
       }
     }
     const int key0 = blk * kBlock + rg;
-    const bool full = (blk + 1) * kBlock <= k1;
+    const bool full = (blk + 1) * kBlock <= u.k1;
     float vf[LPB][EPL];
 #pragma unroll
     for (int r = 0; r < LPB; ++r) {
       IO::widen(vr[r], vf[r]);
-      if (!full && key0 + r * RPL >= k1) {
+      if (!full && key0 + r * RPL >= u.k1) {
 #pragma unroll
         for (int e = 0; e < EPL; ++e) vf[r][e] = 0.f;      // slots past the last visible key
 #pragma unroll
@@ -241,11 +439,11 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
       ll += sm_l[i][hh] * f;
       o += sm_o[i][hh][dd] * f;
     }
-    const int h = h0 + hh;
-    if (n_splits == 1) {
-      IO::store(a.out, ((int64_t)t * a.num_q_heads + h) * D + dd, o / ll);
+    const int h = u.h0 + hh;
+    if (u.n_splits == 1) {
+      IO::store(a.out, ((int64_t)u.t * a.num_q_heads + h) * D + dd, o / ll);
     } else {
-      const int64_t pidx = ((int64_t)row * a.max_splits + split) * a.num_q_heads + h;
+      const int64_t pidx = ((int64_t)u.row * a.max_splits + u.split) * a.num_q_heads + h;
       a.part_o[pidx * D + dd] = o;
       if (dd == 0) {
         a.part_ml[pidx * 2] = mm;
@@ -255,47 +453,108 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
   }
 }
 
+// ------------------------------------------------------------------------------------------
+// Cross-split merge: one workgroup per (row, query head); splits are read in parallel.
+// ------------------------------------------------------------------------------------------
 template <int D, bool BF16>
-__global__ __launch_bounds__(64) void decode_merge_kernel(DecodeArgs a) {
-  using IO = Io<BF16>;
+__global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a) {
+  constexpr int CH = D / 4;                  // float4 chunks of a row
+  constexpr int NG = 256 / CH;               // split groups
+  constexpr int WCAP = 1024;                 // splits whose weights are kept in LDS
+  __shared__ float sw[WCAP];
+  __shared__ float red[256 / kWave];
+  __shared__ float4 racc[NG][CH];
+  __shared__ float s_m, s_l;
+
   const int row = blockIdx.x / a.num_q_heads;
   const int h = blockIdx.x % a.num_q_heads;
   int b, t, n_keys;
   if (!resolve_row(a, row, b, t, n_keys)) return;
-  const int n_splits = (n_keys + a.split - 1) / a.split;
-  if (n_splits <= 1) return;                                // written directly by the split kernel
+  const int n = (n_keys + a.split - 1) / a.split;
+  if (n <= 1) return;                                       // written directly by the split kernel
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1), w = tid >> 6;
   const int64_t pbase = (int64_t)row * a.max_splits * a.num_q_heads + h;
-  float mm = -INFINITY;
-  for (int s = 0; s < n_splits; ++s) mm = fmaxf(mm, a.part_ml[(pbase + (int64_t)s * a.num_q_heads) * 2]);
-  float o[D / 64];
-#pragma unroll
-  for (int i = 0; i < D / 64; ++i) o[i] = 0.f;
-  float ll = 0.f;
-  for (int s = 0; s < n_splits; ++s) {
-    const int64_t p = pbase + (int64_t)s * a.num_q_heads;
-    const float f = fast_exp2(a.part_ml[p * 2] - mm);
-    ll += a.part_ml[p * 2 + 1] * f;
-#pragma unroll
-    for (int i = 0; i < D / 64; ++i) o[i] = fmaf(a.part_o[p * D + threadIdx.x + 64 * i], f, o[i]);
+  const float* ml = a.part_ml;
+
+  float mx = -INFINITY;
+  for (int s = tid; s < n; s += 256) mx = fmaxf(mx, ml[(pbase + (int64_t)s * a.num_q_heads) * 2]);
+  for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+  if (lane == 0) red[w] = mx;
+  __syncthreads();
+  if (tid == 0) s_m = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  __syncthreads();
+  const float M = s_m;
+  float ls = 0.f;
+  for (int s = tid; s < n; s += 256) {
+    const int64_t p = (pbase + (int64_t)s * a.num_q_heads) * 2;
+    const float wgt = fast_exp2(ml[p] - M);
+    if (s < WCAP) sw[s] = wgt;
+    ls = fmaf(wgt, ml[p + 1], ls);
   }
-  const float inv = 1.f / ll;
-#pragma unroll
-  for (int i = 0; i < D / 64; ++i)
-    IO::store(a.out, ((int64_t)t * a.num_q_heads + h) * D + threadIdx.x + 64 * i, o[i] * inv);
+  for (int o = 32; o > 0; o >>= 1) ls += __shfl_xor(ls, o);
+  __syncthreads();
+  if (lane == 0) red[w] = ls;
+  __syncthreads();
+  if (tid == 0) s_l = (red[0] + red[1]) + (red[2] + red[3]);
+  __syncthreads();
+
+  const int cidx = tid % CH, gidx = tid / CH;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll 4
+  for (int s = gidx; s < n; s += NG) {
+    const int64_t p = pbase + (int64_t)s * a.num_q_heads;
+    const float wgt = s < WCAP ? sw[s] : fast_exp2(ml[p * 2] - M);
+    const float4 o = reinterpret_cast<const float4*>(a.part_o + p * D)[cidx];
+    acc.x = fmaf(wgt, o.x, acc.x);
+    acc.y = fmaf(wgt, o.y, acc.y);
+    acc.z = fmaf(wgt, o.z, acc.z);
+    acc.w = fmaf(wgt, o.w, acc.w);
+  }
+  racc[gidx][cidx] = acc;
+  __syncthreads();
+  if (tid < CH) {
+    float4 r = racc[0][tid];
+    for (int gq = 1; gq < NG; ++gq) {
+      const float4 x = racc[gq][tid];
+      r.x += x.x; r.y += x.y; r.z += x.z; r.w += x.w;
+    }
+    const float inv = 1.f / s_l;
+    const int64_t o = ((int64_t)t * a.num_q_heads + h) * D + 4 * tid;
+    if (BF16) {
+      uint2 pk;
+      pk.x = pack_bf16x2(r.x * inv, r.y * inv);
+      pk.y = pack_bf16x2(r.z * inv, r.w * inv);
+      *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(a.out) + o) = pk;
+    } else {
+      *reinterpret_cast<float4*>(reinterpret_cast<float*>(a.out) + o) =
+          make_float4(r.x * inv, r.y * inv, r.z * inv, r.w * inv);
+    }
+  }
 }
 
+// ------------------------------------------------------------------------------------------
 namespace {
+template <int D>
+hipError_t mfma_dispatch(const DecodeArgs& a, dim3 g, hipStream_t s) {
+  const dim3 blk(256);
+  const int hpw = a.heads_per_wg;
+  if (hpw <= 1) decode_mfma_kernel<D, 1><<<g, blk, 0, s>>>(a);
+  else if (hpw <= 2) decode_mfma_kernel<D, 2><<<g, blk, 0, s>>>(a);
+  else if (hpw <= 4) decode_mfma_kernel<D, 4><<<g, blk, 0, s>>>(a);
+  else if (hpw <= 8) decode_mfma_kernel<D, 8><<<g, blk, 0, s>>>(a);
+  else if (hpw <= 16) decode_mfma_kernel<D, 16><<<g, blk, 0, s>>>(a);
+  else return hipErrorInvalidValue;
+  return hipGetLastError();
+}
 template <int D, bool BF16>
-hipError_t split_dispatch(const DecodeArgs& a, hipStream_t s) {
-  const int64_t nz = (int64_t)a.num_kv_heads * (a.group / a.heads_per_wg);
-  const int64_t grid = nz * a.max_splits * a.num_rows;
-  if (grid <= 0 || grid > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
-  const dim3 g((unsigned)grid), blk(256);
+hipError_t valu_dispatch(const DecodeArgs& a, dim3 g, hipStream_t s) {
+  const dim3 blk(256);
   switch (a.heads_per_wg) {
-    case 1: decode_split_kernel<D, 1, BF16><<<g, blk, 0, s>>>(a); break;
-    case 2: decode_split_kernel<D, 2, BF16><<<g, blk, 0, s>>>(a); break;
-    case 4: decode_split_kernel<D, 4, BF16><<<g, blk, 0, s>>>(a); break;
-    case 8: decode_split_kernel<D, 8, BF16><<<g, blk, 0, s>>>(a); break;
+    case 1: decode_valu_kernel<D, 1, BF16><<<g, blk, 0, s>>>(a); break;
+    case 2: decode_valu_kernel<D, 2, BF16><<<g, blk, 0, s>>>(a); break;
+    case 4: decode_valu_kernel<D, 4, BF16><<<g, blk, 0, s>>>(a); break;
+    case 8: decode_valu_kernel<D, 8, BF16><<<g, blk, 0, s>>>(a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -303,15 +562,27 @@ hipError_t split_dispatch(const DecodeArgs& a, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_decode_split(const DecodeArgs& a, int head_dim, bool bf16, hipStream_t s) {
-  if (head_dim == 128) return bf16 ? split_dispatch<128, true>(a, s) : split_dispatch<128, false>(a, s);
-  if (head_dim == 64) return bf16 ? split_dispatch<64, true>(a, s) : split_dispatch<64, false>(a, s);
+  const int64_t nzh = (a.group + a.heads_per_wg - 1) / a.heads_per_wg;
+  const int64_t grid = (int64_t)a.num_kv_heads * nzh * a.max_splits * a.num_rows;
+  if (grid <= 0 || grid > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
+  const dim3 g((unsigned)grid);
+  if (bf16 && a.group > 1) {
+    if (head_dim == 128) return mfma_dispatch<128>(a, g, s);
+    if (head_dim == 64) return mfma_dispatch<64>(a, g, s);
+  } else if (bf16) {
+    if (head_dim == 128) return valu_dispatch<128, true>(a, g, s);
+    if (head_dim == 64) return valu_dispatch<64, true>(a, g, s);
+  } else {
+    if (head_dim == 128) return valu_dispatch<128, false>(a, g, s);
+    if (head_dim == 64) return valu_dispatch<64, false>(a, g, s);
+  }
   return hipErrorInvalidValue;
 }
 
 hipError_t launch_decode_merge(const DecodeArgs& a, int head_dim, bool bf16, hipStream_t s) {
   const int64_t grid = (int64_t)a.num_rows * a.num_q_heads;
   if (grid <= 0 || grid > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
-  const dim3 g((unsigned)grid), blk(64);
+  const dim3 g((unsigned)grid), blk(256);
   if (head_dim == 128) {
     if (bf16) decode_merge_kernel<128, true><<<g, blk, 0, s>>>(a);
     else decode_merge_kernel<128, false><<<g, blk, 0, s>>>(a);

@@ -14,38 +14,30 @@
 //   S^T (64 keys x 32 rows) = K (64 x d) . Q^T (d x 32)     -- v_mfma_f32_32x32x16_bf16
 //   online softmax on S^T in registers (lane = query row, 16 keys per lane and sub-tile)
 //   O^T (d x 32 rows)     += V^T (d x 64) . P^T (64 x 32)   -- P^T stays in registers
-// V is written to LDS transposed, with keys permuted inside each 16-key step so that the eight
-// keys a lane needs for one MFMA operand are contiguous.  Key tiles entirely above the causal
-// diagonal of the last row are never visited; only tiles crossing the diagonal are masked.
+// K and V tiles are staged row-major in LDS, double-buffered: the next tile's global loads are in
+// flight while the current one is consumed, with one workgroup barrier per tile.  V^T operands come
+// from the LDS transpose read; the S^T accumulator layout gives lane half a the keys
+// {4a..4a+3, 8+4a..8+4a+3} of each 16-key step, which is exactly two 4-row transpose reads.
+// Row strides are padded so that both the K reads and the transpose reads are free of bank
+// conflicts.  Key tiles entirely above the causal diagonal of the last row are never visited; only
+// tiles crossing the diagonal are masked.  The running max is only moved (and O rescaled) when some
+// row's max grows by more than 2^8; between moves, probabilities may exceed 1 by at most 2^8.
 #include "pa_common.h"
 #include "pa_internal.h"
 
 namespace pa {
 
-namespace {
-
-// LDS column of key kappa (0..15) inside a 16-key MFMA k-step: the accumulator layout of S^T
-// gives lane half a the keys {4a..4a+3, 8+4a..8+4a+3}; they are stored as slots 8a..8a+7.
-__device__ __forceinline__ int vt_slot(int kappa) {
-  return 8 * ((kappa >> 2) & 1) + 4 * (kappa >> 3) + (kappa & 3);
-}
-
-__device__ __forceinline__ uint32_t pair_lo(uint32_t a, uint32_t b) { return (a & 0xFFFFu) | (b << 16); }
-__device__ __forceinline__ uint32_t pair_hi(uint32_t a, uint32_t b) { return (a >> 16) | (b & 0xFFFF0000u); }
-
-}  // namespace
-
 template <int D>
 __global__ __launch_bounds__(256, 2) void prefill_tile_kernel(TileArgs a) {
-  constexpr int KS = D + 8;                 // K tile row stride (elements)
-  constexpr int VT = kTileKeys + 8;         // V^T tile row stride (elements)
+  constexpr int KS = D + 8;                 // K row stride (elements): conflict-free 16-byte reads
+  constexpr int VS = D + 32;                // V row stride (elements): conflict-free transpose reads
   constexpr int NKK = D / 16;               // MFMA k-steps over d
   constexpr int NDT = D / 32;               // 32-wide d tiles of O^T
   constexpr int CPR = D / 8;                // 16-byte pieces per K/V row
-  constexpr int PAIRS = (kTileKeys / 2) * CPR;
-  static_assert(PAIRS % 256 == 0, "staging split");
-  __shared__ __align__(16) uint16_t Ks[kTileKeys * KS];
-  __shared__ __align__(16) uint16_t Vt[D * VT];
+  constexpr int CPT = kTileKeys * CPR / 256;  // pieces per thread per tile (K and V each)
+  static_assert(CPT * 256 == kTileKeys * CPR, "staging split");
+  __shared__ __align__(16) uint16_t Ks[2][kTileKeys * KS];
+  __shared__ __align__(16) uint16_t Vs[2][kTileKeys * VS];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -90,12 +82,8 @@ __global__ __launch_bounds__(256, 2) void prefill_tile_kernel(TileArgs a) {
     const char* qp = reinterpret_cast<const char*>(a.q) + (((t * a.num_q_heads + h) * D) + 8 * half) * 2;
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk) {
-      if (row_ok) {
-        qreg[kk] = *reinterpret_cast<const bf16x8*>(qp + kk * 32);
-      } else {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) qreg[kk][e] = (__bf16)0.f;
-      }
+      const uint4 v = row_ok ? *reinterpret_cast<const uint4*>(qp + kk * 32) : make_uint4(0, 0, 0, 0);
+      qreg[kk] = __builtin_bit_cast(bf16x8, v);
     }
   }
 
@@ -108,6 +96,34 @@ __global__ __launch_bounds__(256, 2) void prefill_tile_kernel(TileArgs a) {
   const char* vbase = reinterpret_cast<const char*>(a.v_cache) + (int64_t)g * D * 2;
   const int32_t* table = a.block_tables + (int64_t)b * a.max_blocks;
 
+  // staging: piece p = tid + 256 i -> key p / CPR, 16-byte column p % CPR (16 lanes per 256-byte row)
+  uint4 kr[CPT], vr[CPT];
+  auto load_tile = [&](int kt) {
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+      const int p = tid + 256 * i;
+      const int key = p / CPR, dc = p - key * CPR;
+      const int j = kt * kTileKeys + key;
+      if (j < sl) {
+        const int64_t off = (((int64_t)table[j >> 4] * kBlock + (j & 15)) * rs + dc * 8) * 2;
+        kr[i] = *reinterpret_cast<const uint4*>(kbase + off);
+        vr[i] = *reinterpret_cast<const uint4*>(vbase + off);
+      } else {
+        kr[i] = make_uint4(0, 0, 0, 0);
+        vr[i] = make_uint4(0, 0, 0, 0);
+      }
+    }
+  };
+  auto store_tile = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+      const int p = tid + 256 * i;
+      const int key = p / CPR, dc = p - key * CPR;
+      *reinterpret_cast<uint4*>(&Ks[buf][key * KS + dc * 8]) = kr[i];
+      *reinterpret_cast<uint4*>(&Vs[buf][key * VS + dc * 8]) = vr[i];
+    }
+  };
+
   float m_run = -INFINITY, l_run = 0.f;
   floatx16 O[NDT];
 #pragma unroll
@@ -115,41 +131,19 @@ __global__ __launch_bounds__(256, 2) void prefill_tile_kernel(TileArgs a) {
 #pragma unroll
     for (int v = 0; v < 16; ++v) O[dt][v] = 0.f;
 
+  // transpose-read coordinates: 16-lane group (gsel, j), j = 4e + cq
+  const int trj = lane & 15;
+  const int gsel = (lane >> 4) & 1;
+  const int tr_off = (trj >> 2) * VS + 16 * gsel + 4 * (trj & 3);
+
+  load_tile(0);
+  store_tile(0);
+  __syncthreads();
+
   for (int kt = 0; kt < n_kt; ++kt) {
-    // ---- stage K (row-major) and V (transposed, permuted) for keys kt*64 .. kt*64+63 ----
-#pragma unroll
-    for (int it = 0; it < PAIRS / 256; ++it) {
-      const int pc = tid + 256 * it;
-      const int kp = pc / CPR;
-      const int dc = pc - kp * CPR;
-      const int j0 = kt * kTileKeys + 2 * kp;
-      uint4 k0 = make_uint4(0, 0, 0, 0), k1 = k0, v0 = k0, v1 = k0;
-      if (j0 < sl) {
-        const int64_t phys = table[j0 >> 4];
-        const int64_t off = ((phys * kBlock + (j0 & 15)) * rs + dc * 8) * 2;
-        k0 = *reinterpret_cast<const uint4*>(kbase + off);
-        v0 = *reinterpret_cast<const uint4*>(vbase + off);
-        if (j0 + 1 < sl) {
-          k1 = *reinterpret_cast<const uint4*>(kbase + off + rs * 2);
-          v1 = *reinterpret_cast<const uint4*>(vbase + off + rs * 2);
-        }
-      }
-      *reinterpret_cast<uint4*>(&Ks[(2 * kp) * KS + dc * 8]) = k0;
-      *reinterpret_cast<uint4*>(&Ks[(2 * kp + 1) * KS + dc * 8]) = k1;
-      const int key = 2 * kp;
-      const int col = (key & ~15) + vt_slot(key & 15);
-      uint32_t* vt32 = reinterpret_cast<uint32_t*>(Vt);
-      const int r0 = dc * 8;
-      vt32[((r0 + 0) * VT + col) >> 1] = pair_lo(v0.x, v1.x);
-      vt32[((r0 + 1) * VT + col) >> 1] = pair_hi(v0.x, v1.x);
-      vt32[((r0 + 2) * VT + col) >> 1] = pair_lo(v0.y, v1.y);
-      vt32[((r0 + 3) * VT + col) >> 1] = pair_hi(v0.y, v1.y);
-      vt32[((r0 + 4) * VT + col) >> 1] = pair_lo(v0.z, v1.z);
-      vt32[((r0 + 5) * VT + col) >> 1] = pair_hi(v0.z, v1.z);
-      vt32[((r0 + 6) * VT + col) >> 1] = pair_lo(v0.w, v1.w);
-      vt32[((r0 + 7) * VT + col) >> 1] = pair_hi(v0.w, v1.w);
-    }
-    __syncthreads();
+    const int buf = kt & 1;
+    const bool more = kt + 1 < n_kt;
+    if (more) load_tile(kt + 1);                 // in flight during this tile's math
 
     // ---- S^T = K Q^T : two 32-key sub-tiles ----
     floatx16 S[2];
@@ -159,7 +153,7 @@ __global__ __launch_bounds__(256, 2) void prefill_tile_kernel(TileArgs a) {
       for (int v = 0; v < 16; ++v) S[st][v] = 0.f;
 #pragma unroll
       for (int kk = 0; kk < NKK; ++kk) {
-        const bf16x8 kop = *reinterpret_cast<const bf16x8*>(&Ks[(32 * st + l32) * KS + kk * 16 + 8 * half]);
+        const bf16x8 kop = *reinterpret_cast<const bf16x8*>(&Ks[buf][(32 * st + l32) * KS + kk * 16 + 8 * half]);
         S[st] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, qreg[kk], S[st], 0, 0, 0);
       }
     }
@@ -175,16 +169,22 @@ __global__ __launch_bounds__(256, 2) void prefill_tile_kernel(TileArgs a) {
         }
     }
 
-    // ---- online softmax (scores in log2 units via c = scale * log2 e) ----
-    float tm = S[0][0];
+    // ---- online softmax (scores in log2 units via c = scale * log2 e), lazy rescale ----
+    float tm = fmaxf(S[0][0], S[1][0]);
 #pragma unroll
-    for (int st = 0; st < 2; ++st)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) tm = fmaxf(tm, S[st][v]);
-    tm = fmaxf(tm, __shfl_xor(tm, 32));
+    for (int v = 1; v < 16; ++v) tm = fmaxf(tm, fmaxf(S[0][v], S[1][v]));
+    tm = xor32_max(tm);
     const float mn = fmaxf(m_run, tm);
-    const float alpha = (m_run == -INFINITY) ? 0.f : fast_exp2((m_run - mn) * c);
-    const float mc = mn * c;
+    if (__any((mn - m_run) * c > 8.f)) {
+      const float alpha = (m_run == -INFINITY) ? 0.f : fast_exp2((m_run - mn) * c);
+      m_run = mn;
+      l_run *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) O[dt][v] *= alpha;
+    }
+    const float mc = m_run * c;
     bf16x8 P[4];
     float ps = 0.f;
 #pragma unroll
@@ -195,26 +195,26 @@ __global__ __launch_bounds__(256, 2) void prefill_tile_kernel(TileArgs a) {
         ps += p;
         P[2 * st + (v >> 3)][v & 7] = (__bf16)p;
       }
-    l_run = l_run * alpha + ps;
-    m_run = mn;
-#pragma unroll
-    for (int dt = 0; dt < NDT; ++dt)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) O[dt][v] *= alpha;
+    l_run += ps;
 
-    // ---- O^T += V^T P^T ----
+    // ---- O^T += V^T P^T : A operand = two 4-key transpose reads per 16-key step ----
+    const uint16_t* vb = &Vs[buf][tr_off];
 #pragma unroll
-    for (int dt = 0; dt < NDT; ++dt)
+    for (int kk = 0; kk < 4; ++kk) {
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        const bf16x8 vop = *reinterpret_cast<const bf16x8*>(&Vt[(32 * dt + l32) * VT + 16 * kk + 8 * half]);
+      for (int dt = 0; dt < NDT; ++dt) {
+        const bf16x4 lo = lds_read_tr(vb + (16 * kk + 4 * half) * VS + 32 * dt);
+        const bf16x4 hi = lds_read_tr(vb + (16 * kk + 8 + 4 * half) * VS + 32 * dt);
+        const bf16x8 vop = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
         O[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop, P[kk], O[dt], 0, 0, 0);
       }
+    }
+    if (more) store_tile(buf ^ 1);
     __syncthreads();
   }
 
   // ---- epilogue: O / l, round to bf16, store (lane holds 4 consecutive d per group) ----
-  const float lt = l_run + __shfl_xor(l_run, 32);
+  const float lt = xor32_sum(l_run);
   const float inv = 1.f / lt;
   if (row_ok) {
     char* op = reinterpret_cast<char*>(a.out) + ((t * a.num_q_heads + h) * D) * 2;
