@@ -14,34 +14,47 @@
 //   S^T (64 keys x 32 rows) = K (64 x d) . Q^T (d x 32)     -- v_mfma_f32_32x32x16_bf16
 //   online softmax on S^T in registers (lane = query row, 16 keys per lane and sub-tile)
 //   O^T (d x 32 rows)     += V^T (d x 64) . P^T (64 x 32)   -- P^T stays in registers
-// K and V tiles are staged row-major in LDS, double-buffered: the next tile's global loads are in
-// flight while the current one is consumed, with one workgroup barrier per tile.  V^T operands come
-// from the LDS transpose read; the S^T accumulator layout gives lane half a the keys
-// {4a..4a+3, 8+4a..8+4a+3} of each 16-key step, which is exactly two 4-row transpose reads.
-// Row strides are padded so that both the K reads and the transpose reads are free of bank
-// conflicts.  Key tiles entirely above the causal diagonal of the last row are never visited; only
-// tiles crossing the diagonal are masked.  The running max is only moved (and O rescaled) when some
-// row's max grows by more than 2^8; between moves, probabilities may exceed 1 by at most 2^8.
+// K and V tiles are staged in LDS by direct global->LDS loads (no staging registers), double
+// buffered: the next tile's loads are in flight while the current one is consumed, with one
+// workgroup barrier per tile.  Each wave loads one 16-key cache block per tile, so its block-table
+// lookup is a single uniform value.  LDS rows are unpadded and their 16-byte chunks XOR-swizzled by
+// row, which keeps the K operand reads and the V transpose reads free of bank conflicts.  V^T
+// operands come from the LDS transpose read: the S^T accumulator layout gives lane half a the keys
+// {4a..4a+3, 8+4a..8+4a+3} of each 16-key step, which is exactly two 4-row transpose reads.  Key
+// tiles entirely above the causal diagonal of the last row are never visited; only tiles crossing
+// the diagonal are masked.  Keys past the request's length in its last tile load a valid row
+// instead (finite data under a zero probability).  The running max is only moved (and O rescaled)
+// when some row's max grows by more than 2^8; between moves, probabilities may exceed 1 by at most
+// 2^8.
 #include "pa_common.h"
 #include "pa_internal.h"
 
 namespace pa {
 
+namespace {
+// Physical 16-byte chunk of logical chunk q in tile row r (bijective per row).
+template <int D>
+__device__ __forceinline__ int swz(int r) {
+  if constexpr (D == 128) return 4 * (r & 3) + ((r >> 2) & 3);
+  else return (r >> 1) & 7;
+}
+}  // namespace
+
 template <int D>
 __global__ __launch_bounds__(256, 2) void prefill_tile_kernel(TileArgs a) {
-  constexpr int KS = D + 8;                 // K row stride (elements): conflict-free 16-byte reads
-  constexpr int VS = D + 32;                // V row stride (elements): conflict-free transpose reads
+  constexpr int ROWB = D * 2;               // bytes per K/V row
+  constexpr int CPR = D / 8;                // 16-byte chunks per row
+  constexpr int RPI = 1024 / ROWB;          // rows per wave-wide 1 KiB load
+  constexpr int IPB = kBlock / RPI;         // loads per 16-key block (per tensor)
+  constexpr int TILEB = kTileKeys * ROWB;   // bytes per K (or V) tile
   constexpr int NKK = D / 16;               // MFMA k-steps over d
   constexpr int NDT = D / 32;               // 32-wide d tiles of O^T
-  constexpr int CPR = D / 8;                // 16-byte pieces per K/V row
-  constexpr int CPT = kTileKeys * CPR / 256;  // pieces per thread per tile (K and V each)
-  static_assert(CPT * 256 == kTileKeys * CPR, "staging split");
-  __shared__ __align__(16) uint16_t Ks[2][kTileKeys * KS];
-  __shared__ __align__(16) uint16_t Vs[2][kTileKeys * VS];
+  static_assert(kTileKeys == 4 * kBlock, "one cache block per wave and tile");
+  __shared__ __align__(16) char smem[2 * 2 * TILEB];   // [buf][K,V][tile]
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int w = tid >> 6;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31;
   const int half = lane >> 5;
 
@@ -96,31 +109,41 @@ __global__ __launch_bounds__(256, 2) void prefill_tile_kernel(TileArgs a) {
   const char* vbase = reinterpret_cast<const char*>(a.v_cache) + (int64_t)g * D * 2;
   const int32_t* table = a.block_tables + (int64_t)b * a.max_blocks;
 
-  // staging: piece p = tid + 256 i -> key p / CPR, 16-byte column p % CPR (16 lanes per 256-byte row)
-  uint4 kr[CPT], vr[CPT];
-  auto load_tile = [&](int kt) {
+  // ---- staging: wave w loads key rows 16w..16w+15 of the tile (one cache block) ----
+  // load i of the block covers rows RPI*i .. RPI*i + RPI - 1; lane -> (row lane / CPR, physical
+  // chunk lane % CPR), which holds logical chunk (lane % CPR) ^ swz(row).
+  int lane_off[IPB];                              // byte offset within the block, per load
 #pragma unroll
-    for (int i = 0; i < CPT; ++i) {
-      const int p = tid + 256 * i;
-      const int key = p / CPR, dc = p - key * CPR;
-      const int j = kt * kTileKeys + key;
-      if (j < sl) {
-        const int64_t off = (((int64_t)table[j >> 4] * kBlock + (j & 15)) * rs + dc * 8) * 2;
-        kr[i] = *reinterpret_cast<const uint4*>(kbase + off);
-        vr[i] = *reinterpret_cast<const uint4*>(vbase + off);
-      } else {
-        kr[i] = make_uint4(0, 0, 0, 0);
-        vr[i] = make_uint4(0, 0, 0, 0);
+  for (int i = 0; i < IPB; ++i) {
+    const int rr = RPI * i + lane / CPR;          // row within the block (and within the wave's 16)
+    const int q = (lane % CPR) ^ swz<D>(16 * w + rr);
+    lane_off[i] = (int)(rr * rs * 2) + q * 16;
+  }
+  auto stage = [&](int kt, int buf) {
+    char* kl = smem + (2 * buf) * TILEB + 16 * w * ROWB;
+    char* vl = kl + TILEB;
+    const int blk = 4 * kt + w;
+    if ((blk + 1) * kBlock <= sl) {               // whole block valid: one uniform table entry
+      const int64_t boff = (int64_t)table[blk] * kBlock * rs * 2;
+#pragma unroll
+      for (int i = 0; i < IPB; ++i) {
+        __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(kbase + boff + lane_off[i]),
+                                         (__attribute__((address_space(3))) void*)(kl + 1024 * i), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(vbase + boff + lane_off[i]),
+                                         (__attribute__((address_space(3))) void*)(vl + 1024 * i), 16, 0, 0);
       }
-    }
-  };
-  auto store_tile = [&](int buf) {
+    } else {                                      // last block: clamp rows past the length
 #pragma unroll
-    for (int i = 0; i < CPT; ++i) {
-      const int p = tid + 256 * i;
-      const int key = p / CPR, dc = p - key * CPR;
-      *reinterpret_cast<uint4*>(&Ks[buf][key * KS + dc * 8]) = kr[i];
-      *reinterpret_cast<uint4*>(&Vs[buf][key * VS + dc * 8]) = vr[i];
+      for (int i = 0; i < IPB; ++i) {
+        const int rr = RPI * i + lane / CPR;
+        const int j = min(blk * kBlock + rr, sl - 1);
+        const int q = (lane % CPR) ^ swz<D>(16 * w + rr);
+        const int64_t off = (((int64_t)table[j >> 4] * kBlock + (j & 15)) * rs) * 2 + q * 16;
+        __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(kbase + off),
+                                         (__attribute__((address_space(3))) void*)(kl + 1024 * i), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(vbase + off),
+                                         (__attribute__((address_space(3))) void*)(vl + 1024 * i), 16, 0, 0);
+      }
     }
   };
 
@@ -131,48 +154,65 @@ __global__ __launch_bounds__(256, 2) void prefill_tile_kernel(TileArgs a) {
 #pragma unroll
     for (int v = 0; v < 16; ++v) O[dt][v] = 0.f;
 
-  // transpose-read coordinates: 16-lane group (gsel, j), j = 4e + cq
+  // K operand: row 32st + l32, logical chunk 2kk + half
+  int k_off[2][NKK];
+#pragma unroll
+  for (int st = 0; st < 2; ++st)
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) {
+      const int r = 32 * st + l32;
+      k_off[st][kk] = r * ROWB + (((2 * kk + half) ^ swz<D>(r)) * 16);
+    }
+  // V transpose-read coordinates: 16-lane group (gsel, j = 4e + cq) reads row R + e, columns
+  // 32dt + 16gsel + 4cq .. +3 (8 bytes), i.e. logical chunk 4dt + 2gsel + cq/2, half cq & 1.
   const int trj = lane & 15;
   const int gsel = (lane >> 4) & 1;
-  const int tr_off = (trj >> 2) * VS + 16 * gsel + 4 * (trj & 3);
+  const int tre = trj >> 2;
 
-  load_tile(0);
-  store_tile(0);
+  stage(0, 0);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
 
   for (int kt = 0; kt < n_kt; ++kt) {
     const int buf = kt & 1;
     const bool more = kt + 1 < n_kt;
-    if (more) load_tile(kt + 1);                 // in flight during this tile's math
+    if (more) stage(kt + 1, buf ^ 1);             // in flight during this tile's math
+    const char* kl = smem + (2 * buf) * TILEB;
+    const char* vl = kl + TILEB;
 
-    // ---- S^T = K Q^T : two 32-key sub-tiles ----
-    floatx16 S[2];
+    // ---- S^T = K Q^T : two 32-key sub-tiles, chains interleaved, operands read one step ahead ----
+    floatx16 S0, S1;
 #pragma unroll
-    for (int st = 0; st < 2; ++st) {
+    for (int v = 0; v < 16; ++v) { S0[v] = 0.f; S1[v] = 0.f; }
+    bf16x8 a0 = *reinterpret_cast<const bf16x8*>(kl + k_off[0][0]);
+    bf16x8 a1 = *reinterpret_cast<const bf16x8*>(kl + k_off[1][0]);
 #pragma unroll
-      for (int v = 0; v < 16; ++v) S[st][v] = 0.f;
-#pragma unroll
-      for (int kk = 0; kk < NKK; ++kk) {
-        const bf16x8 kop = *reinterpret_cast<const bf16x8*>(&Ks[buf][(32 * st + l32) * KS + kk * 16 + 8 * half]);
-        S[st] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, qreg[kk], S[st], 0, 0, 0);
+    for (int kk = 0; kk < NKK; ++kk) {
+      bf16x8 n0 = a0, n1 = a1;
+      if (kk + 1 < NKK) {
+        n0 = *reinterpret_cast<const bf16x8*>(kl + k_off[0][kk + 1]);
+        n1 = *reinterpret_cast<const bf16x8*>(kl + k_off[1][kk + 1]);
       }
+      S0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qreg[kk], S0, 0, 0, 0);
+      S1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qreg[kk], S1, 0, 0, 0);
+      a0 = n0;
+      a1 = n1;
     }
 
     // ---- causal mask (only on tiles that cross the diagonal of the first row) ----
     if (kt * kTileKeys + kTileKeys - 1 > first_pos) {
 #pragma unroll
-      for (int st = 0; st < 2; ++st)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int key = kt * kTileKeys + 32 * st + 8 * (v >> 2) + 4 * half + (v & 3);
-          if (key > pos) S[st][v] = -INFINITY;
-        }
+      for (int v = 0; v < 16; ++v) {
+        const int key = kt * kTileKeys + 8 * (v >> 2) + 4 * half + (v & 3);
+        if (key > pos) S0[v] = -INFINITY;
+        if (key + 32 > pos) S1[v] = -INFINITY;
+      }
     }
 
     // ---- online softmax (scores in log2 units via c = scale * log2 e), lazy rescale ----
-    float tm = fmaxf(S[0][0], S[1][0]);
+    float tm = fmaxf(S0[0], S1[0]);
 #pragma unroll
-    for (int v = 1; v < 16; ++v) tm = fmaxf(tm, fmaxf(S[0][v], S[1][v]));
+    for (int v = 1; v < 16; ++v) tm = fmaxf(tm, fmaxf(S0[v], S1[v]));
     tm = xor32_max(tm);
     const float mn = fmaxf(m_run, tm);
     if (__any((mn - m_run) * c > 8.f)) {
@@ -188,28 +228,35 @@ __global__ __launch_bounds__(256, 2) void prefill_tile_kernel(TileArgs a) {
     bf16x8 P[4];
     float ps = 0.f;
 #pragma unroll
-    for (int st = 0; st < 2; ++st)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const float p = fast_exp2(fmaf(S[st][v], c, -mc));
-        ps += p;
-        P[2 * st + (v >> 3)][v & 7] = (__bf16)p;
-      }
+    for (int v = 0; v < 16; ++v) {
+      const float p0 = fast_exp2(fmaf(S0[v], c, -mc));
+      const float p1 = fast_exp2(fmaf(S1[v], c, -mc));
+      ps += p0 + p1;
+      P[v >> 3][v & 7] = (__bf16)p0;
+      P[2 + (v >> 3)][v & 7] = (__bf16)p1;
+    }
     l_run += ps;
 
     // ---- O^T += V^T P^T : A operand = two 4-key transpose reads per 16-key step ----
-    const uint16_t* vb = &Vs[buf][tr_off];
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
+      bf16x4 lo[NDT], hi[NDT];
+      const int r_lo = 16 * kk + 4 * half + tre;
+      const int r_hi = r_lo + 8;
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt) {
-        const bf16x4 lo = lds_read_tr(vb + (16 * kk + 4 * half) * VS + 32 * dt);
-        const bf16x4 hi = lds_read_tr(vb + (16 * kk + 8 + 4 * half) * VS + 32 * dt);
-        const bf16x8 vop = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        const int lq = 4 * dt + 2 * gsel + (trj & 3) / 2;      // logical chunk
+        const int sub = (trj & 1) * 8;                         // byte half within the chunk
+        lo[dt] = lds_read_tr(reinterpret_cast<const uint16_t*>(vl + r_lo * ROWB + ((lq ^ swz<D>(r_lo)) * 16) + sub));
+        hi[dt] = lds_read_tr(reinterpret_cast<const uint16_t*>(vl + r_hi * ROWB + ((lq ^ swz<D>(r_hi)) * 16) + sub));
+      }
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) {
+        const bf16x8 vop = __builtin_shufflevector(lo[dt], hi[dt], 0, 1, 2, 3, 4, 5, 6, 7);
         O[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop, P[kk], O[dt], 0, 0, 0);
       }
     }
-    if (more) store_tile(buf ^ 1);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this thread's loads of the next tile landed
     __syncthreads();
   }
 
