@@ -50,7 +50,7 @@ int split_tokens() {
   static int v = [] {
     const char* e = std::getenv("PA_SPLIT_TOKENS");
     int s = e ? std::atoi(e) : pa::kDefaultSplitTokens;
-    if (s < 16 || s % 16 != 0) s = pa::kDefaultSplitTokens;
+    if (s < 16 || s > 1024 || s % 16 != 0) s = pa::kDefaultSplitTokens;  // <= 64 blocks per split
     return s;
   }();
   return v;
@@ -137,10 +137,9 @@ int make_plan(int32_t B, int32_t T, int32_t MB, int32_t Hq, const pa_cache_desc*
   p.bf16 = c->dtype == PA_DTYPE_BF16;
   p.head_dim = c->head_dim;
   p.group = Hq / c->num_kv_heads;
-  // bf16 decode of grouped heads holds up to 16 query heads per workgroup (the MFMA column
-  // count); the vector-ALU decode (fp32, or one query head per KV head) holds a divisor of the
-  // group size up to 8.
-  if (p.bf16 && p.group > 1) p.heads_per_wg = p.group < 16 ? p.group : 16;
+  // bf16 decode holds up to 16 query heads of a KV head per wave (the MFMA column count); the
+  // fp32 vector-ALU decode holds a divisor of the group size up to 8.
+  if (p.bf16) p.heads_per_wg = p.group < 16 ? p.group : 16;
   else p.heads_per_wg = (p.group % 8 == 0) ? 8 : (p.group % 4 == 0) ? 4 : (p.group % 2 == 0) ? 2 : 1;
   if (p.bf16 && p.group > pa::kTileRows)
     return fail(PA_ERR_UNSUPPORTED, "query heads per KV head (%d) above %d", p.group, pa::kTileRows);
@@ -175,7 +174,8 @@ int make_plan(int32_t B, int32_t T, int32_t MB, int32_t Hq, const pa_cache_desc*
   }
   p.total = off;
   const int64_t nzh = (p.group + p.heads_per_wg - 1) / p.heads_per_wg;
-  const int64_t dec_grid = (int64_t)c->num_kv_heads * nzh * p.max_splits * p.rows;
+  const int64_t heads = p.bf16 ? (c->num_kv_heads + 3) / 4 : c->num_kv_heads;
+  const int64_t dec_grid = heads * nzh * p.max_splits * p.rows;
   if (p.run_decode && dec_grid > 0x7FFFFFFF) return fail(PA_ERR_UNSUPPORTED, "batch too large for one launch");
   return PA_OK;
 }

@@ -65,6 +65,24 @@ __device__ __forceinline__ float xor16_sum(float v) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// Block ids a wave will visit, 64 at a time: lane i holds the id of the wave's i-th block of the
+// current window, so the loop takes each id with one v_readlane instead of a memory round trip.
+struct BlockWindow {
+  int ids = 0;
+  int base = -(1 << 30);
+  // ids of blocks first + stride * (base + lane), for base + lane < count
+  __device__ __forceinline__ void load(const int32_t* table, int first, int stride, int count, int new_base) {
+    base = new_base;
+    const int i = new_base + (int)(threadIdx.x & 63);
+    ids = i < count ? table[first + stride * i] : 0;
+  }
+  // id of the wave's k-th block (k < count)
+  __device__ __forceinline__ int get(const int32_t* table, int first, int stride, int count, int k) {
+    if (k - base >= 64 || k < base) load(table, first, stride, count, k);
+    return __builtin_amdgcn_readlane(ids, k - base);
+  }
+};
+
 // Transposed LDS read (ds_read_b64_tr_b16).  Within each 16-lane group, input lane 4e + c gives
 // the address of 4 consecutive elements of row e, columns 4c..4c+3 of a 4 x 16 tile; output lane
 // j receives column j of the tile: rows 0..3.

@@ -10,16 +10,19 @@
 // (scores are kept in log2 units: x * scale * log2 e).  The pages do not describe how partial
 // softmaxes combine; this is the exact decomposition of the row softmax of P3 §3.1.
 //
-// bf16 caches whose KV heads serve several query heads: matrix cores do the arithmetic so that
-// the vector ALUs stay idle however large the group.  Per 16-key block and wave:
+// bf16 caches: matrix cores do the arithmetic so that the vector ALUs stay idle however many
+// query heads share a KV head.  Per 16-key block and wave:
 //   S^T (16 keys x 16 query heads) = K (16 x d) . Q^T   -- v_mfma_f32_16x16x32_bf16, K loaded
 //                                                          from HBM straight into A-operand lanes
 //   O^T (d x 16 heads) += V^T (d x 16 keys) . P^T       -- v_mfma_f32_16x16x16_bf16; V is staged
 //       row-major in a per-wave LDS block and read back transposed with ds_read_b64_tr_b16
 // P^T stays in registers: the S^T accumulator layout (lane = head, 4 keys) is exactly the B
 // operand layout of the second product.  Unused head columns are zero.
-// fp32 caches, and bf16 caches with one query head per KV head: vector-ALU kernel (dot products
-// reduced across 16-lane rows with DPP); for fp32 it serves every query row of the batch.
+// fp32 caches: vector-ALU kernel (dot products reduced across 16-lane rows with DPP), serving every
+// query row of an fp32 batch.
+#include <cstdlib>
+#include <type_traits>
+
 #include "pa_common.h"
 #include "pa_internal.h"
 
@@ -114,84 +117,130 @@ __device__ __forceinline__ bool get_unit(const DecodeArgs& a, int nzh, Unit& u) 
 }  // namespace
 
 // ------------------------------------------------------------------------------------------
-// bf16: matrix-core split kernel.  NCOL = query-head columns held (power of two >= ncols).
+// bf16: matrix-core split kernel.  A workgroup covers four adjacent KV heads of the
+// same query row and split (one wave each), so together its waves read contiguous 4 x 256-byte
+// spans of every token row.  Each wave streams all blocks of the split for its head: K goes from
+// HBM straight into A-operand registers (one block ahead), V is copied by direct global->LDS loads
+// into a per-wave double buffer (rows' 16-byte chunks XOR-swizzled so the transpose reads are free
+// of bank conflicts).  NCOL = query-head columns held (power of two >= the heads per KV head).
 // ------------------------------------------------------------------------------------------
+namespace {
+__device__ __forceinline__ int dswz(int r) { return 2 * (r & 7); }
+}
+
 template <int D, int NCOL>
 __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
   constexpr int NKK = D / 32;                 // 16x16x32 k-steps over d for S^T
   constexpr int NT = D / 16;                  // 16-row d tiles of O^T
-  constexpr int VS = D + 16;                  // LDS row stride (elements) of a staged V block
-  constexpr int VBYTES = 4 * kBlock * VS * 2;
-  constexpr int OBYTES = 4 * NCOL * (D + 2) * 4;
-  constexpr int SMEM = VBYTES > OBYTES ? VBYTES : OBYTES;
-  __shared__ __align__(16) char smem[SMEM];
+  constexpr int ROWB = D * 2;                 // bytes of one head's K or V row
+  constexpr int CPR = D / 8;                  // 16-byte chunks per row
+  constexpr int RPI = 64 / CPR;               // rows per wave-wide 1 KiB copy
+  constexpr int IPB = kBlock / RPI;           // copies per 16-row block
+  constexpr int VB = kBlock * ROWB;           // bytes per staged V block
+  __shared__ __align__(16) char sV0[4 * VB];  // [wave] buffer 0
+  __shared__ __align__(16) char sV1[4 * VB];  // [wave] buffer 1
 
-  Unit u;
-  if (!get_unit(a, (a.group + a.heads_per_wg - 1) / a.heads_per_wg, u)) return;
+  // unit: (row, split, head quad, query-head column group); the wave's KV head is 4 * quad + w
+  const int nzh = (a.group + a.heads_per_wg - 1) / a.heads_per_wg;
+  const int nq = (a.num_kv_heads + 3) / 4;
+  const int nz = nq * nzh;
+  int ib = blockIdx.x;
+  const int z = ib % nz;
+  ib /= nz;
+  const int split = ib % a.max_splits;
+  const int row = ib / a.max_splits;
+  if (row >= a.num_rows) return;
+  int b, t, n_keys;
+  if (!resolve_row(a, row, b, t, n_keys)) return;
+  const int k0 = split * a.split;
+  if (k0 >= n_keys) return;
+  const int k1 = min(k0 + a.split, n_keys);
+  const int n_splits = (n_keys + a.split - 1) / a.split;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int g = 4 * (z / nzh) + w;
+  if (g >= a.num_kv_heads) return;                         // waves are independent: no barriers
+  const int zh = z % nzh;
+  const int h0 = g * a.group + zh * a.heads_per_wg;
+  const int ncols = min(a.heads_per_wg, a.group - zh * a.heads_per_wg);
 
   const int lane = threadIdx.x & (kWave - 1);
-  const int w = threadIdx.x >> 6;
-  const int col = lane & 15;                  // S^T / O^T column = query head; also the K/V row loaded
+  const int col = lane & 15;                  // S^T / O^T column = query head; also the K row loaded
   const int grp = lane >> 4;                  // 4-key group of the accumulator layout
   const float c = a.scale_log2;
 
   // Q^T as the B operand: lane holds d = 32kk + 8grp .. +8 of head h0 + col
   bf16x8 qb[NKK];
   {
-    const bool on = col < u.ncols;
+    const bool on = col < ncols;
     const char* qp = reinterpret_cast<const char*>(a.q) +
-                     (((int64_t)u.t * a.num_q_heads + u.h0 + (on ? col : 0)) * D + 8 * grp) * 2;
+                     (((int64_t)t * a.num_q_heads + h0 + (on ? col : 0)) * D + 8 * grp) * 2;
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk) {
-      uint4 v = on ? *reinterpret_cast<const uint4*>(qp + kk * 64) : make_uint4(0, 0, 0, 0);
+      const uint4 v = on ? *reinterpret_cast<const uint4*>(qp + kk * 64) : make_uint4(0, 0, 0, 0);
       qb[kk] = __builtin_bit_cast(bf16x8, v);
     }
   }
 
-  uint16_t* vs = reinterpret_cast<uint16_t*>(smem) + w * kBlock * VS;
   const int64_t rs = (int64_t)a.num_kv_heads * D;            // elements per cache token row
-  const char* kbase = reinterpret_cast<const char*>(a.k_cache) + ((int64_t)u.g * D + 8 * grp) * 2;
-  const char* vbase = reinterpret_cast<const char*>(a.v_cache) + ((int64_t)u.g * D + 8 * grp) * 2;
-  const int32_t* table = a.block_tables + (int64_t)u.b * a.max_blocks;
-  const int kb0 = u.k0 / kBlock;
-  const int kb1 = (u.k1 + kBlock - 1) / kBlock;
+  const int64_t blkbytes = kBlock * rs * 2;
+  const char* kbase = reinterpret_cast<const char*>(a.k_cache) + (int64_t)g * ROWB;
+  const char* vbase = reinterpret_cast<const char*>(a.v_cache) + (int64_t)g * ROWB;
+  const int32_t* table = a.block_tables + (int64_t)b * a.max_blocks;
+  const int kb0 = k0 / kBlock;
+  const int nb = (k1 + kBlock - 1) / kBlock - kb0;        // <= 64: splits are at most 1024 keys
+  const int ids = lane < nb ? table[kb0 + lane] : 0;       // lane i: id of the split's i-th block
+
+  // K operand: key row `col`, d = 32kk + 8grp: byte offset within the block
+  const uint32_t k_lane = (uint32_t)(col * rs * 2) + 16 * grp;
+  // V copy: copy i covers rows RPI*i ..; lane -> (row RPI*i + lane / CPR, physical chunk lane % CPR)
+  uint32_t v_lane[IPB];
+#pragma unroll
+  for (int i = 0; i < IPB; ++i) {
+    const int r = RPI * i + lane / CPR;
+    v_lane[i] = (uint32_t)(r * rs * 2) + (((lane % CPR) ^ dswz(r)) * 16);
+  }
+  // transpose read: group grp, lane j = 4e + cq reads row 4grp + e, columns 16tt + 4cq .. +3,
+  // i.e. logical chunk 2tt + cq / 2, byte half cq & 1
+  uint32_t tr_off[NT];
+#pragma unroll
+  for (int tt = 0; tt < NT; ++tt) {
+    const int r = 4 * grp + (col >> 2);
+    const int lq = 2 * tt + ((col & 3) >> 1);
+    tr_off[tt] = r * ROWB + ((lq ^ dswz(r)) * 16) + (col & 1) * 8;
+  }
 
   float m = -INFINITY, lsum = 0.f;
   floatx4 O[NT];
 #pragma unroll
   for (int tt = 0; tt < NT; ++tt) O[tt] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-  auto load = [&](int blk, uint4* kr, uint4* vr) {
-    const int64_t off = (((int64_t)table[blk] * kBlock + col) * rs) * 2;
+  auto issue = [&](int i, uint4* kr, char* vdst) {        // block kb0 + i: K to registers, V to LDS
+    const char* kb = kbase + (int64_t)__builtin_amdgcn_readlane(ids, i) * blkbytes;
+    const char* vb = vbase + (kb - kbase);
 #pragma unroll
-    for (int kk = 0; kk < NKK; ++kk) {
-      kr[kk] = *reinterpret_cast<const uint4*>(kbase + off + kk * 64);
-      vr[kk] = *reinterpret_cast<const uint4*>(vbase + off + kk * 64);
-    }
+    for (int kk = 0; kk < NKK; ++kk) kr[kk] = *reinterpret_cast<const uint4*>(kb + k_lane + kk * 64);
+#pragma unroll
+    for (int j = 0; j < IPB; ++j)
+      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(vb + v_lane[j]),
+                                       (__attribute__((address_space(3))) void*)(vdst + w * VB + 1024 * j), 16, 0, 0);
   };
 
-  auto consume = [&](int blk, const uint4* kr, const uint4* vr) {
+  // one block; PARTIAL: the block holds keys past the last visible one (only the split's last)
+  auto consume = [&](auto partial_tag, int i, const uint4* kr, const char* vsrc) {
+    constexpr bool PARTIAL = decltype(partial_tag)::value;
     floatx4 s = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk)
       s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kr[kk]), qb[kk], s, 0, 0, 0);
-    const int kbase_idx = blk * kBlock;
-    const bool partial = kbase_idx + kBlock > u.k1;
-    // stage V (row = key `col`), zeroing rows past the last visible key
-#pragma unroll
-    for (int kk = 0; kk < NKK; ++kk) {
-      uint4 v = vr[kk];
-      if (partial && kbase_idx + col >= u.k1) v = make_uint4(0, 0, 0, 0);
-      *reinterpret_cast<uint4*>(&vs[col * VS + 32 * kk + 8 * grp]) = v;
-    }
-    if (partial) {
+    const int nvis = k1 - (kb0 + i) * kBlock;               // visible keys in this block
+    if constexpr (PARTIAL) {
 #pragma unroll
       for (int v = 0; v < 4; ++v)
-        if (kbase_idx + 4 * grp + v >= u.k1) s[v] = -INFINITY;
+        if (4 * grp + v >= nvis) s[v] = -INFINITY;
     }
     float bm = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
-    bm = fmaxf(bm, __shfl_xor(bm, 16));
-    bm = fmaxf(bm, __shfl_xor(bm, 32));
+    bm = xor16_max(bm);
+    bm = xor32_max(bm);
     const float mn = fmaxf(m, bm);
     const float alpha = (m == -INFINITY) ? 0.f : fast_exp2((m - mn) * c);
     const float mc = mn * c;
@@ -205,89 +254,77 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
     for (int v = 0; v < 4; ++v) pb[v] = (__bf16)p[v];
 #pragma unroll
     for (int tt = 0; tt < NT; ++tt) O[tt] *= alpha;
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    // transpose read: lane (grp, j) addresses row 4grp + j/4, columns 16tt + 4(j%4) .. +4
-    typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
-    const __attribute__((address_space(3))) uint16_t* vl =
-        (const __attribute__((address_space(3))) uint16_t*)(vs + (4 * grp + (col >> 2)) * VS + 4 * (col & 3));
+    const char* vw = vsrc + w * VB;
+    bf16x4 vt[NT];
 #pragma unroll
-    for (int tt = 0; tt < NT; ++tt) {
-      const bf16x4 vt = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(vl + 16 * tt));
-      O[tt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vt, pb, O[tt], 0, 0, 0);
+    for (int tt = 0; tt < NT; ++tt) vt[tt] = lds_read_tr(reinterpret_cast<const uint16_t*>(vw + tr_off[tt]));
+    if constexpr (PARTIAL) {
+      // rows past the last visible key may hold poison under p = 0: zero them
+#pragma unroll
+      for (int tt = 0; tt < NT; ++tt)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (4 * grp + e >= nvis) vt[tt][e] = (__bf16)0.f;
     }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+    for (int tt = 0; tt < NT; ++tt) O[tt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vt[tt], pb, O[tt], 0, 0, 0);
   };
+  using Full = std::integral_constant<bool, false>;
+  using Part = std::integral_constant<bool, true>;
+  const bool last_partial = (kb0 + nb) * kBlock > k1;
 
   {
-    uint4 kA[NKK], vA[NKK], kB[NKK], vB[NKK];
-    int blk = kb0 + w;
-    if (blk < kb1) load(blk, kA, vA);
-    while (blk < kb1) {
-      int nb = blk + 4;
-      if (nb < kb1) load(nb, kB, vB);
-      consume(blk, kA, vA);
-      blk = nb;
-      if (blk >= kb1) break;
-      nb = blk + 4;
-      if (nb < kb1) load(nb, kA, vA);
-      consume(blk, kB, vB);
-      blk = nb;
+    uint4 kA[NKK], kB[NKK];
+    issue(0, kA, sV0);
+    int i = 0;
+    for (; i + 2 < nb; i += 2) {                           // steady state: next block always exists
+      issue(i + 1, kB, sV1);
+      consume(Full{}, i, kA, sV0);
+      issue(i + 2, kA, sV0);                               // sV0 reads above are ahead in the LDS queue
+      consume(Full{}, i + 1, kB, sV1);
+    }
+    if (i + 1 < nb) {                                      // two blocks left
+      issue(i + 1, kB, sV1);
+      consume(Full{}, i, kA, sV0);
+      if (last_partial) consume(Part{}, i + 1, kB, sV1);
+      else consume(Full{}, i + 1, kB, sV1);
+    } else {                                               // one block left
+      if (last_partial) consume(Part{}, i, kA, sV0);
+      else consume(Full{}, i, kA, sV0);
     }
   }
-  lsum += __shfl_xor(lsum, 16);
-  lsum += __shfl_xor(lsum, 32);
+  lsum = xor16_sum(lsum);
+  lsum = xor32_sum(lsum);
 
-  // merge the four waves through LDS (reusing the V staging space)
-  __syncthreads();
-  float* so = reinterpret_cast<float*>(smem);                 // [4][NCOL][D]
-  float* sml = so + 4 * NCOL * D;                             // [4][NCOL][2]
-  if (col < NCOL) {
+  // this wave holds the whole split for its head: write the row or the split's partial
+  if (col < ncols) {
+    const int h = h0 + col;
+    if (n_splits == 1) {
+      const float inv = 1.f / lsum;
+      uint16_t* op = reinterpret_cast<uint16_t*>(a.out) + ((int64_t)t * a.num_q_heads + h) * D;
 #pragma unroll
-    for (int tt = 0; tt < NT; ++tt)
-#pragma unroll
-      for (int v = 0; v < 4; ++v) so[(w * NCOL + col) * D + 16 * tt + 4 * grp + v] = O[tt][v];
-    if (grp == 0) {
-      sml[(w * NCOL + col) * 2] = m;
-      sml[(w * NCOL + col) * 2 + 1] = lsum;
-    }
-  }
-  __syncthreads();
-  for (int idx = threadIdx.x; idx < u.ncols * D; idx += blockDim.x) {
-    const int cc = idx / D;
-    const int dd = idx - cc * D;
-    float mm = -INFINITY;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) mm = fmaxf(mm, sml[(i * NCOL + cc) * 2]);
-    float ll = 0.f, o = 0.f;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float mi = sml[(i * NCOL + cc) * 2];
-      const float f = (mi == -INFINITY) ? 0.f : fast_exp2((mi - mm) * c);
-      ll += sml[(i * NCOL + cc) * 2 + 1] * f;
-      o += so[(i * NCOL + cc) * D + dd] * f;
-    }
-    const int h = u.h0 + cc;
-    if (u.n_splits == 1) {
-      reinterpret_cast<uint16_t*>(a.out)[((int64_t)u.t * a.num_q_heads + h) * D + dd] = f32_to_bf16(o / ll);
+      for (int tt = 0; tt < NT; ++tt) {
+        uint2 pk;
+        pk.x = pack_bf16x2(O[tt][0] * inv, O[tt][1] * inv);
+        pk.y = pack_bf16x2(O[tt][2] * inv, O[tt][3] * inv);
+        *reinterpret_cast<uint2*>(op + 16 * tt + 4 * grp) = pk;
+      }
     } else {
-      const int64_t pidx = ((int64_t)u.row * a.max_splits + u.split) * a.num_q_heads + h;
-      a.part_o[pidx * D + dd] = o;
-      if (dd == 0) {
-        a.part_ml[pidx * 2] = mm * c;     // log2 units
-        a.part_ml[pidx * 2 + 1] = ll;
+      const int64_t pidx = ((int64_t)row * a.max_splits + split) * a.num_q_heads + h;
+      float* po = a.part_o + pidx * D;
+#pragma unroll
+      for (int tt = 0; tt < NT; ++tt)
+        *reinterpret_cast<float4*>(po + 16 * tt + 4 * grp) = make_float4(O[tt][0], O[tt][1], O[tt][2], O[tt][3]);
+      if (grp == 0) {
+        a.part_ml[pidx * 2] = m * c;     // log2 units
+        a.part_ml[pidx * 2 + 1] = lsum;
       }
     }
   }
 }
 
 // ------------------------------------------------------------------------------------------
-// Vector-ALU split kernel: fp32 caches, and bf16 caches whose KV heads serve a single query
-// head (no grouped sharing to amortise, so matrix cores would leave 15 of 16 columns idle).
-// GT query heads per workgroup (GT divides the group size).  Each K/V row is read by a 16-lane
+// Vector-ALU split kernel for fp32 caches.  GT query heads per workgroup (GT divides the group size).  Each K/V row is read by a 16-lane
 // (bf16, d=128) row group with 16-byte loads; q.k is reduced across the group with DPP, and every
 // row group keeps its own running max / sum / accumulator.
 // ------------------------------------------------------------------------------------------
@@ -337,8 +374,10 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeArgs a) {
   const int kb0 = u.k0 / kBlock;
   const int kb1 = (u.k1 + kBlock - 1) / kBlock;
 
+  const int nw = (kb1 - kb0 - w + 3) / 4;             // blocks this wave visits: kb0 + w + 4i
+  BlockWindow win;
   auto load_block = [&](int blk, uint4* kr, uint4* vr) {
-    const int64_t base = (int64_t)table[blk] * kBlock * rs;
+    const int64_t base = (int64_t)win.get(table, kb0 + w, 4, nw, (blk - kb0 - w) >> 2) * kBlock * rs;
 #pragma unroll
     for (int r = 0; r < LPB; ++r) {
       const int64_t off = (base + (int64_t)(r * RPL + rg) * rs) * IO::kEsz;
@@ -535,26 +574,39 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a) {
 
 // ------------------------------------------------------------------------------------------
 namespace {
+// Optional extra dynamic LDS per decode workgroup (PA_DECODE_LDS_PAD bytes): caps how many
+// workgroups share a CU, a tuning knob for the memory system's preferred request depth.
+size_t decode_lds_pad() {
+  static size_t v = [] {
+    const char* e = std::getenv("PA_DECODE_LDS_PAD");
+    long x = e ? std::atol(e) : 0;
+    return (size_t)(x > 0 && x <= 65536 ? x : 0);
+  }();
+  return v;
+}
+
 template <int D>
 hipError_t mfma_dispatch(const DecodeArgs& a, dim3 g, hipStream_t s) {
   const dim3 blk(256);
+  const size_t pad = decode_lds_pad();
   const int hpw = a.heads_per_wg;
-  if (hpw <= 1) decode_mfma_kernel<D, 1><<<g, blk, 0, s>>>(a);
-  else if (hpw <= 2) decode_mfma_kernel<D, 2><<<g, blk, 0, s>>>(a);
-  else if (hpw <= 4) decode_mfma_kernel<D, 4><<<g, blk, 0, s>>>(a);
-  else if (hpw <= 8) decode_mfma_kernel<D, 8><<<g, blk, 0, s>>>(a);
-  else if (hpw <= 16) decode_mfma_kernel<D, 16><<<g, blk, 0, s>>>(a);
+  if (hpw <= 1) decode_mfma_kernel<D, 1><<<g, blk, pad, s>>>(a);
+  else if (hpw <= 2) decode_mfma_kernel<D, 2><<<g, blk, pad, s>>>(a);
+  else if (hpw <= 4) decode_mfma_kernel<D, 4><<<g, blk, pad, s>>>(a);
+  else if (hpw <= 8) decode_mfma_kernel<D, 8><<<g, blk, pad, s>>>(a);
+  else if (hpw <= 16) decode_mfma_kernel<D, 16><<<g, blk, pad, s>>>(a);
   else return hipErrorInvalidValue;
   return hipGetLastError();
 }
 template <int D, bool BF16>
 hipError_t valu_dispatch(const DecodeArgs& a, dim3 g, hipStream_t s) {
   const dim3 blk(256);
+  const size_t pad = decode_lds_pad();
   switch (a.heads_per_wg) {
-    case 1: decode_valu_kernel<D, 1, BF16><<<g, blk, 0, s>>>(a); break;
-    case 2: decode_valu_kernel<D, 2, BF16><<<g, blk, 0, s>>>(a); break;
-    case 4: decode_valu_kernel<D, 4, BF16><<<g, blk, 0, s>>>(a); break;
-    case 8: decode_valu_kernel<D, 8, BF16><<<g, blk, 0, s>>>(a); break;
+    case 1: decode_valu_kernel<D, 1, BF16><<<g, blk, pad, s>>>(a); break;
+    case 2: decode_valu_kernel<D, 2, BF16><<<g, blk, pad, s>>>(a); break;
+    case 4: decode_valu_kernel<D, 4, BF16><<<g, blk, pad, s>>>(a); break;
+    case 8: decode_valu_kernel<D, 8, BF16><<<g, blk, pad, s>>>(a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -563,15 +615,13 @@ hipError_t valu_dispatch(const DecodeArgs& a, dim3 g, hipStream_t s) {
 
 hipError_t launch_decode_split(const DecodeArgs& a, int head_dim, bool bf16, hipStream_t s) {
   const int64_t nzh = (a.group + a.heads_per_wg - 1) / a.heads_per_wg;
-  const int64_t grid = (int64_t)a.num_kv_heads * nzh * a.max_splits * a.num_rows;
+  const int64_t heads = bf16 ? (a.num_kv_heads + 3) / 4 : a.num_kv_heads;   // MFMA: 4 KV heads per WG
+  const int64_t grid = heads * nzh * a.max_splits * a.num_rows;
   if (grid <= 0 || grid > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
   const dim3 g((unsigned)grid);
-  if (bf16 && a.group > 1) {
+  if (bf16) {
     if (head_dim == 128) return mfma_dispatch<128>(a, g, s);
     if (head_dim == 64) return mfma_dispatch<64>(a, g, s);
-  } else if (bf16) {
-    if (head_dim == 128) return valu_dispatch<128, true>(a, g, s);
-    if (head_dim == 64) return valu_dispatch<64, true>(a, g, s);
   } else {
     if (head_dim == 128) return valu_dispatch<128, false>(a, g, s);
     if (head_dim == 64) return valu_dispatch<64, false>(a, g, s);

@@ -8,7 +8,7 @@ namespace pa {
 
 // Query rows with q_len == 1 (and, for fp32 caches, every query row) run on the split-KV
 // decode kernels; bf16 requests with q_len >= 2 run on the MFMA tile kernel.
-constexpr int kDefaultSplitTokens = 256;   // keys per decode split (multiple of 64)
+constexpr int kDefaultSplitTokens = 256;   // keys per decode split (multiple of 16, at most 1024)
 constexpr int kTileRows = 128;             // query rows (position x head-in-group) per MFMA tile
 constexpr int kTileKeys = 64;              // keys per MFMA K/V tile
 

@@ -50,7 +50,12 @@ __global__ __launch_bounds__(256, 2) void prefill_tile_kernel(TileArgs a) {
   constexpr int NKK = D / 16;               // MFMA k-steps over d
   constexpr int NDT = D / 32;               // 32-wide d tiles of O^T
   static_assert(kTileKeys == 4 * kBlock, "one cache block per wave and tile");
-  __shared__ __align__(16) char smem[2 * 2 * TILEB];   // [buf][K,V][tile]
+  // one LDS variable per buffer and tensor: the compiler then knows that loads landing in one
+  // buffer never alias reads of the other, and does not wait for them before those reads
+  __shared__ __align__(16) char sK0[TILEB];
+  __shared__ __align__(16) char sV0[TILEB];
+  __shared__ __align__(16) char sK1[TILEB];
+  __shared__ __align__(16) char sV1[TILEB];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -112,24 +117,29 @@ __global__ __launch_bounds__(256, 2) void prefill_tile_kernel(TileArgs a) {
   // ---- staging: wave w loads key rows 16w..16w+15 of the tile (one cache block) ----
   // load i of the block covers rows RPI*i .. RPI*i + RPI - 1; lane -> (row lane / CPR, physical
   // chunk lane % CPR), which holds logical chunk (lane % CPR) ^ swz(row).
-  int lane_off[IPB];                              // byte offset within the block, per load
+  // wave w visits blocks 4kt + w; those entirely below the length are taken from a window
+  const int n_full = (sl / kBlock - w + 3) / 4;   // count of kt with (4kt + w + 1) * 16 <= sl
+  BlockWindow win;
+  uint32_t lane_off[IPB];                         // byte offset within the block, per load
 #pragma unroll
   for (int i = 0; i < IPB; ++i) {
     const int rr = RPI * i + lane / CPR;          // row within the block (and within the wave's 16)
     const int q = (lane % CPR) ^ swz<D>(16 * w + rr);
-    lane_off[i] = (int)(rr * rs * 2) + q * 16;
+    lane_off[i] = (uint32_t)(rr * rs * 2) + q * 16;
   }
-  auto stage = [&](int kt, int buf) {
-    char* kl = smem + (2 * buf) * TILEB + 16 * w * ROWB;
-    char* vl = kl + TILEB;
+  auto stage = [&](int kt, char* kdst, char* vdst) {
+    char* kl = kdst + 16 * w * ROWB;
+    char* vl = vdst + 16 * w * ROWB;
     const int blk = 4 * kt + w;
     if ((blk + 1) * kBlock <= sl) {               // whole block valid: one uniform table entry
-      const int64_t boff = (int64_t)table[blk] * kBlock * rs * 2;
+      const int64_t boff = (int64_t)win.get(table, w, 4, n_full, kt) * (kBlock * rs * 2);
+      const char* kb = kbase + boff;               // uniform block base; lanes add 32-bit offsets
+      const char* vb = vbase + boff;
 #pragma unroll
       for (int i = 0; i < IPB; ++i) {
-        __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(kbase + boff + lane_off[i]),
+        __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(kb + lane_off[i]),
                                          (__attribute__((address_space(3))) void*)(kl + 1024 * i), 16, 0, 0);
-        __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(vbase + boff + lane_off[i]),
+        __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(vb + lane_off[i]),
                                          (__attribute__((address_space(3))) void*)(vl + 1024 * i), 16, 0, 0);
       }
     } else {                                      // last block: clamp rows past the length
@@ -154,44 +164,41 @@ __global__ __launch_bounds__(256, 2) void prefill_tile_kernel(TileArgs a) {
 #pragma unroll
     for (int v = 0; v < 16; ++v) O[dt][v] = 0.f;
 
-  // K operand: row 32st + l32, logical chunk 2kk + half
-  int k_off[2][NKK];
+  // K operand: row 32st + l32, logical chunk 2kk + half.  swz(r) depends on r mod 16 only, so the
+  // second sub-tile (rows + 32) is the same offset plus an immediate.
+  uint32_t k_off[NKK];
 #pragma unroll
-  for (int st = 0; st < 2; ++st)
-#pragma unroll
-    for (int kk = 0; kk < NKK; ++kk) {
-      const int r = 32 * st + l32;
-      k_off[st][kk] = r * ROWB + (((2 * kk + half) ^ swz<D>(r)) * 16);
-    }
+  for (int kk = 0; kk < NKK; ++kk) k_off[kk] = l32 * ROWB + (((2 * kk + half) ^ swz<D>(l32)) * 16);
   // V transpose-read coordinates: 16-lane group (gsel, j = 4e + cq) reads row R + e, columns
   // 32dt + 16gsel + 4cq .. +3 (8 bytes), i.e. logical chunk 4dt + 2gsel + cq/2, half cq & 1.
   const int trj = lane & 15;
   const int gsel = (lane >> 4) & 1;
   const int tre = trj >> 2;
+  // rows 16kk + 4half + tre (lo) and + 8 (hi): swz of those rows does not depend on kk
+  uint32_t v_off[2][NDT];
+#pragma unroll
+  for (int dt = 0; dt < NDT; ++dt) {
+    const int lq = 4 * dt + 2 * gsel + (trj & 3) / 2;           // logical chunk
+    const int sub = (trj & 1) * 8;                              // byte half within the chunk
+    const int r_lo = 4 * half + tre, r_hi = r_lo + 8;
+    v_off[0][dt] = r_lo * ROWB + ((lq ^ swz<D>(r_lo)) * 16) + sub;
+    v_off[1][dt] = r_hi * ROWB + ((lq ^ swz<D>(r_hi)) * 16) + sub;
+  }
 
-  stage(0, 0);
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();
-
-  for (int kt = 0; kt < n_kt; ++kt) {
-    const int buf = kt & 1;
-    const bool more = kt + 1 < n_kt;
-    if (more) stage(kt + 1, buf ^ 1);             // in flight during this tile's math
-    const char* kl = smem + (2 * buf) * TILEB;
-    const char* vl = kl + TILEB;
-
+  // one key tile: S^T, mask, online softmax, O^T += V^T P^T, reading (kl, vl)
+  auto tile_math = [&](int kt, const char* kl, const char* vl) {
     // ---- S^T = K Q^T : two 32-key sub-tiles, chains interleaved, operands read one step ahead ----
     floatx16 S0, S1;
 #pragma unroll
     for (int v = 0; v < 16; ++v) { S0[v] = 0.f; S1[v] = 0.f; }
-    bf16x8 a0 = *reinterpret_cast<const bf16x8*>(kl + k_off[0][0]);
-    bf16x8 a1 = *reinterpret_cast<const bf16x8*>(kl + k_off[1][0]);
+    bf16x8 a0 = *reinterpret_cast<const bf16x8*>(kl + k_off[0]);
+    bf16x8 a1 = *reinterpret_cast<const bf16x8*>(kl + k_off[0] + 32 * ROWB);
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk) {
       bf16x8 n0 = a0, n1 = a1;
       if (kk + 1 < NKK) {
-        n0 = *reinterpret_cast<const bf16x8*>(kl + k_off[0][kk + 1]);
-        n1 = *reinterpret_cast<const bf16x8*>(kl + k_off[1][kk + 1]);
+        n0 = *reinterpret_cast<const bf16x8*>(kl + k_off[kk + 1]);
+        n1 = *reinterpret_cast<const bf16x8*>(kl + k_off[kk + 1] + 32 * ROWB);
       }
       S0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qreg[kk], S0, 0, 0, 0);
       S1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qreg[kk], S1, 0, 0, 0);
@@ -241,14 +248,10 @@ __global__ __launch_bounds__(256, 2) void prefill_tile_kernel(TileArgs a) {
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
       bf16x4 lo[NDT], hi[NDT];
-      const int r_lo = 16 * kk + 4 * half + tre;
-      const int r_hi = r_lo + 8;
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt) {
-        const int lq = 4 * dt + 2 * gsel + (trj & 3) / 2;      // logical chunk
-        const int sub = (trj & 1) * 8;                         // byte half within the chunk
-        lo[dt] = lds_read_tr(reinterpret_cast<const uint16_t*>(vl + r_lo * ROWB + ((lq ^ swz<D>(r_lo)) * 16) + sub));
-        hi[dt] = lds_read_tr(reinterpret_cast<const uint16_t*>(vl + r_hi * ROWB + ((lq ^ swz<D>(r_hi)) * 16) + sub));
+        lo[dt] = lds_read_tr(reinterpret_cast<const uint16_t*>(vl + v_off[0][dt] + 16 * kk * ROWB));
+        hi[dt] = lds_read_tr(reinterpret_cast<const uint16_t*>(vl + v_off[1][dt] + 16 * kk * ROWB));
       }
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt) {
@@ -256,7 +259,22 @@ __global__ __launch_bounds__(256, 2) void prefill_tile_kernel(TileArgs a) {
         O[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop, P[kk], O[dt], 0, 0, 0);
       }
     }
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this thread's loads of the next tile landed
+  };
+
+  stage(0, sK0, sV0);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+
+  // two tiles per iteration so that each buffer is a fixed LDS variable
+  for (int kt = 0; kt < n_kt; kt += 2) {
+    if (kt + 1 < n_kt) stage(kt + 1, sK1, sV1);     // in flight during this tile's math
+    tile_math(kt, sK0, sV0);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (kt + 1 >= n_kt) break;
+    if (kt + 2 < n_kt) stage(kt + 2, sK0, sV0);
+    tile_math(kt + 1, sK1, sV1);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
   }
 

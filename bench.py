@@ -32,6 +32,30 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+KERNEL_SOURCES = {
+    "decode_split": ["attention_paged_kv_amd/csrc/pa_decode.hip", "attention_paged_kv_amd/csrc/pa_common.h"],
+    "prefill_tile": ["attention_paged_kv_amd/csrc/pa_prefill.hip", "attention_paged_kv_amd/csrc/pa_common.h"],
+}
+
+
+def measured_traffic(kernel, workload):
+    """HBM bytes per launch of `kernel` on `workload` from the committed counter summary
+    (profiles/hbm_traffic.txt), or None if absent or taken on a different kernel source."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "hbm_traffic.txt")
+    if not os.path.exists(path) or kernel not in KERNEL_SOURCES:
+        return None
+    m = hashlib.sha256()
+    for fn in KERNEL_SOURCES[kernel]:
+        m.update(open(os.path.join(ROOT, fn), "rb").read())
+    src = m.hexdigest()[:16]
+    for line in open(path):
+        f = line.split()
+        if len(f) == 8 and not line.startswith("#") and f[0] == kernel and f[1] == workload and f[7] == src:
+            return int(f[6])
+    return None
+
+
 def cpu_baseline(w, steps, is_decode, kv_bytes):
     """Time the fp64 CPU oracle on the host cores over a bounded sample of the same workload.
 
@@ -151,7 +175,7 @@ def main():
                            out=torch.empty(st.q.shape, dtype=tdt, device=dev)))
     ws_need = max(pa.workspace_size(st.num_seqs, st.num_tokens, st.block_tables.shape[1], w.num_q_heads, kc)
                   for st in steps)
-    ws = torch.empty(max(ws_need, 256), dtype=torch.uint8, device=dev)
+    ws = torch.zeros(max(ws_need, 256), dtype=torch.uint8, device=dev)
 
     def run_step():
         for d in dsteps:
@@ -205,7 +229,8 @@ def main():
         per_launch = kv_bytes / dk["launches_per_step"]
         achieved = per_launch / (dk["avg_us"] * 1e-6) / 1e9
         roof = {"bound": "hbm", "kernel": "decode_split", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                "traffic": measured_traffic("decode_split", w.name),
                 "algorithmic_bytes_per_launch": int(per_launch)}
     elif w.dtype == "f32":
         unit = "TFLOP/s"
@@ -224,7 +249,8 @@ def main():
         achieved = per_launch / (tk["avg_us"] * 1e-6) / 1e12
         roof = {"bound": "mfma", "kernel": "prefill_tile", "achieved": round(achieved, 1),
                 "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / BF16_PEAK_TFLOPS, 4),
-                "traffic": None, "algorithmic_flops_per_launch": int(per_launch)}
+                "traffic": measured_traffic("prefill_tile", w.name),
+                "algorithmic_flops_per_launch": int(per_launch)}
 
     cpu = None
     if not args.no_cpu_baseline:
