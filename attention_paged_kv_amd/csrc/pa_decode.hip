@@ -574,39 +574,26 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a) {
 
 // ------------------------------------------------------------------------------------------
 namespace {
-// Optional extra dynamic LDS per decode workgroup (PA_DECODE_LDS_PAD bytes): caps how many
-// workgroups share a CU, a tuning knob for the memory system's preferred request depth.
-size_t decode_lds_pad() {
-  static size_t v = [] {
-    const char* e = std::getenv("PA_DECODE_LDS_PAD");
-    long x = e ? std::atol(e) : 0;
-    return (size_t)(x > 0 && x <= 65536 ? x : 0);
-  }();
-  return v;
-}
-
 template <int D>
 hipError_t mfma_dispatch(const DecodeArgs& a, dim3 g, hipStream_t s) {
   const dim3 blk(256);
-  const size_t pad = decode_lds_pad();
   const int hpw = a.heads_per_wg;
-  if (hpw <= 1) decode_mfma_kernel<D, 1><<<g, blk, pad, s>>>(a);
-  else if (hpw <= 2) decode_mfma_kernel<D, 2><<<g, blk, pad, s>>>(a);
-  else if (hpw <= 4) decode_mfma_kernel<D, 4><<<g, blk, pad, s>>>(a);
-  else if (hpw <= 8) decode_mfma_kernel<D, 8><<<g, blk, pad, s>>>(a);
-  else if (hpw <= 16) decode_mfma_kernel<D, 16><<<g, blk, pad, s>>>(a);
+  if (hpw <= 1) decode_mfma_kernel<D, 1><<<g, blk, 0, s>>>(a);
+  else if (hpw <= 2) decode_mfma_kernel<D, 2><<<g, blk, 0, s>>>(a);
+  else if (hpw <= 4) decode_mfma_kernel<D, 4><<<g, blk, 0, s>>>(a);
+  else if (hpw <= 8) decode_mfma_kernel<D, 8><<<g, blk, 0, s>>>(a);
+  else if (hpw <= 16) decode_mfma_kernel<D, 16><<<g, blk, 0, s>>>(a);
   else return hipErrorInvalidValue;
   return hipGetLastError();
 }
 template <int D, bool BF16>
 hipError_t valu_dispatch(const DecodeArgs& a, dim3 g, hipStream_t s) {
   const dim3 blk(256);
-  const size_t pad = decode_lds_pad();
   switch (a.heads_per_wg) {
-    case 1: decode_valu_kernel<D, 1, BF16><<<g, blk, pad, s>>>(a); break;
-    case 2: decode_valu_kernel<D, 2, BF16><<<g, blk, pad, s>>>(a); break;
-    case 4: decode_valu_kernel<D, 4, BF16><<<g, blk, pad, s>>>(a); break;
-    case 8: decode_valu_kernel<D, 8, BF16><<<g, blk, pad, s>>>(a); break;
+    case 1: decode_valu_kernel<D, 1, BF16><<<g, blk, 0, s>>>(a); break;
+    case 2: decode_valu_kernel<D, 2, BF16><<<g, blk, 0, s>>>(a); break;
+    case 4: decode_valu_kernel<D, 4, BF16><<<g, blk, 0, s>>>(a); break;
+    case 8: decode_valu_kernel<D, 8, BF16><<<g, blk, 0, s>>>(a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
