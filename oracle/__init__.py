@@ -28,7 +28,7 @@ def _load():
         P, I, D = ctypes.c_void_p, ctypes.c_int32, ctypes.c_double
         lib.pa_oracle_append.argtypes = [P, P, P, I, P, P, I, I, I, I, ctypes.c_char_p, I]
         lib.pa_oracle_append.restype = I
-        lib.pa_oracle_attention.argtypes = [P, I, I, P, P, I, I, I, I, P, I, I, P, P, D, P, I, P, P, I,
+        lib.pa_oracle_attention.argtypes = [P, I, I, P, P, I, I, I, I, P, I, I, P, P, D, I, P, I, P, P, I,
                                             ctypes.c_char_p, I]
         lib.pa_oracle_attention.restype = I
         lib.pa_oracle_f64_to_bf16.argtypes = [D]
@@ -75,8 +75,9 @@ def append(k, v, slot_mapping, k_cache, v_cache):
 
 
 def attention(q, k_cache, v_cache, block_tables, seq_lens, query_start_loc, scale, rows=None,
-              want_f64=False, num_threads=None):
-    """Causal attention of every (or the listed) query token row over its request's paged keys.
+              want_f64=False, num_threads=None, window=0):
+    """Causal attention of every (or the listed) query token row over its request's paged keys
+    (with ``window`` > 0, only each row's ``window`` most recent keys).
 
     Returns (out, out_f64): ``out`` in the storage dtype of ``q`` (float32 or uint16 bf16 bits),
     ``out_f64`` the unrounded double result (or None).  Rows not computed are left zero.
@@ -99,15 +100,15 @@ def attention(q, k_cache, v_cache, block_tables, seq_lens, query_start_loc, scal
     err = ctypes.create_string_buffer(256)
     rc = lib.pa_oracle_attention(_ptr(q), T, Hq, _ptr(np.ascontiguousarray(k_cache)),
                                  _ptr(np.ascontiguousarray(v_cache)), NB, Hkv, d, dtype, _ptr(block_tables), B, MB,
-                                 _ptr(seq_lens), _ptr(query_start_loc), float(scale), _ptr(rows_a),
+                                 _ptr(seq_lens), _ptr(query_start_loc), float(scale), int(window), _ptr(rows_a),
                                  0 if rows_a is None else int(rows_a.shape[0]), _ptr(out), _ptr(out64), nt, err, 256)
     if rc != 0:
         raise OracleError(err.value.decode())
     return out, out64
 
 
-def run_step(w, step, k_cache, v_cache, rows=None, want_f64=False, num_threads=None):
+def run_step(w, step, k_cache, v_cache, rows=None, want_f64=False, num_threads=None, window=0):
     """Append the step's K/V into (k_cache, v_cache) in place, then attend; returns (out, out_f64)."""
     append(step.k_new, step.v_new, step.slot_mapping, k_cache, v_cache)
     return attention(step.q, k_cache, v_cache, step.block_tables, step.seq_lens, step.query_start_loc, w.scale,
-                     rows=rows, want_f64=want_f64, num_threads=num_threads)
+                     rows=rows, want_f64=want_f64, num_threads=num_threads, window=window)

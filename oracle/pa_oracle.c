@@ -18,13 +18,17 @@
  *                 then the address), scores are scale * q.k for every key, keys j > p are set to
  *                 -inf (P3 §1.1, §2.1: position i depends only on 0..i, the upper triangle is masked
  *                 before the softmax), a row softmax follows and the weights multiply V
- *                 (P3 §3.1, §5.1: softmax(q K^T) V over all cached keys).
+ *                 (P3 §3.1, §5.1: softmax(q K^T) V over all cached keys).  With a sliding window
+ *                 W > 0, keys j < p - W + 1 are also set to -inf (P3 §6.3, P2 §5.2: keep only the
+ *                 most recent W tokens' K/V); keys that no row can see are not gathered.
  * Precision: inputs are widened exactly to double (bf16: bits << 16), every sum is in double,
  * and the result is rounded once to the output dtype (bf16: nearest, ties to even).
  *
  * Parity: pinned by the tests against a library dense causal softmax on tiny inputs, closed
  * forms (constant V, zero K, single visible key), argmax probes, block-permutation invariance,
- * chunked == one-shot and decode == last prefill row.  No page prints attention output values.
+ * chunked == one-shot and decode == last prefill row; the window by a library softmax over each
+ * row's key slice, W >= context == no window, W = 1 == own V row, and a dominant key one step
+ * outside / at the window's edge.  No page prints attention output values.
  */
 #include <math.h>
 #include <pthread.h>
@@ -127,6 +131,7 @@ typedef struct {
   const void* q;
   int dtype, Hq, Hkv, d;
   int G;
+  int window;         /* > 0: row p sees only keys p - window + 1 .. p */
   double scale;
   const double* Kb;   /* gathered keys   [s][Hkv][d] */
   const double* Vb;   /* gathered values [s][Hkv][d] */
@@ -155,15 +160,18 @@ static void row_head(const job_t* J, int r, int h) {
     for (int c = 0; c < d; ++c) dot += qv[c] * kr[c];
     x[j] = J->scale * dot;
   }
-  /* explicit causal mask */
+  /* explicit causal mask, and the sliding-window lower bound when a window is set */
   for (int j = 0; j < s; ++j)
     if (j > p) x[j] = -INFINITY;
+  if (J->window > 0)
+    for (int j = 0; j < s; ++j)
+      if (j < p - J->window + 1) x[j] = -INFINITY;
   double m = -INFINITY;
   for (int j = 0; j < s; ++j)
     if (x[j] > m) m = x[j];
   double l = 0.0;
   for (int j = 0; j < s; ++j) {
-    double e = (j <= p) ? exp(x[j] - m) : 0.0;
+    double e = (x[j] == -INFINITY) ? 0.0 : exp(x[j] - m);
     if (e == 0.0) continue;
     l += e;
     const double* vr = J->Vb + ((size_t)j * J->Hkv + g) * d;
@@ -194,13 +202,13 @@ typedef struct {
   const int32_t* table;
   double* Kb;
   double* Vb;
-  int s, tid, nthreads;
+  int s, j0, tid, nthreads;   /* gather keys j0 .. s-1 (earlier ones are never visible) */
 } gather_t;
 
 static void* gather_worker(void* arg) {
   const gather_t* Gt = (const gather_t*)arg;
   const size_t row = (size_t)Gt->Hkv * Gt->d;
-  for (int j = Gt->tid; j < Gt->s; j += Gt->nthreads) {
+  for (int j = Gt->j0 + Gt->tid; j < Gt->s; j += Gt->nthreads) {
     const int blk = Gt->table[j / ORACLE_BLOCK];
     const size_t src = ((size_t)blk * ORACLE_BLOCK + (size_t)(j % ORACLE_BLOCK)) * row;
     for (size_t c = 0; c < row; ++c) {
@@ -215,11 +223,12 @@ int pa_oracle_attention(const void* q, int32_t num_tokens, int32_t num_q_heads,
                         const void* k_cache, const void* v_cache, int32_t num_blocks, int32_t num_kv_heads,
                         int32_t head_dim, int32_t dtype, const int32_t* block_tables, int32_t num_seqs,
                         int32_t max_blocks, const int32_t* seq_lens, const int32_t* query_start_loc,
-                        double scale, const int32_t* rows, int32_t num_rows, void* out, double* out_f64,
-                        int32_t num_threads, char* err, int32_t err_len) {
+                        double scale, int32_t window, const int32_t* rows, int32_t num_rows, void* out,
+                        double* out_f64, int32_t num_threads, char* err, int32_t err_len) {
   char m[256];
   if (num_seqs < 1 || num_tokens < 0 || num_q_heads < 1 || num_kv_heads < 1 || head_dim < 1 ||
-      num_q_heads % num_kv_heads != 0 || (dtype != OR_F32 && dtype != OR_BF16) || max_blocks < 1) {
+      num_q_heads % num_kv_heads != 0 || (dtype != OR_F32 && dtype != OR_BF16) || max_blocks < 1 ||
+      window < 0) {
     set_err(err, err_len, "bad sizes");
     return 1;
   }
@@ -236,7 +245,10 @@ int pa_oracle_attention(const void* q, int32_t num_tokens, int32_t num_q_heads,
       set_err(err, err_len, m);
       return 1;
     }
-    for (int j = 0; j < (s + ORACLE_BLOCK - 1) / ORACLE_BLOCK; ++j) {
+    /* with a window, blocks wholly before the first row's window are never read */
+    int first = 0;
+    if (window > 0 && s - ql - window + 1 > 0) first = (s - ql - window + 1) / ORACLE_BLOCK;
+    for (int j = first; j < (s + ORACLE_BLOCK - 1) / ORACLE_BLOCK; ++j) {
       int blk = block_tables[(size_t)b * max_blocks + j];
       if (blk < 0 || blk >= num_blocks) {
         snprintf(m, sizeof m, "request %d: block table entry %d = %d outside the pool", b, j, blk);
@@ -273,8 +285,9 @@ int pa_oracle_attention(const void* q, int32_t num_tokens, int32_t num_q_heads,
       if (want[q0 + r]) rl[nr++] = r;
     /* explicit gather of this request's keys and values through its block table */
     const size_t row = (size_t)num_kv_heads * head_dim;
-    double* Kb = (double*)malloc(sizeof(double) * (size_t)s * row);
-    double* Vb = (double*)malloc(sizeof(double) * (size_t)s * row);
+    const int j0 = (window > 0 && s - ql - window + 1 > 0) ? (s - ql - window + 1) : 0;
+    double* Kb = (double*)calloc((size_t)s * row, sizeof(double));
+    double* Vb = (double*)calloc((size_t)s * row, sizeof(double));
     if (!Kb || !Vb) {
       set_err(err, err_len, "oom");
       free(Kb); free(Vb); free(rl);
@@ -284,7 +297,7 @@ int pa_oracle_attention(const void* q, int32_t num_tokens, int32_t num_q_heads,
     gather_t* gt = (gather_t*)malloc(sizeof(gather_t) * (size_t)num_threads);
     for (int i = 0; i < num_threads; ++i) {
       gather_t g0 = {k_cache, v_cache, dtype, num_kv_heads, head_dim, block_tables + (size_t)b * max_blocks,
-                     Kb, Vb, s, i, num_threads};
+                     Kb, Vb, s, j0, i, num_threads};
       gt[i] = g0;
       pthread_create(&th[i], NULL, gather_worker, &gt[i]);
     }
@@ -292,9 +305,9 @@ int pa_oracle_attention(const void* q, int32_t num_tokens, int32_t num_q_heads,
     free(gt);
     job_t* jobs = (job_t*)malloc(sizeof(job_t) * (size_t)num_threads);
     for (int i = 0; i < num_threads; ++i) {
-      job_t j0 = {q, dtype, num_q_heads, num_kv_heads, head_dim, num_q_heads / num_kv_heads, scale,
+      job_t jb = {q, dtype, num_q_heads, num_kv_heads, head_dim, num_q_heads / num_kv_heads, window, scale,
                   Kb, Vb, s, s - ql, q0, rl, nr, out, out_f64, num_threads, i};
-      jobs[i] = j0;
+      jobs[i] = jb;
       pthread_create(&th[i], NULL, worker, &jobs[i]);
     }
     for (int i = 0; i < num_threads; ++i) pthread_join(th[i], NULL);

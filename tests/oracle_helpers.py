@@ -5,12 +5,12 @@ from attention_paged_kv_amd import workloads as W
 import oracle
 
 
-def oracle_step(w, step=None, rows=None, want_f64=True, caches=None):
+def oracle_step(w, step=None, rows=None, want_f64=True, caches=None, window=0):
     """Run one step through the oracle on copies of the workload's caches."""
     step = step if step is not None else w.steps[0]
     kc = (caches[0] if caches else w.k_cache0).copy()
     vc = (caches[1] if caches else w.v_cache0).copy()
-    out, out64 = oracle.run_step(w, step, kc, vc, rows=rows, want_f64=want_f64)
+    out, out64 = oracle.run_step(w, step, kc, vc, rows=rows, want_f64=want_f64, window=window)
     return out, out64, kc, vc
 
 

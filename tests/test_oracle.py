@@ -12,7 +12,7 @@ import torch
 
 from attention_paged_kv_amd import workloads as W
 import oracle
-from tests.oracle_helpers import oracle_step
+from tests.oracle_helpers import logical_kv, oracle_step
 
 TOL64 = 1e-12
 
@@ -319,3 +319,119 @@ def test_bf16_rounding_is_single_step_from_double():
     assert oracle.f64_to_bf16(2.0 ** -133) == 0x0001
     assert oracle.f64_to_bf16(2.0 ** -134) == 0x0000          # tie at half the smallest subnormal -> even (0)
     assert oracle.f64_to_bf16(2.0 ** -134 * 1.0000001) == 0x0001
+
+
+# --------------------------------------------------------------------------------------------
+# 7. Sliding window (P2 §5.2 and P3 §6.3: only the most recent W tokens' K/V take part).  Reading:
+#    the query at position p sees keys p - W + 1 .. p, itself included; W = 0 means no window.
+# --------------------------------------------------------------------------------------------
+def _sdpa_rows_over_windows(q, k, v, scale, ctx, window):
+    """Library softmax(q K^T) V per query row over the contiguous slice of keys its window covers."""
+    Hq, Hkv = q.shape[1], k.shape[1]
+    out = np.empty_like(q)
+    for r in range(q.shape[0]):
+        p = ctx + r
+        lo = max(0, p - window + 1)
+        qt = torch.from_numpy(q[r:r + 1]).permute(1, 0, 2).unsqueeze(0)
+        kt = torch.from_numpy(k[lo:p + 1]).permute(1, 0, 2).repeat_interleave(Hq // Hkv, dim=0).unsqueeze(0)
+        vt = torch.from_numpy(v[lo:p + 1]).permute(1, 0, 2).repeat_interleave(Hq // Hkv, dim=0).unsqueeze(0)
+        o = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, scale=scale)
+        out[r] = o.squeeze(0).permute(1, 0, 2).numpy()[0]
+    return out
+
+
+@pytest.mark.parametrize("lens,qlens,window", [
+    ([70], [70], 1), ([70], [70], 16), ([70], [70], 17), ([100, 33, 64], [100, 1, 9], 31),
+    ([300, 47], [5, 1], 64), ([40], [40], 39),
+])
+def test_window_matches_library_softmax_over_each_rows_window(lens, qlens, window):
+    w = W.make_batch(40 + window, lens, qlens, 4, 2, 64, "bf16",
+                     num_blocks=sum((s + 15) // 16 for s in lens) + 4)
+    st = w.steps[0]
+    _, o64, kc, vc = oracle_step(w, window=window)
+    for b in range(len(lens)):
+        a, e = st.query_start_loc[b], st.query_start_loc[b + 1]
+        k, v = logical_kv(w, st, kc, vc, b)
+        ref = _sdpa_rows_over_windows(f64(w, st.q[a:e]), k, v, w.scale, int(st.seq_lens[b]) - (e - a), window)
+        assert np.max(np.abs(o64[a:e] - ref)) <= TOL64, b
+
+
+@pytest.mark.parametrize("window", [100, 101, 5000])
+def test_window_at_least_the_context_is_full_causal_bitwise(window):
+    w = W.make_batch(8, [100, 40], [100, 3], 4, 2, 64, "bf16", num_blocks=12)
+    full, _, _, _ = oracle_step(w)
+    win, _, _, _ = oracle_step(w, window=window)
+    assert np.array_equal(full, win)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_window_one_returns_own_value_exactly(dtype):
+    """With W = 1 each row sees only its own key, so the output is its own V row."""
+    w = W.make_batch(9, [50, 20], [50, 4], 4, 4, 64, dtype, num_blocks=10)
+    st = w.steps[0]
+    out, _, _, _ = oracle_step(w, window=1)
+    assert np.array_equal(out, st.v_new)
+
+
+def test_window_chunked_equals_one_shot_and_decode_equals_last_row():
+    S, Wn = 90, 23
+    w = W.make_batch(12, [S], [S], 4, 2, 64, "bf16", num_blocks=8)
+    one, _, _, _ = oracle_step(w, window=Wn)
+    cw = W.chunked_steps(w, [30, 17, 1, 1, 41])
+    kc, vc = w.k_cache0.copy(), w.v_cache0.copy()
+    c = 0
+    for st in cw.steps:
+        o, _ = oracle.run_step(cw, st, kc, vc, window=Wn)
+        n = o.shape[0]
+        assert np.array_equal(o, one[c:c + n]), c
+        c += n
+
+
+def test_key_just_outside_window_is_masked_and_edge_key_is_not():
+    """A dominant key at position p - W (one step too old) has no effect on row p; at p - W + 1
+    it takes the whole softmax weight."""
+    S, Wn, d = 64, 20, 64
+    w = W.make_batch(3, [S], [1], 2, 2, d, "f32", num_blocks=6)
+    st = w.steps[0]
+    base, _, _, _ = oracle_step(w, window=Wn)
+    kc, vc = w.k_cache0.copy(), w.v_cache0.copy()
+    NB = kc.shape[0]
+    p = S - 1
+    for pos, inside in [(p - Wn, False), (p - Wn + 1, True)]:
+        k2, v2 = kc.copy(), vc.copy()
+        slot = W.slots_for(st.block_tables, 0, np.array([pos]))[0]
+        k2.reshape(NB * 16, 2, d)[slot] = 1e3 * st.q[0]
+        out, _, _, _ = oracle_step(w, caches=(k2, v2), window=Wn)
+        if inside:
+            assert np.array_equal(out[0], v2.reshape(NB * 16, 2, d)[slot])
+        else:
+            assert np.array_equal(out[0], base[0])
+
+
+def test_window_poison_and_unmapped_blocks_before_the_window_are_never_read():
+    """Blocks wholly before the first row's window may hold anything, and their table entries may be
+    outside the pool (a cache that drops old blocks); the output is unchanged."""
+    lens, ql, Wn = [200, 97], [3, 1], 40
+    w = W.make_batch(6, lens, ql, 4, 2, 64, "bf16", num_blocks=24)
+    st = w.steps[0]
+    ref, _, _, _ = oracle_step(w, window=Wn)
+    kp, vp = W.poison_cache(w.k_cache0.shape, "bf16")
+    tables = st.block_tables.copy()
+    for b in range(2):
+        s, q = lens[b], ql[b]
+        lo = s - q - Wn + 1
+        keep = np.arange(max(0, lo), s - q)
+        sl = W.slots_for(st.block_tables, b, keep)
+        kp.reshape(-1, 2, 64)[sl] = w.k_cache0.reshape(-1, 2, 64)[sl]
+        vp.reshape(-1, 2, 64)[sl] = w.v_cache0.reshape(-1, 2, 64)[sl]
+        tables[b, :max(0, lo) // 16] = -1
+    st2 = W.Step(q=st.q, k_new=st.k_new, v_new=st.v_new, slot_mapping=st.slot_mapping, seq_lens=st.seq_lens,
+                 query_start_loc=st.query_start_loc, block_tables=tables)
+    out, _, _, _ = oracle_step(w, st2, caches=(kp, vp), window=Wn)
+    assert np.array_equal(out, ref)
+
+
+def test_window_rejects_negative():
+    w = W.make_batch(1, [20], [20], 2, 2, 64, "f32", num_blocks=3)
+    with pytest.raises(Exception):
+        oracle_step(w, window=-1)
