@@ -5,7 +5,7 @@ device memory and the current stream; every step of the computation runs in the 
 kernels.  There is no fallback: if the library is missing or built for another ABI, calls raise.
 
     append_kv(k, v, slot_mapping, k_cache, v_cache)
-    attention(q, k_cache, v_cache, block_tables, seq_lens, query_start_loc, scale, out)
+    attention(q, k_cache, v_cache, block_tables, seq_lens, query_start_loc, scale, out, window=0)
 
 Caches are ``[num_blocks, 16, num_kv_heads, head_dim]`` tensors (float32 or bfloat16),
 ``q``/``out`` are ``[num_tokens, num_q_heads, head_dim]``, indices are int32.
@@ -15,7 +15,7 @@ from __future__ import annotations
 import ctypes
 import os
 
-ABI_VERSION = 1
+ABI_VERSION = 2
 BLOCK_SIZE = 16
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libpa.so")
@@ -33,6 +33,10 @@ class PAError(RuntimeError):
 class _CacheDesc(ctypes.Structure):
     _fields_ = [("num_blocks", ctypes.c_int32), ("block_size", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32),
                 ("head_dim", ctypes.c_int32), ("dtype", ctypes.c_int32)]
+
+
+class _AttnOpts(ctypes.Structure):
+    _fields_ = [("sliding_window", ctypes.c_int32)]
 
 
 def load_library(path: str = LIB_PATH):
@@ -56,6 +60,9 @@ def load_library(path: str = LIB_PATH):
     lib.pa_attention_workspace_size.restype = Z
     lib.pa_attention.argtypes = [P, I, I, P, P, D, P, I, I, P, P, ctypes.c_float, P, P, Z, P]
     lib.pa_attention.restype = ctypes.c_int
+    lib.pa_attention_ex.argtypes = [P, I, I, P, P, D, P, I, I, P, P, ctypes.c_float, P, P, Z,
+                                    ctypes.POINTER(_AttnOpts), P]
+    lib.pa_attention_ex.restype = ctypes.c_int
     lib.pa_timing_enable.argtypes = [ctypes.c_int]
     lib.pa_timing_enable.restype = ctypes.c_int
     lib.pa_timing_read.argtypes = [ctypes.c_char_p, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64)]
@@ -146,8 +153,11 @@ def _workspace(dev, nbytes):
     return ws
 
 
-def attention(q, k_cache, v_cache, block_tables, seq_lens, query_start_loc, scale, out, workspace=None):
-    """Causal attention of the varlen batch over the paged cache; writes ``out`` in place."""
+def attention(q, k_cache, v_cache, block_tables, seq_lens, query_start_loc, scale, out, workspace=None,
+              window=0):
+    """Causal attention of the varlen batch over the paged cache; writes ``out`` in place.
+
+    ``window`` > 0 restricts each query row to its ``window`` most recent keys (pa_attention_ex)."""
     import torch
     lib = load_library()
     dev = q.device
@@ -167,17 +177,18 @@ def attention(q, k_cache, v_cache, block_tables, seq_lens, query_start_loc, scal
     if seq_lens.shape[0] != B or query_start_loc.shape[0] != B + 1:
         raise ValueError("seq_lens must be [B], query_start_loc [B+1]")
     desc = _desc(k_cache)
+    opts = _AttnOpts(int(window))
     need = int(lib.pa_attention_workspace_size(B, T, MB, Hq, ctypes.byref(desc)))
     if need == 0:
-        _err(lib, lib.pa_attention(None, T, Hq, None, None, ctypes.byref(desc), None, B, MB, None, None,
-                                   ctypes.c_float(scale), None, None, 0, None))
+        _err(lib, lib.pa_attention_ex(None, T, Hq, None, None, ctypes.byref(desc), None, B, MB, None, None,
+                                      ctypes.c_float(scale), None, None, 0, ctypes.byref(opts), None))
     if workspace is None:
         workspace = _workspace(dev, need)
     _check_tensor("workspace", workspace, dev)
-    rc = lib.pa_attention(q.data_ptr(), T, Hq, k_cache.data_ptr(), v_cache.data_ptr(), ctypes.byref(desc),
-                          block_tables.data_ptr(), B, MB, seq_lens.data_ptr(), query_start_loc.data_ptr(),
-                          ctypes.c_float(scale), out.data_ptr(), workspace.data_ptr(),
-                          workspace.numel() * workspace.element_size(), _stream(dev))
+    rc = lib.pa_attention_ex(q.data_ptr(), T, Hq, k_cache.data_ptr(), v_cache.data_ptr(), ctypes.byref(desc),
+                             block_tables.data_ptr(), B, MB, seq_lens.data_ptr(), query_start_loc.data_ptr(),
+                             ctypes.c_float(scale), out.data_ptr(), workspace.data_ptr(),
+                             workspace.numel() * workspace.element_size(), ctypes.byref(opts), _stream(dev))
     _err(lib, rc)
     return out
 

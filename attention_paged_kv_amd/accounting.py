@@ -12,6 +12,8 @@ Sources (cited by page and section):
 * KV bytes: P3 §2.3 gives bytes = 2 * L * n_kv_heads * d_head * S * B * bytes_per_elem; a decode
   step reads every cached key and value once per KV head (P3 §3.2).  GQA sharing means a KV row is
   counted once per KV head, never per query head.
+* Sliding window W (P2 §5.2, P3 §6.3): the row at position p sees min(p + 1, W) keys, and a request
+  needs its keys from max(0, ctx - W + 1) on, ctx = s - q; W = 0 means no window.
 """
 from __future__ import annotations
 
@@ -22,15 +24,36 @@ MI355X_BF16_DENSE_FLOPS = 2.5166e15    # 256 CU x 2.4 GHz x 4096 FLOP/clk/CU, de
 MI355X_FP32_VECTOR_FLOPS = 157.3e12
 
 
-def visible_pairs(q_lens, seq_lens) -> int:
+def _tri(n):
+    """1 + 2 + ... + n for n >= 0."""
+    return n * (n + 1) // 2
+
+
+def visible_pairs(q_lens, seq_lens, window: int = 0) -> int:
+    """Visible (query row, key) pairs: sum over rows p = ctx .. s-1 of min(p + 1, W)."""
     q = np.asarray(q_lens, dtype=np.int64)
     s = np.asarray(seq_lens, dtype=np.int64)
-    return int(np.sum(q * (s - q) + q * (q + 1) // 2))
+    if window <= 0:
+        return int(np.sum(q * (s - q) + q * (q + 1) // 2))
+    lo, hi = s - q + 1, s                       # u = p + 1 runs over lo .. hi
+    a = np.minimum(hi, window)                  # u <= W contribute u
+    below = np.where(a >= lo, _tri(a) - _tri(lo - 1), 0)
+    above = (hi - np.maximum(lo, window + 1) + 1).clip(min=0) * window
+    return int(np.sum(below + above))
 
 
-def attention_flops(q_lens, seq_lens, num_q_heads: int, head_dim: int) -> int:
-    """Causal visible-pair FLOPs of Q K^T and P V."""
-    return 4 * head_dim * num_q_heads * visible_pairs(q_lens, seq_lens)
+def attention_flops(q_lens, seq_lens, num_q_heads: int, head_dim: int, window: int = 0) -> int:
+    """Visible-pair FLOPs of Q K^T and P V (causal, optionally windowed)."""
+    return 4 * head_dim * num_q_heads * visible_pairs(q_lens, seq_lens, window)
+
+
+def needed_keys(q_lens, seq_lens, window: int = 0) -> int:
+    """Keys a pass must read per KV head: s for each request, or s - max(0, s - q - W + 1) with a window."""
+    q = np.asarray(q_lens, dtype=np.int64)
+    s = np.asarray(seq_lens, dtype=np.int64)
+    if window <= 0:
+        return int(np.sum(s))
+    return int(np.sum(s - np.maximum(0, s - q - window + 1)))
 
 
 def dense_prefill_attention_flops(num_layers: int, seq_len: int, hidden: int) -> float:
@@ -43,9 +66,13 @@ def kv_bytes_per_token(num_layers: int, num_kv_heads: int, head_dim: int, esz: i
     return 2 * num_layers * num_kv_heads * head_dim * esz
 
 
-def kv_read_bytes(seq_lens, num_kv_heads: int, head_dim: int, esz: int) -> int:
+def kv_read_bytes(seq_lens, num_kv_heads: int, head_dim: int, esz: int, q_lens=None, window: int = 0) -> int:
     """Bytes of K and V one attention pass must read: every visible key once per KV head."""
-    return int(np.sum(np.asarray(seq_lens, dtype=np.int64))) * 2 * num_kv_heads * head_dim * esz
+    if window > 0:
+        n = needed_keys(q_lens, seq_lens, window)
+    else:
+        n = int(np.sum(np.asarray(seq_lens, dtype=np.int64)))
+    return n * 2 * num_kv_heads * head_dim * esz
 
 
 def append_bytes(num_tokens: int, num_kv_heads: int, head_dim: int, esz: int) -> int:

@@ -2,6 +2,7 @@
 // layout, launch sequencing on the caller's stream, check mode, kernel timing and error text.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <atomic>
 #include <cmath>
 #include <cstdarg>
@@ -125,7 +126,8 @@ int validate_desc(const pa_cache_desc* c) {
   return PA_OK;
 }
 
-int make_plan(int32_t B, int32_t T, int32_t MB, int32_t Hq, const pa_cache_desc* c, Plan& p) {
+// window: keys a row sees (pa::kNoWindow for all); it only bounds how many splits a row needs.
+int make_plan(int32_t B, int32_t T, int32_t MB, int32_t Hq, const pa_cache_desc* c, int window, Plan& p) {
   int rc = validate_desc(c);
   if (rc) return rc;
   if (B < 1) return fail(PA_ERR_INVALID_ARG, "num_seqs must be >= 1 (got %d)", B);
@@ -144,7 +146,10 @@ int make_plan(int32_t B, int32_t T, int32_t MB, int32_t Hq, const pa_cache_desc*
   if (p.bf16 && p.group > pa::kTileRows)
     return fail(PA_ERR_UNSUPPORTED, "query heads per KV head (%d) above %d", p.group, pa::kTileRows);
   p.split = split_tokens();
-  p.max_splits = (int)(((int64_t)MB * PA_BLOCK_SIZE + p.split - 1) / p.split);
+  // a row's splits cover keys from the block holding its oldest visible key: at most
+  // min(MB * 16, window + 15) keys
+  const int64_t span = std::min<int64_t>((int64_t)MB * PA_BLOCK_SIZE, (int64_t)window + PA_BLOCK_SIZE - 1);
+  p.max_splits = (int)((span + p.split - 1) / p.split);
   if (p.bf16) {
     p.per_token = 0;
     p.rows = B;
@@ -276,25 +281,35 @@ size_t pa_attention_workspace_size(int32_t num_seqs, int32_t num_q_tokens, int32
                                    int32_t num_q_heads, const pa_cache_desc* cache) {
   Plan p;
   std::string keep = g_err;
-  if (make_plan(num_seqs, num_q_tokens, max_blocks_per_seq, num_q_heads, cache, p) != PA_OK) {
+  if (make_plan(num_seqs, num_q_tokens, max_blocks_per_seq, num_q_heads, cache, pa::kNoWindow, p) != PA_OK) {
     g_err = keep;
     return 0;
   }
   return p.total > 0 ? p.total : 256;
 }
 
-int pa_attention(const void* q, int32_t num_q_tokens, int32_t num_q_heads, const void* k_cache, const void* v_cache,
-                 const pa_cache_desc* cache, const int32_t* block_tables, int32_t num_seqs, int32_t max_blocks_per_seq,
-                 const int32_t* seq_lens, const int32_t* query_start_loc, float scale, void* out, void* workspace,
-                 size_t workspace_bytes, void* stream) {
+int pa_attention_ex(const void* q, int32_t num_q_tokens, int32_t num_q_heads, const void* k_cache,
+                    const void* v_cache, const pa_cache_desc* cache, const int32_t* block_tables, int32_t num_seqs,
+                    int32_t max_blocks_per_seq, const int32_t* seq_lens, const int32_t* query_start_loc, float scale,
+                    void* out, void* workspace, size_t workspace_bytes, const pa_attention_opts* opts,
+                    void* stream) {
   g_err.clear();
+  int window = pa::kNoWindow;
+  if (opts) {
+    if (opts->sliding_window < 0)
+      return fail(PA_ERR_INVALID_ARG, "sliding_window must be >= 0 (got %d)", opts->sliding_window);
+    if (opts->sliding_window > 0 && opts->sliding_window < pa::kNoWindow) window = opts->sliding_window;
+  }
   Plan p;
-  int rc = make_plan(num_seqs, num_q_tokens, max_blocks_per_seq, num_q_heads, cache, p);
+  int rc = make_plan(num_seqs, num_q_tokens, max_blocks_per_seq, num_q_heads, cache, window, p);
   if (rc) return rc;
   if (!q || !k_cache || !v_cache || !block_tables || !seq_lens || !query_start_loc || !out)
     return fail(PA_ERR_INVALID_ARG, "null pointer argument");
   if (out == q || out == k_cache || out == v_cache) return fail(PA_ERR_INVALID_ARG, "out must not alias inputs");
-  if (!std::isfinite(scale)) return fail(PA_ERR_INVALID_ARG, "scale must be finite");
+  // the kernels track the running max of raw scores and apply the scale afterwards, which needs
+  // scale > 0
+  if (!std::isfinite(scale) || !(scale > 0.f))
+    return fail(PA_ERR_INVALID_ARG, "scale must be finite and > 0 (got %g)", (double)scale);
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
 
   char* ws = static_cast<char*>(workspace);
@@ -332,6 +347,7 @@ int pa_attention(const void* q, int32_t num_q_tokens, int32_t num_q_heads, const
     c.max_blocks = max_blocks_per_seq;
     c.num_blocks = cache->num_blocks;
     c.num_q_tokens = num_q_tokens;
+    c.window = window;
     rc = run_check(c, s);
     if (rc) return rc;
   }
@@ -358,6 +374,7 @@ int pa_attention(const void* q, int32_t num_q_tokens, int32_t num_q_heads, const
     d.max_blocks = max_blocks_per_seq;
     d.split = p.split;
     d.max_splits = p.max_splits;
+    d.window = window;
     d.scale_log2 = scale_log2;
     hipError_t e = timed("decode_split", s, [&] { return pa::launch_decode_split(d, p.head_dim, p.bf16, s); });
     if (e != hipSuccess) return device_fail(e, "decode split launch");
@@ -389,11 +406,21 @@ int pa_attention(const void* q, int32_t num_q_tokens, int32_t num_q_heads, const
     t.group = p.group;
     t.pos_per_tile = p.pos_per_tile;
     t.max_blocks = max_blocks_per_seq;
+    t.window = window;
     t.scale_log2 = scale_log2;
     e = timed("prefill_tile", s, [&] { return pa::launch_prefill_tile(t, p.head_dim, s); });
     if (e != hipSuccess) return device_fail(e, "prefill tile launch");
   }
   return PA_OK;
+}
+
+int pa_attention(const void* q, int32_t num_q_tokens, int32_t num_q_heads, const void* k_cache, const void* v_cache,
+                 const pa_cache_desc* cache, const int32_t* block_tables, int32_t num_seqs, int32_t max_blocks_per_seq,
+                 const int32_t* seq_lens, const int32_t* query_start_loc, float scale, void* out, void* workspace,
+                 size_t workspace_bytes, void* stream) {
+  return pa_attention_ex(q, num_q_tokens, num_q_heads, k_cache, v_cache, cache, block_tables, num_seqs,
+                         max_blocks_per_seq, seq_lens, query_start_loc, scale, out, workspace, workspace_bytes,
+                         nullptr, stream);
 }
 
 int pa_timing_enable(int on) {

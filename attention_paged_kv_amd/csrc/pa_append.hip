@@ -74,7 +74,8 @@ __global__ __launch_bounds__(256) void check_kernel(CheckArgs a, unsigned* bitma
       if (sl < ql) { report(a.result, 6, b, sl); continue; }
       if (sl > a.max_blocks * kBlock) { report(a.result, 7, b, sl); continue; }
       const int nb = (sl + kBlock - 1) / kBlock;
-      for (int j = 0; j < nb; ++j) {
+      const int j0 = max(0, sl - ql - a.window + 1) / kBlock;   // older blocks are never read
+      for (int j = j0; j < nb; ++j) {
         const int blk = a.block_tables[(int64_t)b * a.max_blocks + j];
         if (blk < 0 || blk >= a.num_blocks) { report(a.result, 8, b * a.max_blocks + j, blk); break; }
       }

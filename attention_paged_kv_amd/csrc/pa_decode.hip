@@ -52,6 +52,13 @@ __device__ __forceinline__ bool resolve_row(const DecodeArgs& a, int row, int& b
   return true;
 }
 
+// First key a row with `n_keys` causal keys sees (a sliding window drops the older ones), and the
+// block-aligned key where its splits begin.  Every kernel of the pass derives its ranges from these.
+__device__ __forceinline__ int first_visible(const DecodeArgs& a, int n_keys) { return max(0, n_keys - a.window); }
+__device__ __forceinline__ int split_origin(const DecodeArgs& a, int n_keys) {
+  return first_visible(a, n_keys) & ~(kBlock - 1);
+}
+
 __device__ __forceinline__ float wave_max_over_groups(float v, int lpr) {
   for (int o = lpr; o < kWave; o <<= 1) v = fmaxf(v, __shfl_xor(v, o));
   return v;
@@ -89,7 +96,7 @@ struct Io<false> {
 };
 
 struct Unit {
-  int row, b, t, n_keys, split, k0, k1, n_splits, g, h0, ncols;
+  int row, b, t, n_keys, lo, split, k0, k1, n_splits, g, h0, ncols;
 };
 
 // Decode the workgroup index into its unit.  Head-group index is fastest so that neighbouring
@@ -103,10 +110,12 @@ __device__ __forceinline__ bool get_unit(const DecodeArgs& a, int nzh, Unit& u) 
   u.row = i / a.max_splits;
   if (u.row >= a.num_rows) return false;
   if (!resolve_row(a, u.row, u.b, u.t, u.n_keys)) return false;
-  u.k0 = u.split * a.split;
+  u.lo = first_visible(a, u.n_keys);
+  const int kbeg = u.lo & ~(kBlock - 1);
+  u.k0 = kbeg + u.split * a.split;
   if (u.k0 >= u.n_keys) return false;
   u.k1 = min(u.k0 + a.split, u.n_keys);
-  u.n_splits = (u.n_keys + a.split - 1) / a.split;
+  u.n_splits = (u.n_keys - kbeg + a.split - 1) / a.split;
   u.g = z / nzh;
   const int zh = z % nzh;
   u.h0 = u.g * a.group + zh * a.heads_per_wg;
@@ -152,10 +161,12 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
   if (row >= a.num_rows) return;
   int b, t, n_keys;
   if (!resolve_row(a, row, b, t, n_keys)) return;
-  const int k0 = split * a.split;
+  const int lo = first_visible(a, n_keys);                 // keys before lo are outside the window
+  const int kbeg = lo & ~(kBlock - 1);
+  const int k0 = kbeg + split * a.split;
   if (k0 >= n_keys) return;
   const int k1 = min(k0 + a.split, n_keys);
-  const int n_splits = (n_keys + a.split - 1) / a.split;
+  const int n_splits = (n_keys - kbeg + a.split - 1) / a.split;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int g = 4 * (z / nzh) + w;
   if (g >= a.num_kv_heads) return;                         // waves are independent: no barriers
@@ -225,18 +236,20 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
                                        (__attribute__((address_space(3))) void*)(vdst + w * VB + 1024 * j), 16, 0, 0);
   };
 
-  // one block; PARTIAL: the block holds keys past the last visible one (only the split's last)
-  auto consume = [&](auto partial_tag, int i, const uint4* kr, const char* vsrc) {
-    constexpr bool PARTIAL = decltype(partial_tag)::value;
+  // one block; EDGE: the block holds keys outside [lo, k1) -- past the last visible one (the
+  // split's last block) or before a sliding window (the first block of split 0)
+  auto consume = [&](auto edge_tag, int i, const uint4* kr, const char* vsrc) {
+    constexpr bool EDGE = decltype(edge_tag)::value;
     floatx4 s = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk)
       s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kr[kk]), qb[kk], s, 0, 0, 0);
-    const int nvis = k1 - (kb0 + i) * kBlock;               // visible keys in this block
-    if constexpr (PARTIAL) {
+    const int nvis = k1 - (kb0 + i) * kBlock;               // keys of this block below k1
+    const int nlo = lo - (kb0 + i) * kBlock;                // keys of this block below lo
+    if constexpr (EDGE) {
 #pragma unroll
       for (int v = 0; v < 4; ++v)
-        if (4 * grp + v >= nvis) s[v] = -INFINITY;
+        if (4 * grp + v >= nvis || 4 * grp + v < nlo) s[v] = -INFINITY;
     }
     float bm = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
     bm = xor16_max(bm);
@@ -258,38 +271,48 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
     bf16x4 vt[NT];
 #pragma unroll
     for (int tt = 0; tt < NT; ++tt) vt[tt] = lds_read_tr(reinterpret_cast<const uint16_t*>(vw + tr_off[tt]));
-    if constexpr (PARTIAL) {
-      // rows past the last visible key may hold poison under p = 0: zero them
+    if constexpr (EDGE) {
+      // rows outside [lo, k1) may hold poison under p = 0: zero them
 #pragma unroll
       for (int tt = 0; tt < NT; ++tt)
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-          if (4 * grp + e >= nvis) vt[tt][e] = (__bf16)0.f;
+          if (4 * grp + e >= nvis || 4 * grp + e < nlo) vt[tt][e] = (__bf16)0.f;
     }
 #pragma unroll
     for (int tt = 0; tt < NT; ++tt) O[tt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vt[tt], pb, O[tt], 0, 0, 0);
   };
   using Full = std::integral_constant<bool, false>;
-  using Part = std::integral_constant<bool, true>;
+  using Edge = std::integral_constant<bool, true>;
   const bool last_partial = (kb0 + nb) * kBlock > k1;
+  const bool first_cut = kb0 * kBlock < lo;                // split 0 of a row whose window starts mid-block
 
   {
     uint4 kA[NKK], kB[NKK];
     issue(0, kA, sV0);
     int i = 0;
+    if (first_cut && nb > 2) {                             // peel the first pair: block 0 is an edge
+      issue(1, kB, sV1);
+      consume(Edge{}, 0, kA, sV0);
+      issue(2, kA, sV0);
+      consume(Full{}, 1, kB, sV1);
+      i = 2;
+    }
     for (; i + 2 < nb; i += 2) {                           // steady state: next block always exists
       issue(i + 1, kB, sV1);
       consume(Full{}, i, kA, sV0);
       issue(i + 2, kA, sV0);                               // sV0 reads above are ahead in the LDS queue
       consume(Full{}, i + 1, kB, sV1);
     }
+    const bool head_cut = first_cut && i == 0;            // block i is still the first one
     if (i + 1 < nb) {                                      // two blocks left
       issue(i + 1, kB, sV1);
-      consume(Full{}, i, kA, sV0);
-      if (last_partial) consume(Part{}, i + 1, kB, sV1);
+      if (head_cut) consume(Edge{}, i, kA, sV0);
+      else consume(Full{}, i, kA, sV0);
+      if (last_partial) consume(Edge{}, i + 1, kB, sV1);
       else consume(Full{}, i + 1, kB, sV1);
     } else {                                               // one block left
-      if (last_partial) consume(Part{}, i, kA, sV0);
+      if (last_partial || head_cut) consume(Edge{}, i, kA, sV0);
       else consume(Full{}, i, kA, sV0);
     }
   }
@@ -401,14 +424,14 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeArgs a) {
       }
     }
     const int key0 = blk * kBlock + rg;
-    const bool full = (blk + 1) * kBlock <= u.k1;
+    const bool full = (blk + 1) * kBlock <= u.k1 && blk * kBlock >= u.lo;
     float vf[LPB][EPL];
 #pragma unroll
     for (int r = 0; r < LPB; ++r) {
       IO::widen(vr[r], vf[r]);
-      if (!full && key0 + r * RPL >= u.k1) {
+      if (!full && (key0 + r * RPL >= u.k1 || key0 + r * RPL < u.lo)) {
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) vf[r][e] = 0.f;      // slots past the last visible key
+        for (int e = 0; e < EPL; ++e) vf[r][e] = 0.f;      // slots outside [lo, k1)
 #pragma unroll
         for (int hh = 0; hh < GT; ++hh) sc[r][hh] = -INFINITY;
       }
@@ -509,7 +532,7 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a) {
   const int h = blockIdx.x % a.num_q_heads;
   int b, t, n_keys;
   if (!resolve_row(a, row, b, t, n_keys)) return;
-  const int n = (n_keys + a.split - 1) / a.split;
+  const int n = (n_keys - split_origin(a, n_keys) + a.split - 1) / a.split;
   if (n <= 1) return;                                       // written directly by the split kernel
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1), w = tid >> 6;

@@ -11,6 +11,7 @@ namespace pa {
 constexpr int kDefaultSplitTokens = 256;   // keys per decode split (multiple of 16, at most 1024)
 constexpr int kTileRows = 128;             // query rows (position x head-in-group) per MFMA tile
 constexpr int kTileKeys = 64;              // keys per MFMA K/V tile
+constexpr int kNoWindow = 1 << 30;         // window value meaning "every earlier key"
 
 struct AppendArgs {
   const void* k;
@@ -42,6 +43,7 @@ struct DecodeArgs {
   int max_blocks;
   int split;              // keys per split
   int max_splits;
+  int window;             // keys a row sees, its own included (kNoWindow: all earlier keys)
   float scale_log2;       // scale * log2(e)
 };
 
@@ -61,6 +63,7 @@ struct TileArgs {
   int group;
   int pos_per_tile;       // kTileRows / group
   int max_blocks;
+  int window;             // as in DecodeArgs
   float scale_log2;
 };
 
@@ -75,6 +78,7 @@ struct CheckArgs {
   int max_blocks;
   int num_blocks;
   int num_q_tokens;
+  int window;                    // table entries before the first row's window are not checked
   int* result;                   // [4]: flag, code, index, value (device, zeroed by caller)
 };
 

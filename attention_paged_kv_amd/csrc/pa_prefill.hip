@@ -23,7 +23,10 @@
 // {4a..4a+3, 8+4a..8+4a+3} of each 16-key step, which is exactly two 4-row transpose reads.  Key
 // tiles entirely above the causal diagonal of the last row are never visited; only tiles crossing
 // the diagonal are masked.  Keys past the request's length in its last tile load a valid row
-// instead (finite data under a zero probability).  The running max is only moved (and O rescaled)
+// instead (finite data under a zero probability).  With a sliding window (P2 §5.2, P3 §6.3: only
+// the most recent W keys count) the key loop starts at the tile holding the first row's oldest
+// visible key, and tiles crossing the window's lower edge are masked as well; keys older than the
+// request's first window are never read (their blocks may be gone), a valid row stands in.  The running max is only moved (and O rescaled)
 // when some row's max grows by more than 2^8; between moves, probabilities may exceed 1 by at most
 // 2^8.
 #include "pa_common.h"
@@ -108,6 +111,10 @@ __global__ __launch_bounds__(256, 2) void prefill_tile_kernel(TileArgs a) {
   const int kv_end = min(sl, ctx + q_off + n_pos);   // keys needed by the last row of the tile
   const int n_kt = (kv_end + kTileKeys - 1) / kTileKeys;
   const int first_pos = ctx + q_off;
+  const int last_pos = kv_end - 1;
+  const int lo_req = max(0, ctx - a.window + 1);     // oldest key any row of the request sees
+  const int kt_lo = max(0, first_pos - a.window + 1) / kTileKeys;   // first key tile of this tile
+  const int low_edge = last_pos - a.window + 1;      // tiles starting below this need the window mask
   const float c = a.scale_log2;
   const int64_t rs = (int64_t)a.num_kv_heads * D;    // elements per cache token row
   const char* kbase = reinterpret_cast<const char*>(a.k_cache) + (int64_t)g * D * 2;
@@ -131,7 +138,7 @@ __global__ __launch_bounds__(256, 2) void prefill_tile_kernel(TileArgs a) {
     char* kl = kdst + 16 * w * ROWB;
     char* vl = vdst + 16 * w * ROWB;
     const int blk = 4 * kt + w;
-    if ((blk + 1) * kBlock <= sl) {               // whole block valid: one uniform table entry
+    if ((blk + 1) * kBlock <= sl && blk * kBlock >= lo_req) {   // whole block valid: one table entry
       const int64_t boff = (int64_t)win.get(table, w, 4, n_full, kt) * (kBlock * rs * 2);
       const char* kb = kbase + boff;               // uniform block base; lanes add 32-bit offsets
       const char* vb = vbase + boff;
@@ -142,11 +149,11 @@ __global__ __launch_bounds__(256, 2) void prefill_tile_kernel(TileArgs a) {
         __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(vb + lane_off[i]),
                                          (__attribute__((address_space(3))) void*)(vl + 1024 * i), 16, 0, 0);
       }
-    } else {                                      // last block: clamp rows past the length
+    } else {                                      // edge block: clamp rows into [lo_req, sl)
 #pragma unroll
       for (int i = 0; i < IPB; ++i) {
         const int rr = RPI * i + lane / CPR;
-        const int j = min(blk * kBlock + rr, sl - 1);
+        const int j = min(max(blk * kBlock + rr, lo_req), sl - 1);
         const int q = (lane % CPR) ^ swz<D>(16 * w + rr);
         const int64_t off = (((int64_t)table[j >> 4] * kBlock + (j & 15)) * rs) * 2 + q * 16;
         __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(kbase + off),
@@ -206,13 +213,15 @@ __global__ __launch_bounds__(256, 2) void prefill_tile_kernel(TileArgs a) {
       a1 = n1;
     }
 
-    // ---- causal mask (only on tiles that cross the diagonal of the first row) ----
-    if (kt * kTileKeys + kTileKeys - 1 > first_pos) {
+    // ---- causal mask (only on tiles that cross the diagonal of the first row) and window mask
+    //      (only on tiles that start below the last row's oldest visible key) ----
+    if (kt * kTileKeys + kTileKeys - 1 > first_pos || kt * kTileKeys < low_edge) {
+      const int oldest = pos - a.window + 1;
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const int key = kt * kTileKeys + 8 * (v >> 2) + 4 * half + (v & 3);
-        if (key > pos) S0[v] = -INFINITY;
-        if (key + 32 > pos) S1[v] = -INFINITY;
+        if (key > pos || key < oldest) S0[v] = -INFINITY;
+        if (key + 32 > pos || key + 32 < oldest) S1[v] = -INFINITY;
       }
     }
 
@@ -231,7 +240,7 @@ __global__ __launch_bounds__(256, 2) void prefill_tile_kernel(TileArgs a) {
 #pragma unroll
         for (int v = 0; v < 16; ++v) O[dt][v] *= alpha;
     }
-    const float mc = m_run * c;
+    const float mc = (m_run == -INFINITY) ? 0.f : m_run * c;   // a row that has seen no key yet
     bf16x8 P[4];
     float ps = 0.f;
 #pragma unroll
@@ -261,12 +270,12 @@ __global__ __launch_bounds__(256, 2) void prefill_tile_kernel(TileArgs a) {
     }
   };
 
-  stage(0, sK0, sV0);
+  stage(kt_lo, sK0, sV0);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
 
   // two tiles per iteration so that each buffer is a fixed LDS variable
-  for (int kt = 0; kt < n_kt; kt += 2) {
+  for (int kt = kt_lo; kt < n_kt; kt += 2) {
     if (kt + 1 < n_kt) stage(kt + 1, sK1, sV1);     // in flight during this tile's math
     tile_math(kt, sK0, sV0);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");

@@ -5,10 +5,13 @@ A step is one pass of the whole path over one batch: append this step's K/V into
 then causal attention of every query row (decode splits + merge, and prefill/chunk tiles where
 the batch has them).  Inputs are seeded synthetic tensors already resident in HBM.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config c2|c3|c4|c5|c1] [--no-cpu-baseline]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config c2|c3|c4|c5|c1] [--window N]
+                    [--no-cpu-baseline]
 
 Prints one JSON line.  The default workload is the 32-request bf16 decode batch (32/32 heads,
-d=128, contexts U[512, 4096], 16384-block pool); its metric is KV-read GB/s.
+d=128, contexts U[512, 4096], 16384-block pool); its metric is KV-read GB/s.  --window N runs the
+same workload with a sliding window of N keys per query row; work counts then cover only the keys
+and pairs inside the windows.
 """
 import argparse
 import json
@@ -56,7 +59,7 @@ def measured_traffic(kernel, workload):
     return None
 
 
-def cpu_baseline(w, steps, is_decode, kv_bytes):
+def cpu_baseline(w, steps, is_decode, kv_bytes, window=0):
     """Time the fp64 CPU oracle on the host cores over a bounded sample of the same workload.
 
     Decode workloads (and the tiny fp32 sequence) run whole steps, repeated until ~10 s; prefill
@@ -71,14 +74,14 @@ def cpu_baseline(w, steps, is_decode, kv_bytes):
         while t_cpu < 10.0 and reps < 50:
             for st in steps:
                 ta = time.perf_counter()
-                oracle.run_step(w, st, kcs, vcs, num_threads=threads)
+                oracle.run_step(w, st, kcs, vcs, num_threads=threads, window=window)
                 t_cpu += time.perf_counter() - ta
             reps += 1
         per = t_cpu / reps
         if is_decode:
             val, unit = kv_bytes / per / 1e9, "GB/s"
         else:
-            fl = sum(A.attention_flops(st.q_lens, st.seq_lens, w.num_q_heads, w.head_dim) for st in steps)
+            fl = sum(A.attention_flops(st.q_lens, st.seq_lens, w.num_q_heads, w.head_dim, window) for st in steps)
             val, unit = fl / per / 1e12, "TFLOP/s"
         sample = f"whole {w.name} step (append + attention of every row), {reps} run(s), {per:.3f} s per step"
     else:
@@ -93,11 +96,14 @@ def cpu_baseline(w, steps, is_decode, kv_bytes):
                 rows.append(q0 + r)
                 pos.append(ctx + r)
         rows = np.array(rows, np.int32)
-        fl = 4 * w.head_dim * w.num_q_heads * int(np.sum(np.array(pos, np.int64) + 1))
+        seen = np.array(pos, np.int64) + 1
+        if window > 0:
+            seen = np.minimum(seen, window)
+        fl = 4 * w.head_dim * w.num_q_heads * int(np.sum(seen))
         oracle.append(st.k_new, st.v_new, st.slot_mapping, kcs, vcs)
         ta = time.perf_counter()
         oracle.attention(st.q, kcs, vcs, st.block_tables, st.seq_lens, st.query_start_loc, w.scale, rows=rows,
-                         num_threads=threads)
+                         num_threads=threads, window=window)
         per = time.perf_counter() - ta
         val, unit = fl / per / 1e12, "TFLOP/s"
         sample = (f"{len(rows)} of {st.num_tokens} query rows of {w.name} (every 64th prefill row, every decode "
@@ -111,6 +117,7 @@ def main():
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", default="c2", choices=["c1", "c2", "c3", "c4", "c5"])
+    ap.add_argument("--window", type=int, default=0, help="sliding window in keys (0: none)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-ref-mib", type=int, default=0,
                     help="instead of the hot path, time a plain device copy of this many MiB "
@@ -150,6 +157,10 @@ def main():
                           "GBps_read_plus_write": 2 * n / dt / 1e9}), flush=True)
         return
 
+    if args.window < 0:
+        print("--window must be >= 0", file=sys.stderr)
+        sys.exit(2)
+    win = args.window
     t0 = time.time()
     w = W.CONFIGS[args.config]()
     log(f"generated {w.name} in {time.time() - t0:.1f}s")
@@ -180,15 +191,14 @@ def main():
     def run_step():
         for d in dsteps:
             pa.append_kv(d["k"], d["v"], d["slots"], kc, vc)
-            pa.attention(d["q"], kc, vc, d["bt"], d["sl"], d["qsl"], w.scale, d["out"], workspace=ws)
+            pa.attention(d["q"], kc, vc, d["bt"], d["sl"], d["qsl"], w.scale, d["out"], workspace=ws, window=win)
 
     # algorithmic work of one step
-    kv_bytes = sum(A.kv_read_bytes(st.seq_lens, w.num_kv_heads, w.head_dim, w.esz) for st in steps)
-    flops = sum(A.attention_flops(st.q_lens, st.seq_lens, w.num_q_heads, w.head_dim) for st in steps)
-    decode_bytes = sum(A.kv_read_bytes(st.seq_lens[st.q_lens == 1], w.num_kv_heads, w.head_dim, w.esz)
-                       for st in steps)
+    kv_bytes = sum(A.kv_read_bytes(st.seq_lens, w.num_kv_heads, w.head_dim, w.esz, st.q_lens, win) for st in steps)
+    flops = sum(A.attention_flops(st.q_lens, st.seq_lens, w.num_q_heads, w.head_dim, win) for st in steps)
     tile_flops = sum(A.attention_flops(st.q_lens[st.q_lens > 1], st.seq_lens[st.q_lens > 1], w.num_q_heads,
-                                       w.head_dim) for st in steps)
+                                       w.head_dim, win) for st in steps)
+    wname = w.name if win == 0 else f"{w.name}-w{win}"     # names the workload in the counter summary
 
     for _ in range(args.warmup):
         run_step()
@@ -230,7 +240,7 @@ def main():
         achieved = per_launch / (dk["avg_us"] * 1e-6) / 1e9
         roof = {"bound": "hbm", "kernel": "decode_split", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                "traffic": measured_traffic("decode_split", w.name),
+                "traffic": measured_traffic("decode_split", wname),
                 "algorithmic_bytes_per_launch": int(per_launch)}
     elif w.dtype == "f32":
         unit = "TFLOP/s"
@@ -249,12 +259,12 @@ def main():
         achieved = per_launch / (tk["avg_us"] * 1e-6) / 1e12
         roof = {"bound": "mfma", "kernel": "prefill_tile", "achieved": round(achieved, 1),
                 "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / BF16_PEAK_TFLOPS, 4),
-                "traffic": measured_traffic("prefill_tile", w.name),
+                "traffic": measured_traffic("prefill_tile", wname),
                 "algorithmic_flops_per_launch": int(per_launch)}
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(w, steps, is_decode, kv_bytes)
+        cpu = cpu_baseline(w, steps, is_decode, kv_bytes, win)
 
     res = {
         "metric": METRIC,
@@ -270,7 +280,8 @@ def main():
         "vs_baseline": None,
         "dtype": w.dtype,
         "data": "synthetic",
-        "config": {"workload": w.name, "description": w.description, "num_seqs": int(steps[0].num_seqs),
+        "config": {"workload": wname, "description": w.description + (f", sliding window {win}" if win else ""),
+                   "sliding_window": win, "num_seqs": int(steps[0].num_seqs),
                    "q_tokens": int(sum(st.num_tokens for st in steps)),
                    "kv_read_bytes": int(kv_bytes), "flops": int(flops), "parallelism": "single-gpu"},
         "kernels": {k: {kk: round(vv, 3) for kk, vv in v.items()} for k, v in kern.items()},

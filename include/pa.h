@@ -35,7 +35,7 @@
 extern "C" {
 #endif
 
-#define PA_ABI_VERSION 1
+#define PA_ABI_VERSION 2
 #define PA_BLOCK_SIZE 16
 
 typedef enum {
@@ -121,7 +121,7 @@ size_t pa_attention_workspace_size(int32_t num_seqs, int32_t num_q_tokens, int32
  *                    this step's tokens included; 1 <= q_len <= seq_len <= max_blocks_per_seq*16.
  *   query_start_loc  device int32 [num_seqs+1]: 0, then nondecreasing, ending at num_q_tokens;
  *                    every request has q_len >= 1 (so num_q_tokens >= num_seqs).
- *   scale            softmax scale (1/sqrt(d) for standard attention).
+ *   scale            softmax scale, finite and > 0 (1/sqrt(d) for standard attention).
  *   out              device [num_q_tokens][num_q_heads][d], cache->dtype; must not alias inputs.
  *                    Accumulation is fp32 for both dtypes; bf16 output is rounded to nearest even.
  *   workspace        device scratch of at least pa_attention_workspace_size() bytes, owned by
@@ -135,6 +135,28 @@ int pa_attention(const void* q, int32_t num_q_tokens, int32_t num_q_heads,
                  const int32_t* block_tables, int32_t num_seqs, int32_t max_blocks_per_seq,
                  const int32_t* seq_lens, const int32_t* query_start_loc, float scale, void* out,
                  void* workspace, size_t workspace_bytes, void* stream);
+
+/* Options of pa_attention_ex.  A zeroed struct (or a NULL pointer) gives pa_attention's result. */
+typedef struct {
+  /* Sliding window (P2 §5.2 and P3 §6.3: keep only the most recent W tokens' K/V).  0: none.
+   * W > 0: the query row at position p attends to keys max(0, p - W + 1) .. p only, itself
+   * included, so W = 1 returns each row's own V.  Block-table entries of blocks that lie wholly
+   * before the first query row's window, max(0, ctx - W + 1) with ctx = seq_len - q_len, are never
+   * read (any value: a cache may drop such blocks), nor are the cache slots they would name.
+   * Negative values are rejected with PA_ERR_INVALID_ARG. */
+  int32_t sliding_window;
+} pa_attention_opts;
+
+/*
+ * pa_attention with options; same arguments, layouts, ownership and errors, plus `opts` (host,
+ * read during the call only; NULL = no options).  pa_attention_workspace_size() for the same
+ * sizes is enough for every option value (a window only shrinks what is needed).
+ */
+int pa_attention_ex(const void* q, int32_t num_q_tokens, int32_t num_q_heads,
+                    const void* k_cache, const void* v_cache, const pa_cache_desc* cache,
+                    const int32_t* block_tables, int32_t num_seqs, int32_t max_blocks_per_seq,
+                    const int32_t* seq_lens, const int32_t* query_start_loc, float scale, void* out,
+                    void* workspace, size_t workspace_bytes, const pa_attention_opts* opts, void* stream);
 
 /*
  * Measurement support (not part of the computation).  When timing is on, every kernel the

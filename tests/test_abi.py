@@ -81,6 +81,10 @@ def test_bad_sizes_rejected_before_launch(lib):
     assert lib.pa_attention(None, 4, 8, p, p, ctypes.byref(d), p, 4, 16, p, p, ctypes.c_float(1), p, None, 0, None) == 1
     assert lib.pa_attention(p, 4, 8, p, p, ctypes.byref(d), p, 4, 16, p, p, ctypes.c_float(float("inf")), p, None, 0,
                             None) == 1
+    for bad_scale in (0.0, -0.125):
+        assert lib.pa_attention(p, 4, 8, p, p, ctypes.byref(d), p, 4, 16, p, p, ctypes.c_float(bad_scale),
+                                ctypes.c_void_p(48), None, 0, None) == 1
+        assert b"scale" in lib.pa_last_error()
     small = ctypes.c_void_p(256)
     o = ctypes.c_void_p(48)
     assert lib.pa_attention(p, 4, 8, p, p, ctypes.byref(d), p, 4, 16, p, p, ctypes.c_float(1), p, small, 8, None) == 1  # out aliases q
@@ -89,6 +93,21 @@ def test_bad_sizes_rejected_before_launch(lib):
     assert b"workspace" in lib.pa_last_error()
     assert lib.pa_append_kv(p, p, p, -1, p, p, ctypes.byref(d), None) == 1
     assert lib.pa_append_kv(None, None, None, 0, None, None, ctypes.byref(d), None) == 0     # empty append
+
+
+def test_window_option_rejected_when_negative_before_launch(lib):
+    d = _desc()
+    p = ctypes.c_void_p(16)
+    o = ctypes.c_void_p(48)
+    neg = pa._AttnOpts(-1)
+    rc = lib.pa_attention_ex(p, 4, 8, p, p, ctypes.byref(d), p, 4, 16, p, p, ctypes.c_float(1), o, None, 0,
+                             ctypes.byref(neg), None)
+    assert rc == 1 and b"sliding_window" in lib.pa_last_error()
+    # a window does not lift the other checks: the 8-byte workspace is still refused before launch
+    win = pa._AttnOpts(1000)     # rows may span 1015 keys: 4 splits, partials in the workspace
+    small = ctypes.c_void_p(256)
+    assert lib.pa_attention_ex(p, 4, 8, p, p, ctypes.byref(d), p, 4, 64, p, p, ctypes.c_float(1), o, small, 8,
+                               ctypes.byref(win), None) == 4
 
 
 def test_binding_fails_loudly_without_library(tmp_path):

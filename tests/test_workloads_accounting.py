@@ -123,3 +123,22 @@ def test_c1_steps():
     for t in range(1, 17):
         assert w.steps[t].num_tokens == 1 and int(w.steps[t].seq_lens[0]) == 128 + t
     assert sorted(w.steps[0].block_tables[0].tolist()) == list(range(9))
+
+
+@pytest.mark.parametrize("window", [0, 1, 7, 16, 100, 1000, 10 ** 6])
+def test_windowed_counts_match_brute_force(window):
+    """Closed forms for the windowed pair and key counts against explicit loops over rows."""
+    rng = np.random.default_rng(window)
+    s = rng.integers(1, 3000, 20)
+    q = np.minimum(s, rng.integers(1, 400, 20))
+    q[:5] = 1
+    pairs = keys = 0
+    for sb, qb in zip(s, q):
+        ctx = int(sb - qb)
+        lo_req = 0 if window == 0 else max(0, ctx - window + 1)
+        keys += int(sb) - lo_req
+        for p in range(ctx, int(sb)):
+            pairs += p + 1 if window == 0 else min(p + 1, window)
+    assert A.visible_pairs(q, s, window) == pairs
+    assert A.needed_keys(q, s, window) == keys
+    assert A.kv_read_bytes(s, 8, 128, 2, q_lens=q, window=window) == keys * 2 * 8 * 128 * 2
