@@ -23,8 +23,15 @@ Readings taken where the pages are silent:
     requests in order, so physical blocks interleave across requests;
   * slots not holding a live token are poisoned (K = +-3e38, V = NaN) and
     block-table padding is -1, so a kernel that reads outside the visible range
-    produces non-finite output.
-Draw order per workload: lengths -> block permutation -> Q -> K -> V.
+    produces non-finite output;
+  * 8-bit caches (P2 §4.3, §5.4: INT8 KV, calibrated per channel): activations stay
+    bf16; the cached context is drawn directly as int8 codes (N(0,1) * 32 rounded,
+    clipped to +-127: about a quarter of the code range, as N(0,1) data under an
+    absmax/127 calibration would give) with poison code -128 in unused slots, and
+    each (KV head, channel) gets a scale (4/127) * U(0.75, 1.25) for K and for V.
+    The step's new tokens are bf16 values that the append itself quantises.
+Draw order per workload: lengths -> block permutation -> Q -> K -> V
+(-> int8 context codes of K, then of V -> K scales -> V scales).
 """
 from __future__ import annotations
 
@@ -36,7 +43,9 @@ import numpy as np
 
 BLOCK_SIZE = 16
 K_POISON = 3.0e38
+I8_POISON = -128
 DTYPES = ("f32", "bf16")
+CACHE_DTYPES = ("f32", "bf16", "i8")
 
 
 def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
@@ -81,6 +90,22 @@ def normal_storage(rng: np.random.Generator, shape, dtype: str) -> np.ndarray:
         m = min(_CHUNK, n - i)
         out[i:i + m] = f32_to_bf16_bits(rng.standard_normal(m, dtype=np.float32))
     return out.reshape(shape)
+
+
+def int8_codes(rng: np.random.Generator, shape) -> np.ndarray:
+    """Synthetic int8 cache content: N(0,1) * 32 rounded to integers, clipped to [-127, 127]
+    (drawn in chunks, like normal_storage)."""
+    n = int(np.prod(shape))
+    out = np.empty(n, dtype=np.int8)
+    for i in range(0, n, _CHUNK):
+        m = min(_CHUNK, n - i)
+        out[i:i + m] = np.clip(np.rint(rng.standard_normal(m, dtype=np.float32) * 32.0), -127, 127)
+    return out.reshape(shape)
+
+
+def channel_scales(rng: np.random.Generator, num_kv_heads: int, head_dim: int) -> np.ndarray:
+    """One fp32 scale per (KV head, channel): (4/127) * U(0.75, 1.25)."""
+    return (np.float32(4.0 / 127.0) * rng.uniform(0.75, 1.25, (num_kv_heads, head_dim))).astype(np.float32)
 
 
 def to_float(x: np.ndarray, dtype: str) -> np.ndarray:
@@ -145,10 +170,18 @@ class Workload:
     steps: List[Step] = field(default_factory=list)
     seed: int = 0
     description: str = ""
+    kv_dtype: str = ""            # cache element type when it differs from dtype ("i8")
+    k_scale: Optional[np.ndarray] = None   # [Hkv, d] float32, int8 caches only
+    v_scale: Optional[np.ndarray] = None
+
+    @property
+    def cache_dtype(self) -> str:
+        return self.kv_dtype or self.dtype
 
     @property
     def esz(self) -> int:
-        return esize(self.dtype)
+        """Bytes per cache element."""
+        return 1 if self.cache_dtype == "i8" else esize(self.dtype)
 
 
 def _alloc_blocks(rng, seq_lens: Sequence[int], num_blocks: int, max_blocks: int, shuffle: bool, pad: int = -1):
@@ -176,8 +209,8 @@ def make_batch(seed: int, seq_lens: Sequence[int], q_lens: Sequence[int], num_q_
                num_blocks: Optional[int] = None, max_blocks: Optional[int] = None,
                shuffle: bool = True, scale: Optional[float] = None, name: str = "batch",
                rng: Optional[np.random.Generator] = None, description: str = "",
-               values: bool = True) -> Workload:
-    """A single-step varlen batch.
+               values: bool = True, cache: str = "") -> Workload:
+    """A single-step varlen batch (``cache="i8"``: bf16 activations over an int8 cache).
 
     Request b advances ``q_lens[b]`` tokens and then sees ``seq_lens[b]`` keys; its
     first ``seq_lens[b] - q_lens[b]`` tokens are already in the cache.  With ``values=False``
@@ -185,6 +218,8 @@ def make_batch(seed: int, seq_lens: Sequence[int], q_lens: Sequence[int], num_q_
     the same as with values, since lengths and placements are drawn first.
     """
     assert dtype in DTYPES
+    i8 = cache == "i8"
+    assert cache in ("", dtype, "i8") and (not i8 or dtype == "bf16")
     seq_lens = np.asarray(seq_lens, dtype=np.int64)
     q_lens = np.asarray(q_lens, dtype=np.int64)
     assert seq_lens.shape == q_lens.shape and seq_lens.ndim == 1
@@ -213,14 +248,25 @@ def make_batch(seed: int, seq_lens: Sequence[int], q_lens: Sequence[int], num_q_
                     seq_lens=seq_lens.astype(np.int32), query_start_loc=qsl, block_tables=tables)
         return Workload(name=name, dtype=dtype, num_q_heads=Hq, num_kv_heads=Hkv, head_dim=d, num_blocks=NB,
                         scale=float(scale) if scale is not None else 1.0 / math.sqrt(d),
-                        k_cache0=empty, v_cache0=empty, steps=[step], seed=seed, description=description)
+                        k_cache0=empty, v_cache0=empty, steps=[step], seed=seed, description=description,
+                        kv_dtype="i8" if i8 else "")
     q = normal_storage(rng, (T, Hq, d), dtype)
     K = normal_storage(rng, (L, Hkv, d), dtype)
     V = normal_storage(rng, (L, Hkv, d), dtype)
 
-    kc, vc = poison_cache((NB, BLOCK_SIZE, Hkv, d), dtype)
+    n_ctx = int(np.sum(seq_lens - q_lens))
+    if i8:
+        kc = np.full((NB, BLOCK_SIZE, Hkv, d), I8_POISON, dtype=np.int8)
+        vc = np.full((NB, BLOCK_SIZE, Hkv, d), I8_POISON, dtype=np.int8)
+        Kctx = int8_codes(rng, (n_ctx, Hkv, d))
+        Vctx = int8_codes(rng, (n_ctx, Hkv, d))
+        k_scale = channel_scales(rng, Hkv, d)
+        v_scale = channel_scales(rng, Hkv, d)
+    else:
+        kc, vc = poison_cache((NB, BLOCK_SIZE, Hkv, d), dtype)
     kc2 = kc.reshape(NB * BLOCK_SIZE, Hkv, d)
     vc2 = vc.reshape(NB * BLOCK_SIZE, Hkv, d)
+    cpos = 0
     new_rows = np.empty(T, dtype=np.int64)
     slot_mapping = np.empty(T, dtype=np.int32)
     qsl = np.zeros(B + 1, dtype=np.int32)
@@ -231,8 +277,13 @@ def make_batch(seed: int, seq_lens: Sequence[int], q_lens: Sequence[int], num_q_
         ctx = s - ql
         if ctx > 0:
             sl = slots_for(tables, b, np.arange(ctx))
-            kc2[sl] = K[lo:lo + ctx]
-            vc2[sl] = V[lo:lo + ctx]
+            if i8:
+                kc2[sl] = Kctx[cpos:cpos + ctx]
+                vc2[sl] = Vctx[cpos:cpos + ctx]
+                cpos += ctx
+            else:
+                kc2[sl] = K[lo:lo + ctx]
+                vc2[sl] = V[lo:lo + ctx]
         slot_mapping[t:t + ql] = slots_for(tables, b, np.arange(ctx, s))
         new_rows[t:t + ql] = np.arange(lo + ctx, lo + s)
         lo += s
@@ -241,9 +292,12 @@ def make_batch(seed: int, seq_lens: Sequence[int], q_lens: Sequence[int], num_q_
     step = Step(q=q, k_new=np.ascontiguousarray(K[new_rows]), v_new=np.ascontiguousarray(V[new_rows]),
                 slot_mapping=slot_mapping, seq_lens=seq_lens.astype(np.int32), query_start_loc=qsl,
                 block_tables=tables)
-    return Workload(name=name, dtype=dtype, num_q_heads=Hq, num_kv_heads=Hkv, head_dim=d, num_blocks=NB,
-                    scale=float(scale) if scale is not None else 1.0 / math.sqrt(d),
-                    k_cache0=kc, v_cache0=vc, steps=[step], seed=seed, description=description)
+    w = Workload(name=name, dtype=dtype, num_q_heads=Hq, num_kv_heads=Hkv, head_dim=d, num_blocks=NB,
+                 scale=float(scale) if scale is not None else 1.0 / math.sqrt(d),
+                 k_cache0=kc, v_cache0=vc, steps=[step], seed=seed, description=description)
+    if i8:
+        w.kv_dtype, w.k_scale, w.v_scale = "i8", k_scale, v_scale
+    return w
 
 
 # ---------------------------------------------------------------------------------------------
@@ -251,6 +305,14 @@ def make_batch(seed: int, seq_lens: Sequence[int], q_lens: Sequence[int], num_q_
 # users + a 30k-token prompt cut into 2048-token chunks), the 16-token blocks of P1 §2.2-2.3, and
 # the 32-layer / 32- or 8-KV-head / head_dim-128 model shapes used in P3 §2.3 and §6.3.
 # ---------------------------------------------------------------------------------------------
+
+def _sfx(cache: str) -> str:
+    return "-i8" if cache == "i8" else ""
+
+
+def _dsc(cache: str) -> str:
+    return ", int8 KV cache with per-(head, channel) scales" if cache == "i8" else ""
+
 
 def config1(values: bool = True, seed: int = 1) -> Workload:
     """Tiny fp32: 1 sequence, 4 q-heads = 4 KV heads, d=64.  Step 0 prefills 128 tokens,
@@ -280,25 +342,26 @@ def config1(values: bool = True, seed: int = 1) -> Workload:
                     description="fp32, 1 seq, 4/4 heads, d=64: prefill 128 then 16 decode steps")
 
 
-def config2(values: bool = True, seed: int = 2) -> Workload:
+def config2(values: bool = True, seed: int = 2, cache: str = "") -> Workload:
     """Decode batch: 32 requests with q_len 1, contexts U{512..4096}; 32/32 heads, d=128, bf16;
     16384-block pool, shuffled."""
     rng = np.random.default_rng(seed)
     ctx = rng.integers(512, 4096, size=32, endpoint=True)
     return make_batch(seed, ctx, np.ones(32, np.int64), 32, 32, 128, "bf16", num_blocks=16384,
-                      max_blocks=4096 // BLOCK_SIZE, rng=rng, name="c2_decode_b32", values=values,
-                      description="bf16 decode, 32 seqs, 32/32 heads, d=128, ctx U[512,4096], 16384-block pool")
+                      max_blocks=4096 // BLOCK_SIZE, rng=rng, name="c2_decode_b32" + _sfx(cache), values=values,
+                      cache=cache, description="bf16 decode, 32 seqs, 32/32 heads, d=128, ctx U[512,4096], "
+                                               "16384-block pool" + _dsc(cache))
 
 
-def config3(values: bool = True, seed: int = 3) -> Workload:
+def config3(values: bool = True, seed: int = 3, cache: str = "") -> Workload:
     """One-shot causal prefill: S=8192, 32/32 heads, d=128, bf16; 512 blocks, shuffled."""
     rng = np.random.default_rng(seed)
     return make_batch(seed, [8192], [8192], 32, 32, 128, "bf16", num_blocks=512, max_blocks=512,
-                      rng=rng, name="c3_prefill_8k", values=values,
-                      description="bf16 one-shot causal prefill, S=8192, 32/32 heads, d=128")
+                      rng=rng, name="c3_prefill_8k" + _sfx(cache), values=values, cache=cache,
+                      description="bf16 one-shot causal prefill, S=8192, 32/32 heads, d=128" + _dsc(cache))
 
 
-def config4(values: bool = True, seed: int = 4) -> Workload:
+def config4(values: bool = True, seed: int = 4, cache: str = "") -> Workload:
     """Mixed chunked-prefill step: 30 decodes (contexts U{1024..8192}) + chunk 15 of a 30720-token
     prompt (2048 new tokens over 28672 cached); 32 q-heads / 8 KV heads, d=128, bf16."""
     rng = np.random.default_rng(seed)
@@ -307,19 +370,21 @@ def config4(values: bool = True, seed: int = 4) -> Workload:
     ql = np.concatenate([np.ones(30, np.int64), [2048]])
     nb = int(((ctx + BLOCK_SIZE - 1) // BLOCK_SIZE).sum()) + 30720 // BLOCK_SIZE
     return make_batch(seed, seq, ql, 32, 8, 128, "bf16", num_blocks=nb, max_blocks=30720 // BLOCK_SIZE,
-                      rng=rng, name="c4_mixed_chunk", values=values,
-                      description="bf16 mixed step: 30 decodes (ctx U[1024,8192]) + 2048-token chunk at 28672 cached, 32/8 heads")
+                      rng=rng, name="c4_mixed_chunk" + _sfx(cache), values=values, cache=cache,
+                      description="bf16 mixed step: 30 decodes (ctx U[1024,8192]) + 2048-token chunk at 28672 cached, "
+                                  "32/8 heads" + _dsc(cache))
 
 
-def config5(values: bool = True, seed: int = 5) -> Workload:
+def config5(values: bool = True, seed: int = 5, cache: str = "") -> Workload:
     """Length-skewed long decode: 16 requests, contexts log-uniform in [3277, 32768];
     32 q-heads / 8 KV heads, d=128, bf16; pool shuffled so blocks interleave across requests."""
     rng = np.random.default_rng(seed)
     ctx = np.clip(np.round(np.exp(rng.uniform(math.log(3277), math.log(32768), size=16))), 3277, 32768).astype(np.int64)
     nb = int(((ctx + BLOCK_SIZE - 1) // BLOCK_SIZE).sum())
     return make_batch(seed, ctx, np.ones(16, np.int64), 32, 8, 128, "bf16", num_blocks=nb,
-                      max_blocks=32768 // BLOCK_SIZE, rng=rng, name="c5_skewed_decode", values=values,
-                      description="bf16 decode, 16 seqs, ctx log-U[3277,32768], 32/8 heads, interleaved blocks")
+                      max_blocks=32768 // BLOCK_SIZE, rng=rng, name="c5_skewed_decode" + _sfx(cache), values=values,
+                      cache=cache, description="bf16 decode, 16 seqs, ctx log-U[3277,32768], 32/8 heads, "
+                                               "interleaved blocks" + _dsc(cache))
 
 
 CONFIGS = {"c1": config1, "c2": config2, "c3": config3, "c4": config4, "c5": config5}
@@ -346,4 +411,5 @@ def chunked_steps(w: Workload, chunk_sizes: Sequence[int]) -> Workload:
     return Workload(name=w.name + "_chunked", dtype=w.dtype, num_q_heads=w.num_q_heads,
                     num_kv_heads=w.num_kv_heads, head_dim=w.head_dim, num_blocks=w.num_blocks, scale=w.scale,
                     k_cache0=w.k_cache0, v_cache0=w.v_cache0, steps=steps, seed=w.seed,
-                    description=w.description + f" as chunks {list(chunk_sizes)}")
+                    description=w.description + f" as chunks {list(chunk_sizes)}",
+                    kv_dtype=w.kv_dtype, k_scale=w.k_scale, v_scale=w.v_scale)

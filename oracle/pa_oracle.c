@@ -21,6 +21,12 @@
  *                 (P3 §3.1, §5.1: softmax(q K^T) V over all cached keys).  With a sliding window
  *                 W > 0, keys j < p - W + 1 are also set to -inf (P3 §6.3, P2 §5.2: keep only the
  *                 most recent W tokens' K/V); keys that no row can see are not gathered.
+ *   8-bit cache -- P2 §4.3 and §5.4 (INT8 KV halves memory and bandwidth; calibrate per channel):
+ *                 the cache holds int8 codes with one fp32 scale per (KV head, channel).  Append
+ *                 quantises each element of the bf16 input x with its channel's scale s:
+ *                 code = x / s rounded to fp32, then to the nearest integer (ties to even), clamped
+ *                 to [-127, 127]; NaN gives 0.  Attention reads code * s (exact in double) and is
+ *                 otherwise the computation above.
  * Precision: inputs are widened exactly to double (bf16: bits << 16), every sum is in double,
  * and the result is rounded once to the output dtype (bf16: nearest, ties to even).
  *
@@ -28,7 +34,10 @@
  * forms (constant V, zero K, single visible key), argmax probes, block-permutation invariance,
  * chunked == one-shot and decode == last prefill row; the window by a library softmax over each
  * row's key slice, W >= context == no window, W = 1 == own V row, and a dominant key one step
- * outside / at the window's edge.  No page prints attention output values.
+ * outside / at the window's edge; the int8 path by hand-computed codes (exact multiples, ties,
+ * clamps, NaN), the fp32 quotient deciding the rounding, bitwise equality with the fp32 path over
+ * a dequantised cache, a library softmax over dequantised values and a dequantised argmax probe.
+ * No page prints attention output values.
  */
 #include <math.h>
 #include <pthread.h>
@@ -39,7 +48,7 @@
 
 #define ORACLE_BLOCK 16
 
-enum { OR_F32 = 0, OR_BF16 = 1 };
+enum { OR_F32 = 0, OR_BF16 = 1, OR_I8 = 2 };
 
 static void set_err(char* err, int err_len, const char* msg) {
   if (err && err_len > 0) {
@@ -83,20 +92,13 @@ static void store_elem(void* base, size_t idx, int dtype, double v) {
 /* ---------------------------------------------------------------------------------------- */
 /* append                                                                                    */
 /* ---------------------------------------------------------------------------------------- */
-int pa_oracle_append(const void* k, const void* v, const int32_t* slot_mapping, int32_t num_tokens,
-                     void* k_cache, void* v_cache, int32_t num_blocks, int32_t num_kv_heads,
-                     int32_t head_dim, int32_t esz, char* err, int32_t err_len) {
-  if (num_tokens < 0 || num_blocks < 1 || num_kv_heads < 1 || head_dim < 1 || (esz != 2 && esz != 4)) {
-    set_err(err, err_len, "bad sizes");
-    return 1;
-  }
-  int64_t nslots = (int64_t)num_blocks * ORACLE_BLOCK;
-  size_t row = (size_t)num_kv_heads * (size_t)head_dim * (size_t)esz;
+/* Slots must lie in the pool and be distinct (negative = skip).  Returns 0 or an error code. */
+static int check_slots(const int32_t* slot_mapping, int32_t num_tokens, int64_t nslots, char* err, int err_len) {
   unsigned char* seen = (unsigned char*)calloc((size_t)nslots, 1);
   if (!seen) { set_err(err, err_len, "oom"); return 1; }
   for (int32_t i = 0; i < num_tokens; ++i) {
     int32_t s = slot_mapping[i];
-    if (s < 0) continue;                       /* padding token: nothing to write */
+    if (s < 0) continue;
     if ((int64_t)s >= nslots) {
       char m[128];
       snprintf(m, sizeof m, "slot %d of token %d is outside the pool", s, i);
@@ -113,13 +115,60 @@ int pa_oracle_append(const void* k, const void* v, const int32_t* slot_mapping, 
     }
     seen[s] = 1;
   }
+  free(seen);
+  return 0;
+}
+
+/* int8 code of x under scale s (see the header): fp32 quotient, nearest-even, clamp, NaN -> 0. */
+static int8_t quantize(float x, float s) {
+  float r = x / s;                 /* one IEEE single-precision division */
+  if (r != r) return 0;
+  r = rintf(r);                    /* default rounding mode: nearest, ties to even */
+  if (r > 127.f) r = 127.f;
+  if (r < -127.f) r = -127.f;
+  return (int8_t)r;
+}
+
+int pa_oracle_quantize(float x, float s) { return quantize(x, s); }
+
+int pa_oracle_append_i8(const uint16_t* k, const uint16_t* v, const int32_t* slot_mapping, int32_t num_tokens,
+                        int8_t* k_cache, int8_t* v_cache, int32_t num_blocks, int32_t num_kv_heads,
+                        int32_t head_dim, const float* k_scale, const float* v_scale, char* err, int32_t err_len) {
+  if (num_tokens < 0 || num_blocks < 1 || num_kv_heads < 1 || head_dim < 1 || !k_scale || !v_scale) {
+    set_err(err, err_len, "bad sizes");
+    return 1;
+  }
+  int rc = check_slots(slot_mapping, num_tokens, (int64_t)num_blocks * ORACLE_BLOCK, err, err_len);
+  if (rc) return rc;
+  const size_t row = (size_t)num_kv_heads * (size_t)head_dim;
   for (int32_t i = 0; i < num_tokens; ++i) {
     int32_t s = slot_mapping[i];
     if (s < 0) continue;
+    for (size_t c = 0; c < row; ++c) {
+      k_cache[(size_t)s * row + c] = quantize((float)load_elem(k, (size_t)i * row + c, OR_BF16), k_scale[c]);
+      v_cache[(size_t)s * row + c] = quantize((float)load_elem(v, (size_t)i * row + c, OR_BF16), v_scale[c]);
+    }
+  }
+  return 0;
+}
+
+int pa_oracle_append(const void* k, const void* v, const int32_t* slot_mapping, int32_t num_tokens,
+                     void* k_cache, void* v_cache, int32_t num_blocks, int32_t num_kv_heads,
+                     int32_t head_dim, int32_t esz, char* err, int32_t err_len) {
+  if (num_tokens < 0 || num_blocks < 1 || num_kv_heads < 1 || head_dim < 1 || (esz != 2 && esz != 4)) {
+    set_err(err, err_len, "bad sizes");
+    return 1;
+  }
+  int64_t nslots = (int64_t)num_blocks * ORACLE_BLOCK;
+  size_t row = (size_t)num_kv_heads * (size_t)head_dim * (size_t)esz;
+  int rc = check_slots(slot_mapping, num_tokens, nslots, err, err_len);
+  if (rc) return rc;
+  for (int32_t i = 0; i < num_tokens; ++i) {
+    int32_t s = slot_mapping[i];
+    if (s < 0) continue;                       /* padding token: nothing to write */
     memcpy((char*)k_cache + (size_t)s * row, (const char*)k + (size_t)i * row, row);
     memcpy((char*)v_cache + (size_t)s * row, (const char*)v + (size_t)i * row, row);
   }
-  free(seen);
   return 0;
 }
 
@@ -198,7 +247,9 @@ static void* worker(void* arg) {
 typedef struct {
   const void* kc;
   const void* vc;
-  int dtype, Hkv, d;
+  int dtype, Hkv, d;          /* dtype of the cache elements */
+  const float* k_scale;       /* [Hkv][d], int8 caches only */
+  const float* v_scale;
   const int32_t* table;
   double* Kb;
   double* Vb;
@@ -212,8 +263,13 @@ static void* gather_worker(void* arg) {
     const int blk = Gt->table[j / ORACLE_BLOCK];
     const size_t src = ((size_t)blk * ORACLE_BLOCK + (size_t)(j % ORACLE_BLOCK)) * row;
     for (size_t c = 0; c < row; ++c) {
-      Gt->Kb[(size_t)j * row + c] = load_elem(Gt->kc, src + c, Gt->dtype);
-      Gt->Vb[(size_t)j * row + c] = load_elem(Gt->vc, src + c, Gt->dtype);
+      if (Gt->dtype == OR_I8) {             /* dequantise: code * scale of (head, channel) c */
+        Gt->Kb[(size_t)j * row + c] = (double)((const int8_t*)Gt->kc)[src + c] * (double)Gt->k_scale[c];
+        Gt->Vb[(size_t)j * row + c] = (double)((const int8_t*)Gt->vc)[src + c] * (double)Gt->v_scale[c];
+      } else {
+        Gt->Kb[(size_t)j * row + c] = load_elem(Gt->kc, src + c, Gt->dtype);
+        Gt->Vb[(size_t)j * row + c] = load_elem(Gt->vc, src + c, Gt->dtype);
+      }
     }
   }
   return NULL;
@@ -221,14 +277,16 @@ static void* gather_worker(void* arg) {
 
 int pa_oracle_attention(const void* q, int32_t num_tokens, int32_t num_q_heads,
                         const void* k_cache, const void* v_cache, int32_t num_blocks, int32_t num_kv_heads,
-                        int32_t head_dim, int32_t dtype, const int32_t* block_tables, int32_t num_seqs,
+                        int32_t head_dim, int32_t dtype, int32_t cache_dtype, const float* k_scale,
+                        const float* v_scale, const int32_t* block_tables, int32_t num_seqs,
                         int32_t max_blocks, const int32_t* seq_lens, const int32_t* query_start_loc,
                         double scale, int32_t window, const int32_t* rows, int32_t num_rows, void* out,
                         double* out_f64, int32_t num_threads, char* err, int32_t err_len) {
   char m[256];
   if (num_seqs < 1 || num_tokens < 0 || num_q_heads < 1 || num_kv_heads < 1 || head_dim < 1 ||
       num_q_heads % num_kv_heads != 0 || (dtype != OR_F32 && dtype != OR_BF16) || max_blocks < 1 ||
-      window < 0) {
+      window < 0 || (cache_dtype != dtype && !(cache_dtype == OR_I8 && dtype == OR_BF16)) ||
+      (cache_dtype == OR_I8 && (!k_scale || !v_scale))) {
     set_err(err, err_len, "bad sizes");
     return 1;
   }
@@ -296,8 +354,8 @@ int pa_oracle_attention(const void* q, int32_t num_tokens, int32_t num_q_heads,
     }
     gather_t* gt = (gather_t*)malloc(sizeof(gather_t) * (size_t)num_threads);
     for (int i = 0; i < num_threads; ++i) {
-      gather_t g0 = {k_cache, v_cache, dtype, num_kv_heads, head_dim, block_tables + (size_t)b * max_blocks,
-                     Kb, Vb, s, j0, i, num_threads};
+      gather_t g0 = {k_cache, v_cache, cache_dtype, num_kv_heads, head_dim, k_scale, v_scale,
+                     block_tables + (size_t)b * max_blocks, Kb, Vb, s, j0, i, num_threads};
       gt[i] = g0;
       pthread_create(&th[i], NULL, gather_worker, &gt[i]);
     }

@@ -435,3 +435,117 @@ def test_window_rejects_negative():
     w = W.make_batch(1, [20], [20], 2, 2, 64, "f32", num_blocks=3)
     with pytest.raises(Exception):
         oracle_step(w, window=-1)
+
+
+# --------------------------------------------------------------------------------------------
+# 8. 8-bit cache (P2 §4.3, §5.4: INT8 KV cache calibrated per channel).  Reading: symmetric codes
+#    in [-127, 127], one fp32 scale per (KV head, channel); append rounds x / s, computed in fp32,
+#    to the nearest integer with ties to even; NaN -> 0; attention reads code * s.
+# --------------------------------------------------------------------------------------------
+def test_quantize_closed_forms():
+    s = 0.25
+    for n in list(range(-127, 128, 7)) + [-127, 127, 0]:
+        assert oracle.quantize(n * s, s) == n
+    for n, even in [(0, 0), (1, 2), (2, 2), (-1, 0), (-2, -2), (-3, -2), (126, 126), (125, 126)]:
+        assert oracle.quantize((n + 0.5) * s, s) == even, n         # ties go to the even code
+    assert oracle.quantize(128 * s, s) == 127 and oracle.quantize(-1e30, s) == -127
+    assert oracle.quantize(float("inf"), s) == 127 and oracle.quantize(float("-inf"), s) == -127
+    assert oracle.quantize(float("nan"), s) == 0
+
+
+def test_quantize_decides_in_single_precision():
+    """The rounding follows the fp32 quotient (the library's IEEE division), also where the exact
+    quotient lies on the other side of a half-integer."""
+    rng = np.random.default_rng(0)
+    disagreements = 0
+    for _ in range(4000):
+        sc = np.float32(rng.uniform(0.01, 0.05))
+        n = int(rng.integers(-120, 120))
+        x = np.float32((n + 0.5) * float(sc))
+        q32 = np.float32(x) / np.float32(sc)
+        expect = int(np.clip(np.rint(q32), -127, 127))
+        assert oracle.quantize(float(x), float(sc)) == expect
+        if expect != int(np.clip(np.rint(float(x) / float(sc)), -127, 127)):
+            disagreements += 1
+    assert disagreements > 0      # the sample exercises cases where fp64 would decide differently
+
+
+def _i8_batch(seed, lens, qlens, Hq=4, Hkv=2, d=64, pow2=False):
+    w = W.make_batch(seed, lens, qlens, Hq, Hkv, d, "bf16", num_blocks=sum((s + 15) // 16 for s in lens) + 3,
+                     cache="i8")
+    if pow2:
+        rng = np.random.default_rng(seed)
+        w.k_scale = (2.0 ** -rng.integers(4, 8, (Hkv, d))).astype(np.float32)
+        w.v_scale = (2.0 ** -rng.integers(4, 8, (Hkv, d))).astype(np.float32)
+    return w
+
+
+def test_int8_append_writes_quantised_rows_at_slots_and_nothing_else():
+    w = _i8_batch(31, [40, 20], [40, 3])
+    st = w.steps[0]
+    kc, vc = w.k_cache0.copy(), w.v_cache0.copy()
+    oracle.append(st.k_new, st.v_new, st.slot_mapping, kc, vc, w.k_scale, w.v_scale)
+    for new, cache0, cache, sc in [(st.k_new, w.k_cache0, kc, w.k_scale), (st.v_new, w.v_cache0, vc, w.v_scale)]:
+        x = W.to_float(new, "bf16")
+        expect = np.clip(np.rint(x / sc[None]), -127, 127).astype(np.int8)     # numpy fp32 division
+        flat, flat0 = cache.reshape(-1, 2, 64), cache0.reshape(-1, 2, 64)
+        assert np.array_equal(flat[st.slot_mapping], expect)
+        others = np.setdiff1d(np.arange(flat.shape[0]), st.slot_mapping)
+        assert np.array_equal(flat[others], flat0[others])
+
+
+def test_int8_attention_equals_fp32_attention_over_dequantised_cache_bitwise():
+    """With power-of-two scales every code * scale is exact in fp32, so reading the int8 cache must
+    give the very doubles that the fp32 path computes from the dequantised cache."""
+    w = _i8_batch(32, [300, 47, 128], [1, 1, 20], Hq=8, Hkv=2, d=64, pow2=True)
+    st = w.steps[0]
+    kc, vc = w.k_cache0.copy(), w.v_cache0.copy()
+    _, o8 = oracle.run_step(w, st, kc, vc, want_f64=True)
+    kf = (kc.astype(np.float32) * w.k_scale[None, None]).astype(np.float32)
+    vf = (vc.astype(np.float32) * w.v_scale[None, None]).astype(np.float32)
+    qf = W.to_float(st.q, "bf16")
+    _, of = oracle.attention(qf, kf, vf, st.block_tables, st.seq_lens, st.query_start_loc, w.scale, want_f64=True)
+    assert np.array_equal(o8, of)
+
+
+@pytest.mark.parametrize("window", [0, 37])
+def test_int8_attention_matches_library_softmax_over_dequantised_values(window):
+    w = _i8_batch(33, [200, 65, 90], [1, 65, 7], Hq=4, Hkv=2, d=64)
+    st = w.steps[0]
+    kc, vc = w.k_cache0.copy(), w.v_cache0.copy()
+    _, o64 = oracle.run_step(w, st, kc, vc, want_f64=True, window=window)
+    for b in range(3):
+        s = int(st.seq_lens[b])
+        sl = W.slots_for(st.block_tables, b, np.arange(s))
+        k = kc.reshape(-1, 2, 64)[sl].astype(np.float64) * w.k_scale[None].astype(np.float64)
+        v = vc.reshape(-1, 2, 64)[sl].astype(np.float64) * w.v_scale[None].astype(np.float64)
+        a, e = st.query_start_loc[b], st.query_start_loc[b + 1]
+        ctx = s - (e - a)
+        ref = _sdpa_rows_over_windows(f64(w, st.q[a:e]), k, v, w.scale, ctx, window or s)
+        assert np.max(np.abs(o64[a:e] - ref)) <= TOL64, b
+
+
+def test_int8_argmax_probe_returns_dequantised_target_exactly():
+    d, Hq, Hkv, S = 64, 4, 2, 67
+    for target in [0, 15, 16, 40, S - 1]:
+        w = _i8_batch(34, [S], [1], Hq=Hq, Hkv=Hkv, d=d, pow2=True)
+        w.k_scale[:, 0] = 1.0
+        st = w.steps[0]
+        kc, vc = w.k_cache0.copy(), w.v_cache0.copy()
+        slots = W.slots_for(st.block_tables, 0, np.arange(S))
+        kflat = kc.reshape(-1, Hkv, d)
+        kflat[slots[:-1]] = 0
+        knew = np.zeros((1, Hkv, d), np.float32)
+        if target == S - 1:
+            knew[0, :, 0] = 127.0
+        else:
+            kflat[slots[target], :, 0] = 127
+        qf = np.zeros((1, Hq, d), np.float32)
+        qf[:, :, 0] = 64.0
+        st2 = W.Step(q=W.to_storage(qf, "bf16"), k_new=W.to_storage(knew, "bf16"), v_new=st.v_new,
+                     slot_mapping=st.slot_mapping, seq_lens=st.seq_lens, query_start_loc=st.query_start_loc,
+                     block_tables=st.block_tables)
+        out, _ = oracle.run_step(w, st2, kc, vc)
+        vt = vc.reshape(-1, Hkv, d)[slots[target]].astype(np.float32) * w.v_scale      # exact
+        expect = np.repeat(W.to_storage(vt, "bf16"), Hq // Hkv, axis=0)
+        assert np.array_equal(out[0], expect), target
