@@ -7,15 +7,16 @@ kernels.  There is no fallback: if the library is missing or built for another A
     append_kv(k, v, slot_mapping, k_cache, v_cache)
     attention(q, k_cache, v_cache, block_tables, seq_lens, query_start_loc, scale, out, window=0)
 
-Caches are ``[num_blocks, 16, num_kv_heads, head_dim]`` tensors (float32 or bfloat16),
-``q``/``out`` are ``[num_tokens, num_q_heads, head_dim]``, indices are int32.
+Caches are ``[num_blocks, 16, num_kv_heads, head_dim]`` tensors (float32, bfloat16, or int8
+codes with ``k_scale``/``v_scale`` float32 ``[num_kv_heads, head_dim]`` scales and bfloat16
+activations), ``q``/``out`` are ``[num_tokens, num_q_heads, head_dim]``, indices are int32.
 """
 from __future__ import annotations
 
 import ctypes
 import os
 
-ABI_VERSION = 2
+ABI_VERSION = 3
 BLOCK_SIZE = 16
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libpa.so")
@@ -32,7 +33,8 @@ class PAError(RuntimeError):
 
 class _CacheDesc(ctypes.Structure):
     _fields_ = [("num_blocks", ctypes.c_int32), ("block_size", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32),
-                ("head_dim", ctypes.c_int32), ("dtype", ctypes.c_int32)]
+                ("head_dim", ctypes.c_int32), ("dtype", ctypes.c_int32), ("k_scale", ctypes.c_void_p),
+                ("v_scale", ctypes.c_void_p)]
 
 
 class _AttnOpts(ctypes.Structure):
@@ -86,7 +88,15 @@ def _dtype_code(t):
         return 0
     if t.dtype == torch.bfloat16:
         return 1
-    raise TypeError(f"unsupported dtype {t.dtype} (float32 or bfloat16)")
+    if t.dtype == torch.int8:
+        return 2
+    raise TypeError(f"unsupported cache dtype {t.dtype} (float32, bfloat16 or int8)")
+
+
+def _act_dtype(k_cache):
+    """dtype of q, k, v and out for this cache."""
+    import torch
+    return torch.bfloat16 if k_cache.dtype == torch.int8 else k_cache.dtype
 
 
 def _check_tensor(name, t, device, dtype=None, ndim=None):
@@ -103,11 +113,23 @@ def _check_tensor(name, t, device, dtype=None, ndim=None):
         raise ValueError(f"{name} must have {ndim} dims, got {tuple(t.shape)}")
 
 
-def _desc(k_cache):
+def _desc(k_cache, k_scale=None, v_scale=None):
+    import torch
     nb, bs, hkv, d = k_cache.shape
     if bs != BLOCK_SIZE:
         raise ValueError(f"cache block size must be {BLOCK_SIZE}, got {bs}")
-    return _CacheDesc(nb, bs, hkv, d, _dtype_code(k_cache))
+    code = _dtype_code(k_cache)
+    if code == 2:
+        if k_scale is None or v_scale is None:
+            raise ValueError("an int8 cache needs k_scale and v_scale")
+        for name, t in (("k_scale", k_scale), ("v_scale", v_scale)):
+            _check_tensor(name, t, k_cache.device, dtype=torch.float32, ndim=2)
+            if tuple(t.shape) != (hkv, d):
+                raise ValueError(f"{name} must be [{hkv}, {d}], got {tuple(t.shape)}")
+        return _CacheDesc(nb, bs, hkv, d, code, k_scale.data_ptr(), v_scale.data_ptr())
+    if k_scale is not None or v_scale is not None:
+        raise ValueError("k_scale / v_scale are for int8 caches only")
+    return _CacheDesc(nb, bs, hkv, d, code)
 
 
 def _stream(device):
@@ -115,8 +137,9 @@ def _stream(device):
     return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
 
 
-def append_kv(k, v, slot_mapping, k_cache, v_cache):
-    """Write each token's K/V row ([T, Hkv, d]) to cache slot slot_mapping[t] (negative = skip)."""
+def append_kv(k, v, slot_mapping, k_cache, v_cache, k_scale=None, v_scale=None):
+    """Write each token's K/V row ([T, Hkv, d]) to cache slot slot_mapping[t] (negative = skip);
+    int8 caches store the per-(head, channel) quantised codes of the bf16 rows."""
     import torch
     lib = load_library()
     dev = k_cache.device
@@ -124,21 +147,22 @@ def append_kv(k, v, slot_mapping, k_cache, v_cache):
     _check_tensor("v_cache", v_cache, dev, dtype=k_cache.dtype, ndim=4)
     if v_cache.shape != k_cache.shape:
         raise ValueError("k_cache and v_cache shapes differ")
-    _check_tensor("k", k, dev, dtype=k_cache.dtype, ndim=3)
-    _check_tensor("v", v, dev, dtype=k_cache.dtype, ndim=3)
+    _check_tensor("k", k, dev, dtype=_act_dtype(k_cache), ndim=3)
+    _check_tensor("v", v, dev, dtype=_act_dtype(k_cache), ndim=3)
     _check_tensor("slot_mapping", slot_mapping, dev, dtype=torch.int32, ndim=1)
     T = k.shape[0]
     if v.shape != k.shape or tuple(k.shape[1:]) != tuple(k_cache.shape[2:]) or slot_mapping.shape[0] != T:
         raise ValueError("k/v must be [T, Hkv, d] matching the cache, slot_mapping [T]")
-    desc = _desc(k_cache)
+    desc = _desc(k_cache, k_scale, v_scale)
     rc = lib.pa_append_kv(k.data_ptr(), v.data_ptr(), slot_mapping.data_ptr(), T, k_cache.data_ptr(),
                           v_cache.data_ptr(), ctypes.byref(desc), _stream(dev))
     _err(lib, rc)
 
 
-def workspace_size(num_seqs, num_q_tokens, max_blocks_per_seq, num_q_heads, k_cache) -> int:
+def workspace_size(num_seqs, num_q_tokens, max_blocks_per_seq, num_q_heads, k_cache, k_scale=None,
+                   v_scale=None) -> int:
     lib = load_library()
-    desc = _desc(k_cache)
+    desc = _desc(k_cache, k_scale, v_scale)
     return int(lib.pa_attention_workspace_size(num_seqs, num_q_tokens, max_blocks_per_seq, num_q_heads,
                                                ctypes.byref(desc)))
 
@@ -154,16 +178,19 @@ def _workspace(dev, nbytes):
 
 
 def attention(q, k_cache, v_cache, block_tables, seq_lens, query_start_loc, scale, out, workspace=None,
-              window=0):
+              window=0, k_scale=None, v_scale=None):
     """Causal attention of the varlen batch over the paged cache; writes ``out`` in place.
 
-    ``window`` > 0 restricts each query row to its ``window`` most recent keys (pa_attention_ex)."""
+    ``window`` > 0 restricts each query row to its ``window`` most recent keys (pa_attention_ex);
+    int8 caches take their ``k_scale``/``v_scale``."""
     import torch
     lib = load_library()
     dev = q.device
     _check_tensor("q", q, dev, ndim=3)
-    _check_tensor("k_cache", k_cache, dev, dtype=q.dtype, ndim=4)
-    _check_tensor("v_cache", v_cache, dev, dtype=q.dtype, ndim=4)
+    _check_tensor("k_cache", k_cache, dev, ndim=4)
+    _check_tensor("v_cache", v_cache, dev, dtype=k_cache.dtype, ndim=4)
+    if q.dtype != _act_dtype(k_cache):
+        raise TypeError(f"q must be {_act_dtype(k_cache)} for a {k_cache.dtype} cache, got {q.dtype}")
     _check_tensor("out", out, dev, dtype=q.dtype, ndim=3)
     _check_tensor("block_tables", block_tables, dev, dtype=torch.int32, ndim=2)
     _check_tensor("seq_lens", seq_lens, dev, dtype=torch.int32, ndim=1)
@@ -176,7 +203,7 @@ def attention(q, k_cache, v_cache, block_tables, seq_lens, query_start_loc, scal
         raise ValueError("out must match q, head_dim must match the cache")
     if seq_lens.shape[0] != B or query_start_loc.shape[0] != B + 1:
         raise ValueError("seq_lens must be [B], query_start_loc [B+1]")
-    desc = _desc(k_cache)
+    desc = _desc(k_cache, k_scale, v_scale)
     opts = _AttnOpts(int(window))
     need = int(lib.pa_attention_workspace_size(B, T, MB, Hq, ctypes.byref(desc)))
     if need == 0:

@@ -108,7 +108,8 @@ size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 // Where each piece of an attention call lives in the workspace, and what runs.
 struct Plan {
-  bool bf16 = false;
+  bool bf16 = false;      // bf16 activations (bf16 or int8 cache)
+  bool i8 = false;        // int8 cache
   int head_dim = 0, group = 0, heads_per_wg = 0;
   bool run_decode = false, run_tiles = false;
   int rows = 0, per_token = 0, split = 0, max_splits = 0;
@@ -121,7 +122,12 @@ int validate_desc(const pa_cache_desc* c) {
   if (c->block_size != PA_BLOCK_SIZE) return fail(PA_ERR_INVALID_ARG, "block_size must be 16 (got %d)", c->block_size);
   if (c->num_blocks < 1) return fail(PA_ERR_INVALID_ARG, "num_blocks must be >= 1 (got %d)", c->num_blocks);
   if (c->num_kv_heads < 1) return fail(PA_ERR_INVALID_ARG, "num_kv_heads must be >= 1 (got %d)", c->num_kv_heads);
-  if (c->dtype != PA_DTYPE_F32 && c->dtype != PA_DTYPE_BF16) return fail(PA_ERR_UNSUPPORTED, "unsupported dtype %d", c->dtype);
+  if (c->dtype != PA_DTYPE_F32 && c->dtype != PA_DTYPE_BF16 && c->dtype != PA_DTYPE_I8)
+    return fail(PA_ERR_UNSUPPORTED, "unsupported dtype %d", c->dtype);
+  if (c->dtype == PA_DTYPE_I8 && (!c->k_scale || !c->v_scale))
+    return fail(PA_ERR_INVALID_ARG, "an int8 cache needs k_scale and v_scale");
+  if (c->dtype != PA_DTYPE_I8 && (c->k_scale || c->v_scale))
+    return fail(PA_ERR_INVALID_ARG, "k_scale / v_scale are for int8 caches only");
   if (c->head_dim != 64 && c->head_dim != 128) return fail(PA_ERR_UNSUPPORTED, "head_dim must be 64 or 128 (got %d)", c->head_dim);
   return PA_OK;
 }
@@ -136,7 +142,8 @@ int make_plan(int32_t B, int32_t T, int32_t MB, int32_t Hq, const pa_cache_desc*
   if ((int64_t)MB * PA_BLOCK_SIZE > (1 << 30)) return fail(PA_ERR_INVALID_ARG, "max_blocks_per_seq too large");
   if (Hq < 1 || Hq % c->num_kv_heads != 0)
     return fail(PA_ERR_INVALID_ARG, "num_q_heads (%d) must be a positive multiple of num_kv_heads (%d)", Hq, c->num_kv_heads);
-  p.bf16 = c->dtype == PA_DTYPE_BF16;
+  p.i8 = c->dtype == PA_DTYPE_I8;
+  p.bf16 = c->dtype == PA_DTYPE_BF16 || p.i8;
   p.head_dim = c->head_dim;
   p.group = Hq / c->num_kv_heads;
   // bf16 decode holds up to 16 query heads of a KV head per wave (the MFMA column count); the
@@ -157,6 +164,8 @@ int make_plan(int32_t B, int32_t T, int32_t MB, int32_t Hq, const pa_cache_desc*
     p.run_tiles = T > B;                         // some request has q_len >= 2
     p.pos_per_tile = pa::kTileRows / p.group;
     p.num_slots = (T + p.pos_per_tile - 1) / p.pos_per_tile + B;
+    if (p.i8 && p.run_tiles)
+      return fail(PA_ERR_UNSUPPORTED, "int8 caches serve q_len == 1 rows only (num_q_tokens %d > num_seqs %d)", T, B);
   } else {
     p.per_token = 1;
     p.rows = T;
@@ -262,7 +271,7 @@ int pa_append_kv(const void* k, const void* v, const int32_t* slot_mapping, int3
   if (!k || !v || !slot_mapping || !k_cache || !v_cache) return fail(PA_ERR_INVALID_ARG, "null pointer argument");
   if (k_cache == v_cache) return fail(PA_ERR_INVALID_ARG, "k_cache and v_cache must differ");
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  const int64_t esz = cache->dtype == PA_DTYPE_BF16 ? 2 : 4;
+  const int64_t esz = cache->dtype == PA_DTYPE_F32 ? 4 : 2;         // input rows (bf16 for int8 caches)
   if (check_on()) {
     pa::CheckArgs c{};
     c.slot_mapping = slot_mapping;
@@ -271,7 +280,8 @@ int pa_append_kv(const void* k, const void* v, const int32_t* slot_mapping, int3
     rc = run_check(c, s);
     if (rc) return rc;
   }
-  pa::AppendArgs a{k, v, slot_mapping, k_cache, v_cache, num_tokens, (int64_t)cache->num_kv_heads * cache->head_dim * esz};
+  pa::AppendArgs a{k, v, slot_mapping, k_cache, v_cache, num_tokens, (int64_t)cache->num_kv_heads * cache->head_dim * esz,
+                   cache->k_scale, cache->v_scale};
   hipError_t e = timed("append", s, [&] { return pa::launch_append(a, s); });
   if (e != hipSuccess) return device_fail(e, "append launch");
   return PA_OK;
@@ -376,7 +386,11 @@ int pa_attention_ex(const void* q, int32_t num_q_tokens, int32_t num_q_heads, co
     d.max_splits = p.max_splits;
     d.window = window;
     d.scale_log2 = scale_log2;
-    hipError_t e = timed("decode_split", s, [&] { return pa::launch_decode_split(d, p.head_dim, p.bf16, s); });
+    d.k_scale = cache->k_scale;
+    d.v_scale = cache->v_scale;
+    hipError_t e = timed("decode_split", s, [&] {
+      return p.i8 ? pa::launch_decode_split_i8(d, p.head_dim, s) : pa::launch_decode_split(d, p.head_dim, p.bf16, s);
+    });
     if (e != hipSuccess) return device_fail(e, "decode split launch");
     if (p.max_splits > 1) {
       e = timed("decode_merge", s, [&] { return pa::launch_decode_merge(d, p.head_dim, p.bf16, s); });

@@ -5,6 +5,11 @@
 // index).  With the position-major cache layout a token's row is contiguous in the cache, so
 // the scatter is a coalesced 16-byte-per-lane copy: consecutive lanes move consecutive 16-byte
 // pieces of the same row.
+//
+// 8-bit caches (P2 §4.3, §5.4: INT8 KV with per-channel calibration): the append quantises
+// instead of copying.  Element c of a token row (c = head * d + channel) becomes
+// clamp(rne(x / s_c), -127, 127) with the division rounded to fp32 and NaN mapped to 0; a lane
+// handles 8 elements (16 bytes of bf16 in, 8 bytes of codes out).
 #include "pa_common.h"
 #include "pa_internal.h"
 
@@ -28,12 +33,47 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
   }
 }
 
+__device__ __forceinline__ uint32_t quantize(float x, float s) {
+  float r = __fdiv_rn(x, s);
+  if (r != r) return 0u;
+  r = fminf(fmaxf(rintf(r), -127.f), 127.f);
+  return (uint32_t)(int)r & 0xFFu;
+}
+
+__device__ __forceinline__ uint2 quantize8(const uint4& x, const float4& s0, const float4& s1) {
+  uint2 o;
+  o.x = quantize(bf16_lo(x.x), s0.x) | quantize(bf16_hi(x.x), s0.y) << 8 | quantize(bf16_lo(x.y), s0.z) << 16 |
+        quantize(bf16_hi(x.y), s0.w) << 24;
+  o.y = quantize(bf16_lo(x.z), s1.x) | quantize(bf16_hi(x.z), s1.y) << 8 | quantize(bf16_lo(x.w), s1.z) << 16 |
+        quantize(bf16_hi(x.w), s1.w) << 24;
+  return o;
+}
+
+__global__ __launch_bounds__(256) void append_i8_kernel(AppendArgs a) {
+  const int64_t per_row = a.row_bytes >> 4;                 // 8-element pieces per token row
+  const int64_t total = a.num_tokens * per_row;
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; c < total; c += stride) {
+    const int64_t tok = c / per_row;
+    const int64_t piece = c - tok * per_row;
+    const int32_t slot = a.slot_mapping[tok];
+    if (slot < 0) continue;
+    const int64_t src = tok * per_row + piece;
+    const int64_t dst = (int64_t)slot * per_row + piece;
+    const float4* ks = reinterpret_cast<const float4*>(a.k_scale) + 2 * piece;
+    const float4* vs = reinterpret_cast<const float4*>(a.v_scale) + 2 * piece;
+    reinterpret_cast<uint2*>(a.k_cache)[dst] = quantize8(reinterpret_cast<const uint4*>(a.k)[src], ks[0], ks[1]);
+    reinterpret_cast<uint2*>(a.v_cache)[dst] = quantize8(reinterpret_cast<const uint4*>(a.v)[src], vs[0], vs[1]);
+  }
+}
+
 hipError_t launch_append(const AppendArgs& a, hipStream_t s) {
   const int64_t total = a.num_tokens * (a.row_bytes >> 4);
   int64_t blocks = (total + 255) / 256;
   if (blocks > 65536) blocks = 65536;
   if (blocks < 1) blocks = 1;
-  append_kernel<<<dim3((unsigned)blocks), dim3(256), 0, s>>>(a);
+  if (a.k_scale) append_i8_kernel<<<dim3((unsigned)blocks), dim3(256), 0, s>>>(a);
+  else append_kernel<<<dim3((unsigned)blocks), dim3(256), 0, s>>>(a);
   return hipGetLastError();
 }
 

@@ -25,39 +25,11 @@
 
 #include "pa_common.h"
 #include "pa_internal.h"
+#include "pa_rows.h"
 
 namespace pa {
 
 namespace {
-
-// Resolve a row slot to (request, token, visible keys).  Returns false if the slot is not a
-// row of this pass (bf16 requests with q_len != 1 go to the tile kernel).
-__device__ __forceinline__ bool resolve_row(const DecodeArgs& a, int row, int& b, int& t, int& n_keys) {
-  if (a.per_token) {
-    t = row;
-    int lo = 0, hi = a.num_seqs;                       // qsl[lo] <= t < qsl[hi]
-    while (hi - lo > 1) {
-      const int mid = (lo + hi) >> 1;
-      if (a.qsl[mid] <= t) lo = mid; else hi = mid;
-    }
-    b = lo;
-  } else {
-    b = row;
-    if (a.qsl[b + 1] - a.qsl[b] != 1) return false;
-    t = a.qsl[b];
-  }
-  const int q0 = a.qsl[b];
-  const int ql = a.qsl[b + 1] - q0;
-  n_keys = a.seq_lens[b] - ql + (t - q0) + 1;          // keys 0 .. position of this row
-  return true;
-}
-
-// First key a row with `n_keys` causal keys sees (a sliding window drops the older ones), and the
-// block-aligned key where its splits begin.  Every kernel of the pass derives its ranges from these.
-__device__ __forceinline__ int first_visible(const DecodeArgs& a, int n_keys) { return max(0, n_keys - a.window); }
-__device__ __forceinline__ int split_origin(const DecodeArgs& a, int n_keys) {
-  return first_visible(a, n_keys) & ~(kBlock - 1);
-}
 
 __device__ __forceinline__ float wave_max_over_groups(float v, int lpr) {
   for (int o = lpr; o < kWave; o <<= 1) v = fmaxf(v, __shfl_xor(v, o));
@@ -131,13 +103,13 @@ __device__ __forceinline__ bool get_unit(const DecodeArgs& a, int nzh, Unit& u) 
 // spans of every token row.  Each wave streams all blocks of the split for its head: K goes from
 // HBM straight into A-operand registers (one block ahead), V is copied by direct global->LDS loads
 // into a per-wave double buffer (rows' 16-byte chunks XOR-swizzled so the transpose reads are free
-// of bank conflicts).  NCOL = query-head columns held (power of two >= the heads per KV head).
+// of bank conflicts).  Columns beyond the heads of the workgroup's group are zero.
 // ------------------------------------------------------------------------------------------
 namespace {
 __device__ __forceinline__ int dswz(int r) { return 2 * (r & 7); }
 }
 
-template <int D, int NCOL>
+template <int D>
 __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
   constexpr int NKK = D / 32;                 // 16x16x32 k-steps over d for S^T
   constexpr int NT = D / 16;                  // 16-row d tiles of O^T
@@ -599,14 +571,8 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a) {
 namespace {
 template <int D>
 hipError_t mfma_dispatch(const DecodeArgs& a, dim3 g, hipStream_t s) {
-  const dim3 blk(256);
-  const int hpw = a.heads_per_wg;
-  if (hpw <= 1) decode_mfma_kernel<D, 1><<<g, blk, 0, s>>>(a);
-  else if (hpw <= 2) decode_mfma_kernel<D, 2><<<g, blk, 0, s>>>(a);
-  else if (hpw <= 4) decode_mfma_kernel<D, 4><<<g, blk, 0, s>>>(a);
-  else if (hpw <= 8) decode_mfma_kernel<D, 8><<<g, blk, 0, s>>>(a);
-  else if (hpw <= 16) decode_mfma_kernel<D, 16><<<g, blk, 0, s>>>(a);
-  else return hipErrorInvalidValue;
+  if (a.heads_per_wg < 1 || a.heads_per_wg > 16) return hipErrorInvalidValue;   // 16 MFMA columns
+  decode_mfma_kernel<D><<<g, dim3(256), 0, s>>>(a);
   return hipGetLastError();
 }
 template <int D, bool BF16>

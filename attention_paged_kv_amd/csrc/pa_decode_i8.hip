@@ -1,0 +1,327 @@
+// pa_decode_i8.hip -- split-KV attention for single query rows over an 8-bit cache.
+//
+// The cache holds int8 codes with one fp32 scale per (KV head, channel) for K and for V (P2 §4.3
+// and §5.4: INT8 halves the bytes a decode step must read; calibration is per channel).  The pass
+// stays bound by HBM bandwidth (P3 §3.2), now over half the bytes.  Work split, head-quad
+// workgroups, online softmax in log2 units and the partial layout are those of the bf16 decode
+// kernel; what changes is how the codes meet the matrix cores:
+//   * K: the channel scale is folded into the query, q'[c] = q[c] * k_scale[g][c], rounded once to
+//     bf16 (the B operand); K codes go from HBM straight into A-operand registers and are widened
+//     to bf16, which is exact for |code| <= 127.
+//   * V: the channel scale factors out of the sum over keys, so O is multiplied by v_scale[g][c]
+//     once at the end.  V codes are staged in LDS by direct global->LDS loads and read back with
+//     the 8-bit transpose read (ds_read_b64_tr_b8), which hands each lane 8 keys of one channel:
+//     exactly the A operand of a 16x16x32 product.
+// Keys are consumed in units of 32 (two cache blocks): S^T of both blocks, one softmax update,
+// then O^T += V^T (d x 32 keys) . P^T (32 keys x heads) with v_mfma_f32_16x16x32_bf16.  Masked keys
+// need no zeroing of V: every code is a finite number under a zero probability.
+#include <type_traits>
+
+#include "pa_common.h"
+#include "pa_internal.h"
+#include "pa_rows.h"
+
+namespace pa {
+
+namespace {
+
+typedef int i32x2 __attribute__((ext_vector_type(2)));
+
+// Physical 16-byte chunk of logical chunk q in row r of staged block blk is q ^ vswz(blk, r):
+// with it the transpose reads of a wave hit every LDS bank once.
+template <int D>
+__device__ __forceinline__ int vswz(int blk, int r) {
+  if constexpr (D == 128) return ((r ^ (r >> 2)) & 3) | (blk << 2);
+  else return (((r >> 1) ^ (r >> 2)) & 1) | (blk << 1);
+}
+
+// Eight int8 codes (little-endian in lo, hi) widened to bf16, exactly.
+__device__ __forceinline__ bf16x8 codes_to_bf16(uint32_t lo, uint32_t hi) {
+  bf16x8 r;
+  r[0] = (__bf16)(float)(signed char)(lo);
+  r[1] = (__bf16)(float)(signed char)(lo >> 8);
+  r[2] = (__bf16)(float)(signed char)(lo >> 16);
+  r[3] = (__bf16)(float)(signed char)(lo >> 24);
+  r[4] = (__bf16)(float)(signed char)(hi);
+  r[5] = (__bf16)(float)(signed char)(hi >> 8);
+  r[6] = (__bf16)(float)(signed char)(hi >> 16);
+  r[7] = (__bf16)(float)(signed char)(hi >> 24);
+  return r;
+}
+
+// 8-bit transpose read: in each 16-lane group, lane 2e + h gives the address of bytes 8h..8h+7 of
+// row e of an 8 x 16-byte tile; lane j receives column j of the tile (rows 0..7).
+typedef __attribute__((address_space(3))) i32x2 lds_i32x2_t;
+__device__ __forceinline__ i32x2 lds_read_tr8(const char* p) {
+  return __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2_t*)(const __attribute__((address_space(3))) char*)p);
+}
+
+}  // namespace
+
+template <int D>
+__global__ __launch_bounds__(256, 2) void decode_i8_kernel(DecodeArgs a) {
+  constexpr int NKK = D / 32;                 // 16x16x32 k-steps over d for S^T (8 codes per lane)
+  constexpr int NT = D / 16;                  // 16-row d tiles of O^T
+  constexpr int KL = D / 64;                  // 16-byte K loads per lane and block
+  constexpr int CPR = D / 16;                 // 16-byte chunks per row
+  constexpr int RPI = 1024 / D;               // rows per wave-wide 1 KiB copy
+  constexpr int IPB = kBlock / RPI;           // copies per 16-row block
+  constexpr int UB = 2 * kBlock * D;          // bytes of one staged 32-key unit (two blocks)
+  __shared__ __align__(16) char sV0[4 * UB];  // [wave] buffer 0
+  __shared__ __align__(16) char sV1[4 * UB];  // [wave] buffer 1
+
+  // unit: (row, split, head quad, query-head column group); the wave's KV head is 4 * quad + w
+  const int nzh = (a.group + a.heads_per_wg - 1) / a.heads_per_wg;
+  const int nq = (a.num_kv_heads + 3) / 4;
+  const int nz = nq * nzh;
+  int ib = blockIdx.x;
+  const int z = ib % nz;
+  ib /= nz;
+  const int split = ib % a.max_splits;
+  const int row = ib / a.max_splits;
+  if (row >= a.num_rows) return;
+  int b, t, n_keys;
+  if (!resolve_row(a, row, b, t, n_keys)) return;
+  const int lo = first_visible(a, n_keys);
+  const int kbeg = lo & ~(kBlock - 1);
+  const int k0 = kbeg + split * a.split;
+  if (k0 >= n_keys) return;
+  const int k1 = min(k0 + a.split, n_keys);
+  const int n_splits = (n_keys - kbeg + a.split - 1) / a.split;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int g = 4 * (z / nzh) + w;
+  if (g >= a.num_kv_heads) return;                         // waves are independent: no barriers
+  const int zh = z % nzh;
+  const int h0 = g * a.group + zh * a.heads_per_wg;
+  const int ncols = min(a.heads_per_wg, a.group - zh * a.heads_per_wg);
+
+  const int lane = threadIdx.x & (kWave - 1);
+  const int col = lane & 15;                  // S^T / O^T column = query head; also the K row loaded
+  const int grp = lane >> 4;
+  const float c = a.scale_log2;
+
+  // q' = q * k_scale as the B operand.  Step kk covers channels 64(kk/2) + 16grp + 8(kk%2) + [0, 8)
+  // (any order of the channels works as long as K uses the same one).
+  bf16x8 qb[NKK];
+  {
+    const bool on = col < ncols;
+    const uint16_t* qp = reinterpret_cast<const uint16_t*>(a.q) + ((int64_t)t * a.num_q_heads + h0 + (on ? col : 0)) * D;
+    const float* ksp = a.k_scale + (int64_t)g * D;
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) {
+      const int d0 = 64 * (kk >> 1) + 16 * grp + 8 * (kk & 1);
+      const uint4 v = on ? *reinterpret_cast<const uint4*>(qp + d0) : make_uint4(0, 0, 0, 0);
+      const float4 s0 = *reinterpret_cast<const float4*>(ksp + d0);
+      const float4 s1 = *reinterpret_cast<const float4*>(ksp + d0 + 4);
+      qb[kk][0] = (__bf16)(bf16_lo(v.x) * s0.x);
+      qb[kk][1] = (__bf16)(bf16_hi(v.x) * s0.y);
+      qb[kk][2] = (__bf16)(bf16_lo(v.y) * s0.z);
+      qb[kk][3] = (__bf16)(bf16_hi(v.y) * s0.w);
+      qb[kk][4] = (__bf16)(bf16_lo(v.z) * s1.x);
+      qb[kk][5] = (__bf16)(bf16_hi(v.z) * s1.y);
+      qb[kk][6] = (__bf16)(bf16_lo(v.w) * s1.z);
+      qb[kk][7] = (__bf16)(bf16_hi(v.w) * s1.w);
+    }
+  }
+
+  const int64_t rs = (int64_t)a.num_kv_heads * D;          // bytes per cache token row
+  const int64_t blkbytes = kBlock * rs;
+  const char* kbase = reinterpret_cast<const char*>(a.k_cache) + (int64_t)g * D;
+  const char* vbase = reinterpret_cast<const char*>(a.v_cache) + (int64_t)g * D;
+  const int32_t* table = a.block_tables + (int64_t)b * a.max_blocks;
+  const int kb0 = k0 / kBlock;
+  const int nb = (k1 + kBlock - 1) / kBlock - kb0;         // <= 64: splits are at most 1024 keys
+  const int nu = (nb + 1) >> 1;                            // 32-key units
+  const int ids = lane < nb ? table[kb0 + lane] : 0;       // lane i: id of the split's i-th block
+
+  // K operand: key row `col`, bytes 64j + 16grp .. +16 of it
+  const uint32_t k_lane = (uint32_t)(col * rs) + 16 * grp;
+  // V copy i of staged block sb: lane -> (row RPI*i + lane / CPR, physical chunk lane % CPR)
+  uint32_t v_lane[2][IPB];
+#pragma unroll
+  for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+    for (int i = 0; i < IPB; ++i) {
+      const int r = RPI * i + lane / CPR;
+      v_lane[sb][i] = (uint32_t)(r * rs) + (((lane % CPR) ^ vswz<D>(sb, r)) * 16);
+    }
+  // transpose read of tile tt: lane 2e + hh of group grp -> key e of the group, i.e. staged block
+  // e / 4, row 4grp + e % 4, channels 16tt + 8hh .. +7
+  uint32_t tr_off[NT];
+  {
+    const int e = col >> 1, hh = col & 1;
+    const int sb = e >> 2, r = 4 * grp + (e & 3);
+#pragma unroll
+    for (int tt = 0; tt < NT; ++tt) tr_off[tt] = sb * (kBlock * D) + r * D + ((tt ^ vswz<D>(sb, r)) * 16) + 8 * hh;
+  }
+
+  float m = -INFINITY, lsum = 0.f;
+  floatx4 O[NT];
+#pragma unroll
+  for (int tt = 0; tt < NT; ++tt) O[tt] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+  // unit u = blocks 2u and 2u + 1 of the split; a missing second block is replaced by the first
+  // (valid memory) and all its keys are masked
+  auto issue = [&](int u, uint4* kr, char* vdst) {
+    const int i1 = min(2 * u + 1, nb - 1);
+    const int64_t o0 = (int64_t)__builtin_amdgcn_readlane(ids, 2 * u) * blkbytes;
+    const int64_t o1 = (int64_t)__builtin_amdgcn_readlane(ids, i1) * blkbytes;
+#pragma unroll
+    for (int j = 0; j < KL; ++j) {
+      kr[j] = *reinterpret_cast<const uint4*>(kbase + o0 + k_lane + 64 * j);
+      kr[KL + j] = *reinterpret_cast<const uint4*>(kbase + o1 + k_lane + 64 * j);
+    }
+    char* vw = vdst + w * UB;
+#pragma unroll
+    for (int i = 0; i < IPB; ++i)
+      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(vbase + o0 + v_lane[0][i]),
+                                       (__attribute__((address_space(3))) void*)(vw + 1024 * i), 16, 0, 0);
+#pragma unroll
+    for (int i = 0; i < IPB; ++i)
+      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(vbase + o1 + v_lane[1][i]),
+                                       (__attribute__((address_space(3))) void*)(vw + kBlock * D + 1024 * i), 16, 0, 0);
+  };
+
+  // one unit; EDGE: it holds keys outside [lo, k1) (the split's last unit, or its first one when a
+  // sliding window starts inside it)
+  auto consume = [&](auto edge_tag, int u, const uint4* kr, const char* vsrc) {
+    constexpr bool EDGE = decltype(edge_tag)::value;
+    floatx4 sA = floatx4{0.f, 0.f, 0.f, 0.f}, sB = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) {
+      const uint4 xa = kr[kk >> 1], xb = kr[KL + (kk >> 1)];
+      const bf16x8 ka = (kk & 1) ? codes_to_bf16(xa.z, xa.w) : codes_to_bf16(xa.x, xa.y);
+      const bf16x8 kb = (kk & 1) ? codes_to_bf16(xb.z, xb.w) : codes_to_bf16(xb.x, xb.y);
+      sA = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qb[kk], sA, 0, 0, 0);
+      sB = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb, qb[kk], sB, 0, 0, 0);
+    }
+    if constexpr (EDGE) {
+      const int base = (kb0 + 2 * u) * kBlock;
+      const int nvis = k1 - base, nlo = lo - base;          // keys [nlo, nvis) of the unit are visible
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int ka = 4 * grp + v, kb = kBlock + 4 * grp + v;
+        if (ka >= nvis || ka < nlo) sA[v] = -INFINITY;
+        if (kb >= nvis || kb < nlo) sB[v] = -INFINITY;
+      }
+    }
+    float bm = fmaxf(fmaxf(fmaxf(sA[0], sA[1]), fmaxf(sA[2], sA[3])), fmaxf(fmaxf(sB[0], sB[1]), fmaxf(sB[2], sB[3])));
+    bm = xor16_max(bm);
+    bm = xor32_max(bm);
+    const float mn = fmaxf(m, bm);
+    const float alpha = (m == -INFINITY) ? 0.f : fast_exp2((m - mn) * c);
+    const float mc = mn * c;
+    bf16x8 pb;
+    float ps = 0.f;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const float pa = fast_exp2(fmaf(sA[v], c, -mc));
+      const float pv = fast_exp2(fmaf(sB[v], c, -mc));
+      ps += pa + pv;
+      pb[v] = (__bf16)pa;
+      pb[4 + v] = (__bf16)pv;
+    }
+    lsum = lsum * alpha + ps;
+    m = mn;
+#pragma unroll
+    for (int tt = 0; tt < NT; ++tt) O[tt] *= alpha;
+    const char* vw = vsrc + w * UB;
+#pragma unroll
+    for (int tt = 0; tt < NT; ++tt) {
+      const i32x2 x = lds_read_tr8(vw + tr_off[tt]);
+      O[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(codes_to_bf16((uint32_t)x[0], (uint32_t)x[1]), pb, O[tt], 0, 0, 0);
+    }
+  };
+  using Full = std::integral_constant<bool, false>;
+  using Edge = std::integral_constant<bool, true>;
+  const bool last_partial = (kb0 + 2 * nu) * kBlock > k1;
+  const bool first_cut = kb0 * kBlock < lo;                // split 0 of a row whose window starts mid-block
+
+  {
+    uint4 kA[2 * KL], kB[2 * KL];
+    issue(0, kA, sV0);
+    int u = 0;
+    if (first_cut && nu > 2) {                             // peel the first pair: unit 0 is an edge
+      issue(1, kB, sV1);
+      consume(Edge{}, 0, kA, sV0);
+      issue(2, kA, sV0);
+      consume(Full{}, 1, kB, sV1);
+      u = 2;
+    }
+    for (; u + 2 < nu; u += 2) {                           // steady state: next unit always exists
+      issue(u + 1, kB, sV1);
+      consume(Full{}, u, kA, sV0);
+      issue(u + 2, kA, sV0);                               // sV0 reads above are ahead in the LDS queue
+      consume(Full{}, u + 1, kB, sV1);
+    }
+    const bool head_cut = first_cut && u == 0;
+    if (u + 1 < nu) {                                      // two units left
+      issue(u + 1, kB, sV1);
+      if (head_cut) consume(Edge{}, u, kA, sV0);
+      else consume(Full{}, u, kA, sV0);
+      if (last_partial) consume(Edge{}, u + 1, kB, sV1);
+      else consume(Full{}, u + 1, kB, sV1);
+    } else {                                               // one unit left
+      if (last_partial || head_cut) consume(Edge{}, u, kA, sV0);
+      else consume(Full{}, u, kA, sV0);
+    }
+  }
+  lsum = xor16_sum(lsum);
+  lsum = xor32_sum(lsum);
+
+  if (col < ncols) {
+    // O^T rows held by this lane are channels 16tt + 4grp + v: apply their V scale
+    const float* vsp = a.v_scale + (int64_t)g * D + 4 * grp;
+#pragma unroll
+    for (int tt = 0; tt < NT; ++tt) {
+      const float4 s = *reinterpret_cast<const float4*>(vsp + 16 * tt);
+      O[tt][0] *= s.x;
+      O[tt][1] *= s.y;
+      O[tt][2] *= s.z;
+      O[tt][3] *= s.w;
+    }
+    const int h = h0 + col;
+    if (n_splits == 1) {
+      const float inv = 1.f / lsum;
+      uint16_t* op = reinterpret_cast<uint16_t*>(a.out) + ((int64_t)t * a.num_q_heads + h) * D;
+#pragma unroll
+      for (int tt = 0; tt < NT; ++tt) {
+        uint2 pk;
+        pk.x = pack_bf16x2(O[tt][0] * inv, O[tt][1] * inv);
+        pk.y = pack_bf16x2(O[tt][2] * inv, O[tt][3] * inv);
+        *reinterpret_cast<uint2*>(op + 16 * tt + 4 * grp) = pk;
+      }
+    } else {
+      const int64_t pidx = ((int64_t)row * a.max_splits + split) * a.num_q_heads + h;
+      float* po = a.part_o + pidx * D;
+#pragma unroll
+      for (int tt = 0; tt < NT; ++tt)
+        *reinterpret_cast<float4*>(po + 16 * tt + 4 * grp) = make_float4(O[tt][0], O[tt][1], O[tt][2], O[tt][3]);
+      if (grp == 0) {
+        a.part_ml[pidx * 2] = m * c;     // log2 units
+        a.part_ml[pidx * 2 + 1] = lsum;
+      }
+    }
+  }
+}
+
+namespace {
+template <int D>
+hipError_t i8_dispatch(const DecodeArgs& a, dim3 g, hipStream_t s) {
+  if (a.heads_per_wg < 1 || a.heads_per_wg > 16) return hipErrorInvalidValue;   // 16 MFMA columns
+  decode_i8_kernel<D><<<g, dim3(256), 0, s>>>(a);
+  return hipGetLastError();
+}
+}  // namespace
+
+hipError_t launch_decode_split_i8(const DecodeArgs& a, int head_dim, hipStream_t s) {
+  const int64_t nzh = (a.group + a.heads_per_wg - 1) / a.heads_per_wg;
+  const int64_t grid = (int64_t)((a.num_kv_heads + 3) / 4) * nzh * a.max_splits * a.num_rows;
+  if (grid <= 0 || grid > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
+  const dim3 g((unsigned)grid);
+  if (head_dim == 128) return i8_dispatch<128>(a, g, s);
+  if (head_dim == 64) return i8_dispatch<64>(a, g, s);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace pa

@@ -20,7 +20,9 @@ struct AppendArgs {
   void* k_cache;
   void* v_cache;
   int64_t num_tokens;
-  int64_t row_bytes;      // Hkv * d * esz
+  int64_t row_bytes;      // Hkv * d * esz of the input rows
+  const float* k_scale;   // int8 caches: [Hkv][d] scales (row elements share the row index)
+  const float* v_scale;   //   nullptr: plain copy
 };
 
 struct DecodeArgs {
@@ -45,6 +47,8 @@ struct DecodeArgs {
   int max_splits;
   int window;             // keys a row sees, its own included (kNoWindow: all earlier keys)
   float scale_log2;       // scale * log2(e)
+  const float* k_scale;   // int8 caches: [Hkv][d]
+  const float* v_scale;
 };
 
 struct TileArgs {
@@ -84,6 +88,7 @@ struct CheckArgs {
 
 hipError_t launch_append(const AppendArgs& a, hipStream_t s);
 hipError_t launch_decode_split(const DecodeArgs& a, int head_dim, bool bf16, hipStream_t s);
+hipError_t launch_decode_split_i8(const DecodeArgs& a, int head_dim, hipStream_t s);
 hipError_t launch_decode_merge(const DecodeArgs& a, int head_dim, bool bf16, hipStream_t s);
 hipError_t launch_plan_tiles(const int32_t* qsl, int num_seqs, int pos_per_tile, int4* tiles, int* num_tiles,
                              hipStream_t s);

@@ -6,12 +6,14 @@ then causal attention of every query row (decode splits + merge, and prefill/chu
 the batch has them).  Inputs are seeded synthetic tensors already resident in HBM.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--config c2|c3|c4|c5|c1] [--window N]
-                    [--no-cpu-baseline]
+                    [--kv bf16|i8] [--no-cpu-baseline]
 
 Prints one JSON line.  The default workload is the 32-request bf16 decode batch (32/32 heads,
 d=128, contexts U[512, 4096], 16384-block pool); its metric is KV-read GB/s.  --window N runs the
 same workload with a sliding window of N keys per query row; work counts then cover only the keys
-and pairs inside the windows.
+and pairs inside the windows.  --kv i8 keeps the workload's shapes and lengths over an 8-bit cache
+(int8 codes, fp32 scale per KV head and channel; decode workloads only): KV bytes count 1 byte per
+element.
 """
 import argparse
 import json
@@ -36,7 +38,8 @@ def log(*a):
 
 
 KERNEL_SOURCES = {
-    "decode_split": ["attention_paged_kv_amd/csrc/pa_decode.hip", "attention_paged_kv_amd/csrc/pa_common.h"],
+    "decode_split": ["attention_paged_kv_amd/csrc/pa_decode.hip", "attention_paged_kv_amd/csrc/pa_decode_i8.hip",
+                     "attention_paged_kv_amd/csrc/pa_rows.h", "attention_paged_kv_amd/csrc/pa_common.h"],
     "prefill_tile": ["attention_paged_kv_amd/csrc/pa_prefill.hip", "attention_paged_kv_amd/csrc/pa_common.h"],
 }
 
@@ -118,6 +121,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", default="c2", choices=["c1", "c2", "c3", "c4", "c5"])
     ap.add_argument("--window", type=int, default=0, help="sliding window in keys (0: none)")
+    ap.add_argument("--kv", default="bf16", choices=["bf16", "i8"], help="cache element type")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-ref-mib", type=int, default=0,
                     help="instead of the hot path, time a plain device copy of this many MiB "
@@ -161,8 +165,11 @@ def main():
         print("--window must be >= 0", file=sys.stderr)
         sys.exit(2)
     win = args.window
+    if args.kv == "i8" and args.config not in ("c2", "c5"):
+        print("--kv i8 serves the decode workloads (c2, c5)", file=sys.stderr)
+        sys.exit(2)
     t0 = time.time()
-    w = W.CONFIGS[args.config]()
+    w = W.CONFIGS[args.config](cache="i8") if args.kv == "i8" else W.CONFIGS[args.config]()
     log(f"generated {w.name} in {time.time() - t0:.1f}s")
     tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
 
@@ -176,22 +183,30 @@ def main():
 
     # c1 is a 17-step sequence; its "step" is the whole sequence.  Others are one step.
     steps = w.steps
-    kc = to_dev(w.k_cache0)
-    vc = to_dev(w.v_cache0)
+    if w.cache_dtype == "i8":
+        kc = torch.from_numpy(w.k_cache0).to(dev)
+        vc = torch.from_numpy(w.v_cache0).to(dev)
+        ks = torch.from_numpy(w.k_scale).to(dev)
+        vs = torch.from_numpy(w.v_scale).to(dev)
+    else:
+        kc = to_dev(w.k_cache0)
+        vc = to_dev(w.v_cache0)
+        ks = vs = None
     dsteps = []
     for st in steps:
         dsteps.append(dict(q=to_dev(st.q), k=to_dev(st.k_new), v=to_dev(st.v_new),
                            slots=to_dev(st.slot_mapping.astype(np.int32)), bt=to_dev(st.block_tables),
                            sl=to_dev(st.seq_lens), qsl=to_dev(st.query_start_loc),
                            out=torch.empty(st.q.shape, dtype=tdt, device=dev)))
-    ws_need = max(pa.workspace_size(st.num_seqs, st.num_tokens, st.block_tables.shape[1], w.num_q_heads, kc)
+    ws_need = max(pa.workspace_size(st.num_seqs, st.num_tokens, st.block_tables.shape[1], w.num_q_heads, kc, ks, vs)
                   for st in steps)
     ws = torch.zeros(max(ws_need, 256), dtype=torch.uint8, device=dev)
 
     def run_step():
         for d in dsteps:
-            pa.append_kv(d["k"], d["v"], d["slots"], kc, vc)
-            pa.attention(d["q"], kc, vc, d["bt"], d["sl"], d["qsl"], w.scale, d["out"], workspace=ws, window=win)
+            pa.append_kv(d["k"], d["v"], d["slots"], kc, vc, ks, vs)
+            pa.attention(d["q"], kc, vc, d["bt"], d["sl"], d["qsl"], w.scale, d["out"], workspace=ws, window=win,
+                         k_scale=ks, v_scale=vs)
 
     # algorithmic work of one step
     kv_bytes = sum(A.kv_read_bytes(st.seq_lens, w.num_kv_heads, w.head_dim, w.esz, st.q_lens, win) for st in steps)
@@ -281,7 +296,7 @@ def main():
         "dtype": w.dtype,
         "data": "synthetic",
         "config": {"workload": wname, "description": w.description + (f", sliding window {win}" if win else ""),
-                   "sliding_window": win, "num_seqs": int(steps[0].num_seqs),
+                   "sliding_window": win, "kv_cache": w.cache_dtype, "num_seqs": int(steps[0].num_seqs),
                    "q_tokens": int(sum(st.num_tokens for st in steps)),
                    "kv_read_bytes": int(kv_bytes), "flops": int(flops), "parallelism": "single-gpu"},
         "kernels": {k: {kk: round(vv, 3) for kk, vv in v.items()} for k, v in kern.items()},

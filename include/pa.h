@@ -35,7 +35,7 @@
 extern "C" {
 #endif
 
-#define PA_ABI_VERSION 2
+#define PA_ABI_VERSION 3
 #define PA_BLOCK_SIZE 16
 
 typedef enum {
@@ -47,17 +47,22 @@ typedef enum {
   PA_ERR_CHECK_FAILED = 5   /* check mode found an invalid index in device-side arguments   */
 } pa_status;
 
-typedef enum { PA_DTYPE_F32 = 0, PA_DTYPE_BF16 = 1 } pa_dtype;
+/* PA_DTYPE_I8: 8-bit cache (P2 §4.3 and §5.4: an INT8 KV cache halves memory and bandwidth and
+ * needs per-channel calibration).  Cache elements are int8 codes in [-127, 127] with one fp32
+ * scale per (KV head, channel) for K and one for V; the value of a code is code * scale. */
+typedef enum { PA_DTYPE_F32 = 0, PA_DTYPE_BF16 = 1, PA_DTYPE_I8 = 2 } pa_dtype;
 
 /* Describes both caches.  block_size must be 16 (P1 §2.3: 16 tokens per block, a 4096-token
- * prompt takes 256 blocks).  head_dim must be 64 or 128.  The same dtype is used for q, k, v,
- * both caches and out. */
+ * prompt takes 256 blocks).  head_dim must be 64 or 128.  For F32 and BF16 caches the same dtype
+ * is used for q, k, v, both caches and out; for I8 caches q, k, v and out are bf16. */
 typedef struct {
   int32_t num_blocks;     /* NB: physical blocks in the pool                                */
   int32_t block_size;     /* must be PA_BLOCK_SIZE                                          */
   int32_t num_kv_heads;   /* Hkv                                                            */
   int32_t head_dim;       /* d: 64 or 128                                                   */
-  int32_t dtype;          /* pa_dtype                                                       */
+  int32_t dtype;          /* pa_dtype of the cache elements                                 */
+  const float* k_scale;   /* I8 only: device fp32 [Hkv][d], finite and > 0 (caller's          */
+  const float* v_scale;   /*   calibration); must be NULL for the other dtypes              */
 } pa_cache_desc;
 
 /* ABI version compiled into the library; a binding must refuse to run if it differs from
@@ -83,13 +88,17 @@ void pa_set_check(int on);
  * written at their page index), P3 §3.1 (a decode step appends its K/V before attending),
  * P4 "把长输入切成块" (a prefill chunk writes its own K/V after reading the earlier ones).
  *
- *   k, v          device, [num_tokens][Hkv][d] contiguous, cache->dtype.  Must not alias the caches.
+ *   k, v          device, [num_tokens][Hkv][d] contiguous, cache->dtype (bf16 for I8 caches).  Must
+ *                 not alias the caches.
  *   slot_mapping  device int32 [num_tokens]: destination slot of each token (block*16 + offset);
  *                 a negative slot skips that token (padding).  Slots must lie in [0, NB*16) and be
  *                 distinct; otherwise the result is undefined (check mode reports it).
  *   k_cache,
  *   v_cache       device, layout above; row `slot` of each is overwritten bit for bit, all other
- *                 bytes are left untouched.
+ *                 bytes are left untouched.  I8 caches: element c of head g is written as the code of
+ *                 x = k[i][g][c] under s = k_scale[g][c] (v likewise): x / s rounded to fp32 (IEEE
+ *                 division), then to the nearest integer with ties to even, clamped to [-127, 127];
+ *                 NaN gives 0.
  * num_tokens == 0 is a no-op returning PA_OK.
  */
 int pa_append_kv(const void* k, const void* v, const int32_t* slot_mapping, int32_t num_tokens,
@@ -112,6 +121,8 @@ size_t pa_attention_workspace_size(int32_t num_seqs, int32_t num_q_tokens, int32
  * at absolute position ctx + r and attends to keys 0 .. ctx + r, read through block_tables[b].
  * Query head h uses KV head h / (Hq/Hkv).
  *   out[t][h][:] = sum_j softmax_j(scale * <q[t][h], K[j][g]>) * V[j][g]
+ * where for I8 caches K[j][g][c] = code * k_scale[g][c] and V likewise (q and out are bf16; the
+ * product q[c] * k_scale[g][c] is rounded to bf16 before it meets the codes).
  *
  *   q                device [num_q_tokens][num_q_heads][d], cache->dtype.
  *   k_cache, v_cache device, layout above (already holding this step's appended K/V).

@@ -20,12 +20,16 @@ def say(*a):
 
 def dev_tensor(a, dtype):
     a = np.ascontiguousarray(a)
+    if dtype == "i8":
+        return torch.from_numpy(a.astype(np.int8, copy=False)).to(DEV)
     if dtype == "bf16":
         return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(DEV)
     return torch.from_numpy(a).to(DEV)
 
 
 def host_array(t, dtype):
+    if dtype == "i8":
+        return t.cpu().numpy()
     if dtype == "bf16":
         return t.view(torch.int16).cpu().numpy().view(np.uint16)
     return t.cpu().numpy()
@@ -40,8 +44,12 @@ class GpuState:
 
     def __init__(self, w, kc=None, vc=None):
         self.w = w
-        self.kc = dev_tensor(w.k_cache0 if kc is None else kc, w.dtype)
-        self.vc = dev_tensor(w.v_cache0 if vc is None else vc, w.dtype)
+        self.kc = dev_tensor(w.k_cache0 if kc is None else kc, w.cache_dtype)
+        self.vc = dev_tensor(w.v_cache0 if vc is None else vc, w.cache_dtype)
+        self.ks = self.vs = None
+        if w.cache_dtype == "i8":
+            self.ks = torch.from_numpy(np.ascontiguousarray(w.k_scale)).to(DEV)
+            self.vs = torch.from_numpy(np.ascontiguousarray(w.v_scale)).to(DEV)
 
     def inputs(self, st):
         return dict(q=dev_tensor(st.q, self.w.dtype), k=dev_tensor(st.k_new, self.w.dtype),
@@ -51,9 +59,10 @@ class GpuState:
     def step(self, st, append=True, window=0):
         x = self.inputs(st)
         if append:
-            pa.append_kv(x["k"], x["v"], x["slots"], self.kc, self.vc)
+            pa.append_kv(x["k"], x["v"], x["slots"], self.kc, self.vc, self.ks, self.vs)
         out = torch.empty_like(x["q"])
-        pa.attention(x["q"], self.kc, self.vc, x["bt"], x["sl"], x["qsl"], self.w.scale, out, window=window)
+        pa.attention(x["q"], self.kc, self.vc, x["bt"], x["sl"], x["qsl"], self.w.scale, out, window=window,
+                     k_scale=self.ks, v_scale=self.vs)
         torch.cuda.synchronize()
         return host_array(out, self.w.dtype)
 

@@ -110,6 +110,25 @@ def test_window_option_rejected_when_negative_before_launch(lib):
                                ctypes.byref(win), None) == 4
 
 
+def test_int8_descriptor_rules_checked_before_launch(lib):
+    p = ctypes.c_void_p(16)
+    o = ctypes.c_void_p(48)
+    sc = ctypes.c_void_p(4096)
+    no_scales = _desc(dtype=2)
+    rc = lib.pa_attention(p, 4, 8, p, p, ctypes.byref(no_scales), p, 4, 16, p, p, ctypes.c_float(1), o, None, 0, None)
+    assert rc == 1 and b"k_scale" in lib.pa_last_error()
+    assert lib.pa_append_kv(p, p, p, 4, p, p, ctypes.byref(no_scales), None) == 1
+    stray = pa._CacheDesc(8, 16, 2, 128, 1, sc, sc)          # scales on a bf16 cache
+    assert lib.pa_attention(p, 4, 8, p, p, ctypes.byref(stray), p, 4, 16, p, p, ctypes.c_float(1), o, None, 0,
+                            None) == 1
+    i8 = pa._CacheDesc(8, 16, 2, 128, 2, sc, sc)
+    # q_len >= 2 somewhere (5 tokens over 4 requests): not served on int8 caches, refused before launch
+    assert lib.pa_attention(p, 5, 8, p, p, ctypes.byref(i8), p, 4, 16, p, p, ctypes.c_float(1), o, None, 0,
+                            None) == 2
+    assert b"int8" in lib.pa_last_error()
+    assert lib.pa_attention_workspace_size(4, 4, 64, 8, ctypes.byref(i8)) > 0
+
+
 def test_binding_fails_loudly_without_library(tmp_path):
     with pytest.raises(ImportError):
         saved = pa._lib

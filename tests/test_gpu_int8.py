@@ -1,0 +1,134 @@
+"""GPU parity of the 8-bit KV cache (P2 §4.3, §5.4: INT8 codes with per-channel calibration) against
+the CPU oracle: quantising append bit for bit over the whole cache, attention within the bf16
+tolerances, dequantised argmax probes bit-exact."""
+import numpy as np
+import pytest
+
+import attention_paged_kv_amd as pa
+from attention_paged_kv_amd import workloads as W
+import oracle
+from tests.gpu_helpers import GpuState, compare, host_array, say
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def check_mode():
+    pa.set_check(True)
+    yield
+    pa.set_check(False)
+
+
+def run_i8(w, window=0, rows=None, what=""):
+    st = w.steps[0]
+    g = GpuState(w)
+    out_g = g.step(st, window=window)
+    kc, vc = w.k_cache0.copy(), w.v_cache0.copy()
+    out_r, _ = oracle.run_step(w, st, kc, vc, rows=rows, window=window)
+    assert np.array_equal(host_array(g.kc, "i8"), kc), f"{what}: K codes differ after append"
+    assert np.array_equal(host_array(g.vc, "i8"), vc), f"{what}: V codes differ after append"
+    compare(out_g, out_r, "bf16", rows=rows, what=what)
+    return out_g
+
+
+def i8_batch(seed, seq, Hq, Hkv, d, nb_extra=3):
+    return W.make_batch(seed, seq, [1] * len(seq), Hq, Hkv, d, "bf16",
+                        num_blocks=sum((s + 15) // 16 for s in seq) + nb_extra, cache="i8")
+
+
+CASES = [
+    # seq_lens (all decode rows), Hq, Hkv, d
+    ([1], 1, 1, 128),
+    ([15, 16, 17, 31, 32, 33], 8, 2, 128),
+    ([47, 48, 49, 63, 64, 65], 4, 4, 64),
+    ([255, 256, 257, 511, 512, 513], 32, 8, 128),
+    ([1000, 2048, 3000], 32, 32, 128),
+    ([700, 129, 5], 16, 1, 64),
+    ([1030, 300], 24, 3, 128),
+    ([4097, 9000], 64, 4, 128),
+]
+
+
+@pytest.mark.parametrize("case", range(len(CASES)))
+def test_int8_decode_batches(case):
+    seq, Hq, Hkv, d = CASES[case]
+    say(f"int8 case {case}: seq {seq} Hq {Hq} Hkv {Hkv} d {d}")
+    run_i8(i8_batch(600 + case, seq, Hq, Hkv, d), what=f"int8[{case}]")
+
+
+@pytest.mark.parametrize("window", [1, 16, 17, 100, 1000])
+def test_int8_decode_with_window(window):
+    w = i8_batch(650 + window, [15, 16, 17, 600, 2000, 3001], 8, 2, 128)
+    run_i8(w, window=window, what=f"int8 W={window}")
+
+
+def test_int8_argmax_probe_bit_exact():
+    """Power-of-two scales make code * scale exact; with one dominant key per row the output is its
+    dequantised V row, bit for bit, after the split merge too."""
+    d, Hq, Hkv = 128, 8, 2
+    lens = [67, 300, 1500, 16, 17]
+    w = i8_batch(700, lens, Hq, Hkv, d)
+    rng = np.random.default_rng(7)
+    w.k_scale = (2.0 ** -rng.integers(4, 8, (Hkv, d))).astype(np.float32)
+    w.v_scale = (2.0 ** -rng.integers(4, 8, (Hkv, d))).astype(np.float32)
+    w.k_scale[:, 0] = 1.0
+    st = w.steps[0]
+    kc, vc = w.k_cache0.copy(), w.v_cache0.copy()
+    kflat = kc.reshape(-1, Hkv, d)
+    targets = []
+    for b, s in enumerate(lens):
+        slots = W.slots_for(st.block_tables, b, np.arange(s - 1))
+        kflat[slots] = 0
+        if s > 1:
+            tgt = int(rng.integers(0, s - 1))
+            kflat[slots[tgt], :, 0] = 127
+            targets.append(slots[tgt])
+        else:
+            targets.append(None)
+    knew = np.zeros((len(lens), Hkv, d), np.float32)
+    qf = np.zeros((len(lens), Hq, d), np.float32)
+    qf[:, :, 0] = 64.0
+    st2 = W.Step(q=W.to_storage(qf, "bf16"), k_new=W.to_storage(knew, "bf16"), v_new=st.v_new,
+                 slot_mapping=st.slot_mapping, seq_lens=st.seq_lens, query_start_loc=st.query_start_loc,
+                 block_tables=st.block_tables)
+    g = GpuState(w, kc, vc)
+    out = g.step(st2)
+    for b, tslot in enumerate(targets):
+        if tslot is None:
+            continue
+        vt = vc.reshape(-1, Hkv, d)[tslot].astype(np.float32) * w.v_scale
+        expect = np.repeat(W.to_storage(vt, "bf16"), Hq // Hkv, axis=0)
+        assert np.array_equal(out[b], expect), b
+
+
+def test_int8_repeat_runs_bitwise_identical():
+    w = i8_batch(710, [3000, 47, 900], 32, 8, 128)
+    a = GpuState(w).step(w.steps[0])
+    b = GpuState(w).step(w.steps[0])
+    assert np.array_equal(a, b)
+
+
+def test_int8_rejects_prefill_rows():
+    import torch
+    w = W.make_batch(711, [40, 20], [40, 1], 8, 2, 128, "bf16", num_blocks=8, cache="i8")
+    g = GpuState(w)
+    x = g.inputs(w.steps[0])
+    out = torch.empty_like(x["q"])
+    with pytest.raises(pa.PAError) as e:
+        pa.attention(x["q"], g.kc, g.vc, x["bt"], x["sl"], x["qsl"], w.scale, out, k_scale=g.ks, v_scale=g.vs)
+    assert e.value.code == 2
+
+
+@pytest.mark.timeout(600)
+def test_int8_c2_decode_batch():
+    run_i8(W.config2(cache="i8"), what="c2 int8")
+
+
+@pytest.mark.timeout(600)
+def test_int8_c5_skewed_long_decode():
+    run_i8(W.config5(cache="i8"), what="c5 int8")
+
+
+@pytest.mark.timeout(600)
+def test_int8_c5_window():
+    run_i8(W.config5(cache="i8"), window=4096, what="c5 int8 W=4096")
