@@ -4,16 +4,21 @@
 // and §5.4: INT8 halves the bytes a decode step must read; calibration is per channel).  The pass
 // stays bound by HBM bandwidth (P3 §3.2), now over half the bytes.  Work split, head-quad
 // workgroups, online softmax in log2 units and the partial layout are those of the bf16 decode
-// kernel; what changes is how the codes meet the matrix cores:
-//   * K: the channel scale is folded into the query, q'[c] = q[c] * k_scale[g][c], rounded once to
-//     bf16 (the B operand); K codes go from HBM straight into A-operand registers and are widened
-//     to bf16, which is exact for |code| <= 127.
+// kernel; what changes is how the codes meet the matrix cores (fp16 products, fp32 accumulation):
+//   * Codes become fp16 with byte permutes: u = code + 128 (an XOR of the sign bit) placed under the
+//     fp16 exponent of 1024 is exactly 1024 + u = 1152 + code.
+//   * K: the channel scale is folded into the query, q'[c] = q[c] * k_scale[g][c], scaled by a power
+//     of two per head so that max |q'| lies in [0.5, 1) and rounded once to fp16 (the B operand).
+//     K enters as 1152 + code, so every score of a head carries the same bias 1152 * sum_c q'[c];
+//     it is subtracted once per 32 keys, before the softmax.
 //   * V: the channel scale factors out of the sum over keys, so O is multiplied by v_scale[g][c]
 //     once at the end.  V codes are staged in LDS by direct global->LDS loads and read back with
-//     the 8-bit transpose read (ds_read_b64_tr_b8), which hands each lane 8 keys of one channel:
-//     exactly the A operand of a 16x16x32 product.
+//     the 8-bit transpose read (ds_read_b64_tr_b8), which hands each lane 8 keys of one channel
+//     (the A operand of a 16x16x32 product); one packed fp16 subtraction of 1152 recovers the
+//     exact codes.
 // Keys are consumed in units of 32 (two cache blocks): S^T of both blocks, one softmax update,
-// then O^T += V^T (d x 32 keys) . P^T (32 keys x heads) with v_mfma_f32_16x16x32_bf16.  Masked keys
+// then O^T += V^T (d x 32 keys) . P^T (32 keys x heads) with v_mfma_f32_16x16x32_f16.  O is only
+// rescaled when a head's running max grows by more than 2^8, so P <= 2^8 fits fp16.  Masked keys
 // need no zeroing of V: every code is a finite number under a zero probability.
 #include <type_traits>
 
@@ -26,6 +31,10 @@ namespace pa {
 namespace {
 
 typedef int i32x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kCodeBias = 1152.f;          // value of fp16 bits 0x6400 | (code ^ 0x80)
 
 // Physical 16-byte chunk of logical chunk q in row r of staged block blk is q ^ vswz(blk, r):
 // with it the transpose reads of a wave hit every LDS bank once.
@@ -35,17 +44,28 @@ __device__ __forceinline__ int vswz(int blk, int r) {
   else return (((r >> 1) ^ (r >> 2)) & 1) | (blk << 1);
 }
 
-// Eight int8 codes (little-endian in lo, hi) widened to bf16, exactly.
-__device__ __forceinline__ bf16x8 codes_to_bf16(uint32_t lo, uint32_t hi) {
-  bf16x8 r;
-  r[0] = (__bf16)(float)(signed char)(lo);
-  r[1] = (__bf16)(float)(signed char)(lo >> 8);
-  r[2] = (__bf16)(float)(signed char)(lo >> 16);
-  r[3] = (__bf16)(float)(signed char)(lo >> 24);
-  r[4] = (__bf16)(float)(signed char)(hi);
-  r[5] = (__bf16)(float)(signed char)(hi >> 8);
-  r[6] = (__bf16)(float)(signed char)(hi >> 16);
-  r[7] = (__bf16)(float)(signed char)(hi >> 24);
+// Eight int8 codes (little-endian in lo, hi) as fp16 values 1152 + code, exactly.  v_perm_b32
+// picks bytes of {0x64646464 : x}: selector 0-3 = byte of x, 4 = 0x64.
+__device__ __forceinline__ f16x8 codes_biased_f16(uint32_t lo, uint32_t hi) {
+  lo ^= 0x80808080u;
+  hi ^= 0x80808080u;
+  uint4 r;
+  r.x = __builtin_amdgcn_perm(0x64646464u, lo, 0x04010400u);
+  r.y = __builtin_amdgcn_perm(0x64646464u, lo, 0x04030402u);
+  r.z = __builtin_amdgcn_perm(0x64646464u, hi, 0x04010400u);
+  r.w = __builtin_amdgcn_perm(0x64646464u, hi, 0x04030402u);
+  return __builtin_bit_cast(f16x8, r);
+}
+
+// Eight int8 codes as exact fp16 codes.
+__device__ __forceinline__ f16x8 codes_f16(uint32_t lo, uint32_t hi) {
+  const f16x8 b = codes_biased_f16(lo, hi);
+  const f16x2 nb = f16x2{(_Float16)-kCodeBias, (_Float16)-kCodeBias};
+  f16x8 r;
+  const f16x2 r0 = f16x2{b[0], b[1]} + nb, r1 = f16x2{b[2], b[3]} + nb;
+  const f16x2 r2 = f16x2{b[4], b[5]} + nb, r3 = f16x2{b[6], b[7]} + nb;
+  r[0] = r0[0]; r[1] = r0[1]; r[2] = r1[0]; r[3] = r1[1];
+  r[4] = r2[0]; r[5] = r2[1]; r[6] = r3[0]; r[7] = r3[1];
   return r;
 }
 
@@ -58,8 +78,10 @@ __device__ __forceinline__ i32x2 lds_read_tr8(const char* p) {
 
 }  // namespace
 
-template <int D>
-__global__ __launch_bounds__(256, 2) void decode_i8_kernel(DecodeArgs a) {
+// NW waves per workgroup, one adjacent KV head each: together they read NW * d contiguous bytes of
+// every token row they visit.
+template <int D, int NW>
+__global__ __launch_bounds__(64 * NW, NW == 4 ? 3 : 2) void decode_i8_kernel(DecodeArgs a) {
   constexpr int NKK = D / 32;                 // 16x16x32 k-steps over d for S^T (8 codes per lane)
   constexpr int NT = D / 16;                  // 16-row d tiles of O^T
   constexpr int KL = D / 64;                  // 16-byte K loads per lane and block
@@ -67,12 +89,12 @@ __global__ __launch_bounds__(256, 2) void decode_i8_kernel(DecodeArgs a) {
   constexpr int RPI = 1024 / D;               // rows per wave-wide 1 KiB copy
   constexpr int IPB = kBlock / RPI;           // copies per 16-row block
   constexpr int UB = 2 * kBlock * D;          // bytes of one staged 32-key unit (two blocks)
-  __shared__ __align__(16) char sV0[4 * UB];  // [wave] buffer 0
-  __shared__ __align__(16) char sV1[4 * UB];  // [wave] buffer 1
+  __shared__ __align__(16) char sV0[NW * UB];  // [wave] buffer 0
+  __shared__ __align__(16) char sV1[NW * UB];  // [wave] buffer 1
 
-  // unit: (row, split, head quad, query-head column group); the wave's KV head is 4 * quad + w
+  // unit: (row, split, head group, query-head column group); the wave's KV head is NW * group + w
   const int nzh = (a.group + a.heads_per_wg - 1) / a.heads_per_wg;
-  const int nq = (a.num_kv_heads + 3) / 4;
+  const int nq = (a.num_kv_heads + NW - 1) / NW;
   const int nz = nq * nzh;
   int ib = blockIdx.x;
   const int z = ib % nz;
@@ -89,7 +111,7 @@ __global__ __launch_bounds__(256, 2) void decode_i8_kernel(DecodeArgs a) {
   const int k1 = min(k0 + a.split, n_keys);
   const int n_splits = (n_keys - kbeg + a.split - 1) / a.split;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int g = 4 * (z / nzh) + w;
+  const int g = NW * (z / nzh) + w;
   if (g >= a.num_kv_heads) return;                         // waves are independent: no barriers
   const int zh = z % nzh;
   const int h0 = g * a.group + zh * a.heads_per_wg;
@@ -98,30 +120,52 @@ __global__ __launch_bounds__(256, 2) void decode_i8_kernel(DecodeArgs a) {
   const int lane = threadIdx.x & (kWave - 1);
   const int col = lane & 15;                  // S^T / O^T column = query head; also the K row loaded
   const int grp = lane >> 4;
-  const float c = a.scale_log2;
 
-  // q' = q * k_scale as the B operand.  Step kk covers channels 64(kk/2) + 16grp + 8(kk%2) + [0, 8)
-  // (any order of the channels works as long as K uses the same one).
-  bf16x8 qb[NKK];
+  // q' = q * k_scale * 2^-e as the B operand.  Step kk covers channels 64(kk/2) + 16grp + 8(kk%2)
+  // + [0, 8) (any order of the channels works as long as K uses the same one).  The four lanes
+  // of a column (grp = 0..3) share e, the scaled softmax factor c and the score bias.
+  f16x8 qb[NKK];
+  float c, bias;
   {
     const bool on = col < ncols;
     const uint16_t* qp = reinterpret_cast<const uint16_t*>(a.q) + ((int64_t)t * a.num_q_heads + h0 + (on ? col : 0)) * D;
     const float* ksp = a.k_scale + (int64_t)g * D;
+    float qf[NKK][8];
+    float mx = 0.f;
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk) {
       const int d0 = 64 * (kk >> 1) + 16 * grp + 8 * (kk & 1);
       const uint4 v = on ? *reinterpret_cast<const uint4*>(qp + d0) : make_uint4(0, 0, 0, 0);
       const float4 s0 = *reinterpret_cast<const float4*>(ksp + d0);
       const float4 s1 = *reinterpret_cast<const float4*>(ksp + d0 + 4);
-      qb[kk][0] = (__bf16)(bf16_lo(v.x) * s0.x);
-      qb[kk][1] = (__bf16)(bf16_hi(v.x) * s0.y);
-      qb[kk][2] = (__bf16)(bf16_lo(v.y) * s0.z);
-      qb[kk][3] = (__bf16)(bf16_hi(v.y) * s0.w);
-      qb[kk][4] = (__bf16)(bf16_lo(v.z) * s1.x);
-      qb[kk][5] = (__bf16)(bf16_hi(v.z) * s1.y);
-      qb[kk][6] = (__bf16)(bf16_lo(v.w) * s1.z);
-      qb[kk][7] = (__bf16)(bf16_hi(v.w) * s1.w);
+      qf[kk][0] = bf16_lo(v.x) * s0.x;
+      qf[kk][1] = bf16_hi(v.x) * s0.y;
+      qf[kk][2] = bf16_lo(v.y) * s0.z;
+      qf[kk][3] = bf16_hi(v.y) * s0.w;
+      qf[kk][4] = bf16_lo(v.z) * s1.x;
+      qf[kk][5] = bf16_hi(v.z) * s1.y;
+      qf[kk][6] = bf16_lo(v.w) * s1.z;
+      qf[kk][7] = bf16_hi(v.w) * s1.w;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) mx = fmaxf(mx, fabsf(qf[kk][i]));
     }
+    mx = xor16_max(mx);
+    mx = xor32_max(mx);
+    int e = 0;
+    if (mx > 0.f) frexpf(mx, &e);                           // mx = f * 2^e, f in [0.5, 1)
+    float qs = 0.f;
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const _Float16 h = (_Float16)ldexpf(qf[kk][i], -e);
+        qb[kk][i] = h;
+        qs += (float)h;
+      }
+    qs = xor16_sum(qs);
+    qs = xor32_sum(qs);
+    bias = kCodeBias * qs;                                  // score offset from the biased K codes
+    c = ldexpf(a.scale_log2, e);                            // log2-unit factor of this column's scores
   }
 
   const int64_t rs = (int64_t)a.num_kv_heads * D;          // bytes per cache token row
@@ -190,10 +234,15 @@ __global__ __launch_bounds__(256, 2) void decode_i8_kernel(DecodeArgs a) {
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk) {
       const uint4 xa = kr[kk >> 1], xb = kr[KL + (kk >> 1)];
-      const bf16x8 ka = (kk & 1) ? codes_to_bf16(xa.z, xa.w) : codes_to_bf16(xa.x, xa.y);
-      const bf16x8 kb = (kk & 1) ? codes_to_bf16(xb.z, xb.w) : codes_to_bf16(xb.x, xb.y);
-      sA = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qb[kk], sA, 0, 0, 0);
-      sB = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb, qb[kk], sB, 0, 0, 0);
+      const f16x8 ka = (kk & 1) ? codes_biased_f16(xa.z, xa.w) : codes_biased_f16(xa.x, xa.y);
+      const f16x8 kb = (kk & 1) ? codes_biased_f16(xb.z, xb.w) : codes_biased_f16(xb.x, xb.y);
+      sA = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka, qb[kk], sA, 0, 0, 0);
+      sB = __builtin_amdgcn_mfma_f32_16x16x32_f16(kb, qb[kk], sB, 0, 0, 0);
+    }
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      sA[v] -= bias;
+      sB[v] -= bias;
     }
     if constexpr (EDGE) {
       const int base = (kb0 + 2 * u) * kBlock;
@@ -209,27 +258,30 @@ __global__ __launch_bounds__(256, 2) void decode_i8_kernel(DecodeArgs a) {
     bm = xor16_max(bm);
     bm = xor32_max(bm);
     const float mn = fmaxf(m, bm);
-    const float alpha = (m == -INFINITY) ? 0.f : fast_exp2((m - mn) * c);
-    const float mc = mn * c;
-    bf16x8 pb;
+    if (__any((mn - m) * c > 8.f)) {                       // move the max (and rescale) lazily
+      const float alpha = (m == -INFINITY) ? 0.f : fast_exp2((m - mn) * c);
+      m = mn;
+      lsum *= alpha;
+#pragma unroll
+      for (int tt = 0; tt < NT; ++tt) O[tt] *= alpha;
+    }
+    const float mc = m * c;
+    f16x8 pb;
     float ps = 0.f;
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
       const float pa = fast_exp2(fmaf(sA[v], c, -mc));
       const float pv = fast_exp2(fmaf(sB[v], c, -mc));
       ps += pa + pv;
-      pb[v] = (__bf16)pa;
-      pb[4 + v] = (__bf16)pv;
+      pb[v] = (_Float16)pa;
+      pb[4 + v] = (_Float16)pv;
     }
-    lsum = lsum * alpha + ps;
-    m = mn;
-#pragma unroll
-    for (int tt = 0; tt < NT; ++tt) O[tt] *= alpha;
+    lsum += ps;
     const char* vw = vsrc + w * UB;
 #pragma unroll
     for (int tt = 0; tt < NT; ++tt) {
       const i32x2 x = lds_read_tr8(vw + tr_off[tt]);
-      O[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(codes_to_bf16((uint32_t)x[0], (uint32_t)x[1]), pb, O[tt], 0, 0, 0);
+      O[tt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(codes_f16((uint32_t)x[0], (uint32_t)x[1]), pb, O[tt], 0, 0, 0);
     }
   };
   using Full = std::integral_constant<bool, false>;
@@ -306,21 +358,21 @@ __global__ __launch_bounds__(256, 2) void decode_i8_kernel(DecodeArgs a) {
 }
 
 namespace {
-template <int D>
-hipError_t i8_dispatch(const DecodeArgs& a, dim3 g, hipStream_t s) {
+template <int D, int NW>
+hipError_t i8_dispatch(const DecodeArgs& a, hipStream_t s) {
   if (a.heads_per_wg < 1 || a.heads_per_wg > 16) return hipErrorInvalidValue;   // 16 MFMA columns
-  decode_i8_kernel<D><<<g, dim3(256), 0, s>>>(a);
+  const int64_t nzh = (a.group + a.heads_per_wg - 1) / a.heads_per_wg;
+  const int64_t grid = (int64_t)((a.num_kv_heads + NW - 1) / NW) * nzh * a.max_splits * a.num_rows;
+  if (grid <= 0 || grid > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
+  decode_i8_kernel<D, NW><<<dim3((unsigned)grid), dim3(64 * NW), 0, s>>>(a);
   return hipGetLastError();
 }
 }  // namespace
 
+// Four waves per workgroup: eight (one workgroup per CU at this register count) measured slower.
 hipError_t launch_decode_split_i8(const DecodeArgs& a, int head_dim, hipStream_t s) {
-  const int64_t nzh = (a.group + a.heads_per_wg - 1) / a.heads_per_wg;
-  const int64_t grid = (int64_t)((a.num_kv_heads + 3) / 4) * nzh * a.max_splits * a.num_rows;
-  if (grid <= 0 || grid > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
-  const dim3 g((unsigned)grid);
-  if (head_dim == 128) return i8_dispatch<128>(a, g, s);
-  if (head_dim == 64) return i8_dispatch<64>(a, g, s);
+  if (head_dim == 128) return i8_dispatch<128, 4>(a, s);
+  if (head_dim == 64) return i8_dispatch<64, 4>(a, s);
   return hipErrorInvalidValue;
 }
 
