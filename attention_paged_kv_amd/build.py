@@ -1,4 +1,4 @@
-"""Build libpa.so (HIP kernels + C ABI) for gfx950 with hipcc, in-tree.
+"""Build libpa.so (HIP kernels + C ABI, and the host step planner) for gfx950 with hipcc, in-tree.
 
     python -m attention_paged_kv_amd.build [-v]
 """
@@ -15,6 +15,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libpa.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+CXX = os.environ.get("CXX", "g++")
 ARCH = "gfx950"
 
 # -packed-fp32-ops: keep the compiler from forming packed fp32 VALU ops (v_pk_*_f32).
@@ -28,16 +29,23 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-I", INCLUDE,
 EXTRA = {"pa_prefill.hip": ["-fno-honor-nans"]}
 
 
+# Host-only C++ (no device code) is compiled by the host compiler.
+HOST = ["-O2", "-std=c++17", "-fPIC", "-I", INCLUDE, "-I", CSRC, "-Wall", "-Wextra"]
+
+
 def _compile(src, verbose):
     obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
-    cmd = [HIPCC, *COMMON, *EXTRA.get(os.path.basename(src), []), "-c", src, "-o", obj]
+    if src.endswith(".cpp"):
+        cmd = [CXX, *HOST, "-c", src, "-o", obj]
+    else:
+        cmd = [HIPCC, *COMMON, *EXTRA.get(os.path.basename(src), []), "-c", src, "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
     out = "\n".join(l for l in (r.stdout + r.stderr).splitlines()
                     if "packed-fp32-ops' is not a recognized feature" not in l)
     if r.returncode != 0:
-        raise RuntimeError(f"hipcc failed for {src}:\n{out}")
+        raise RuntimeError(f"compiling {src} failed:\n{out}")
     if out.strip() and verbose:
         print(out)
     return obj
@@ -45,7 +53,7 @@ def _compile(src, verbose):
 
 def build(verbose: bool = False) -> str:
     os.makedirs(BUILD_DIR, exist_ok=True)
-    srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
+    srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")) + glob.glob(os.path.join(CSRC, "*.cpp")))
     with cf.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
         objs = list(ex.map(lambda s: _compile(s, verbose), srcs))
     tmp = LIB + ".tmp"

@@ -14,13 +14,15 @@
 #include <vector>
 
 #include "pa.h"
+#include "pa_error.h"
 #include "pa_internal.h"
 
 namespace {
-
 thread_local std::string g_err;
+}  // namespace
 
-int fail(int code, const char* fmt, ...) {
+namespace pa {
+int set_error(int code, const char* fmt, ...) {
   char buf[512];
   va_list ap;
   va_start(ap, fmt);
@@ -28,6 +30,15 @@ int fail(int code, const char* fmt, ...) {
   va_end(ap);
   g_err = buf;
   return code;
+}
+void clear_error() { g_err.clear(); }
+}  // namespace pa
+
+namespace {
+
+template <class... A>
+int fail(int code, const char* fmt, A... args) {
+  return pa::set_error(code, fmt, args...);
 }
 
 int device_fail(hipError_t e, const char* what) {
