@@ -116,3 +116,20 @@ def test_planner_errors_leave_state_untouched():
         Planner(0, 4, 32)
     with pytest.raises(pa.PAError):
         Planner(16, 4, 0)
+
+
+@pytest.mark.parametrize("seed,nb,budget,prefix", [(0, 40, 96, True), (1, 18, 64, True), (2, 40, 96, False)])
+def test_planned_steps_on_the_paged_oracle_equal_attention_from_scratch(seed, nb, budget, prefix):
+    """The planner's batches, run by the oracle over one shared paged cache (blocks reused across
+    requests by the prefix cache, recycled after evictions, rewritten after preemption), give bit
+    for bit what the oracle gives from scratch on a contiguous cache per request."""
+    from tests.serving_helpers import OraclePagedExecutor, drive
+
+    def check(out, ref, step, b):
+        assert np.array_equal(out, ref), step
+    c = drive(seed, nb, budget, prefix, OraclePagedExecutor(nb), check)
+    assert c["steps"] > 20
+    if prefix:
+        assert c["hits"] > 0
+    if nb < 20:
+        assert c["preempts"] > 0
