@@ -372,7 +372,9 @@ int pa_sched_schedule(pa_sched* s, pa_sched_batch* out) {
     out->request_ids[i] = r->id;
     out->seq_lens[i] = p.start + p.n;
     int32_t* row = out->block_tables + (int64_t)i * mb;
-    for (int32_t j = 0; j < mb; ++j) row[j] = j < (int32_t)r->blocks.size() ? r->blocks[j] : -1;
+    const size_t nbk = r->blocks.size();
+    std::memcpy(row, r->blocks.data(), nbk * sizeof(int32_t));
+    std::fill(row + nbk, row + mb, -1);
     for (int32_t q = p.start; q < p.start + p.n; ++q, ++t) {
       out->slot_mapping[t] = r->blocks[q / kBlk] * kBlk + q % kBlk;
       out->token_ids[t] = r->tokens[q];

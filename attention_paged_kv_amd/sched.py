@@ -128,26 +128,39 @@ class Planner:
     def abort(self, request_id):
         _check(self._l, self._l.pa_sched_abort(self._h, int(request_id)))
 
+    def _buffers(self, cap_s):
+        """Host arrays the planner writes into, kept across steps and grown when needed."""
+        if getattr(self, "_cap_s", 0) < cap_s:
+            cap_s = max(cap_s, 2 * getattr(self, "_cap_s", 0))
+            cap_t = self.token_budget
+            self._arr = dict(ids=np.zeros(cap_s, np.int64), qsl=np.zeros(cap_s + 1, np.int32),
+                             sl=np.zeros(cap_s, np.int32), bt=np.zeros((cap_s, self.mb), np.int32),
+                             slots=np.zeros(cap_t, np.int32), toks=np.zeros(cap_t, np.int32),
+                             pos=np.zeros(cap_t, np.int32), smp=np.zeros(cap_s, np.int32))
+            a = self._arr
+            self._batch = _Batch(cap_s, cap_t, 0, 0, a["ids"].ctypes.data_as(_I64P), a["qsl"].ctypes.data_as(_I32P),
+                                 a["sl"].ctypes.data_as(_I32P), a["bt"].ctypes.data_as(_I32P),
+                                 a["slots"].ctypes.data_as(_I32P), a["toks"].ctypes.data_as(_I32P),
+                                 a["pos"].ctypes.data_as(_I32P), a["smp"].ctypes.data_as(_I32P))
+            self._cap_s = cap_s
+        return self._arr, self._batch
+
     def schedule(self) -> Batch:
+        """Plans one step; the returned arrays are copies the caller may keep."""
         st = self.stats()
-        cap_s = self.max_seqs if self.max_seqs > 0 else max(1, st["running"] + st["waiting"])
-        cap_t = self.token_budget
-        ids = np.zeros(cap_s, np.int64)
-        qsl = np.zeros(cap_s + 1, np.int32)
-        sl = np.zeros(cap_s, np.int32)
-        bt = np.full((cap_s, self.mb), -1, np.int32)
-        slots = np.zeros(cap_t, np.int32)
-        toks = np.zeros(cap_t, np.int32)
-        pos = np.zeros(cap_t, np.int32)
-        smp = np.zeros(cap_s, np.int32)
-        b = _Batch(cap_s, cap_t, 0, 0, ids.ctypes.data_as(_I64P), qsl.ctypes.data_as(_I32P),
-                   sl.ctypes.data_as(_I32P), bt.ctypes.data_as(_I32P), slots.ctypes.data_as(_I32P),
-                   toks.ctypes.data_as(_I32P), pos.ctypes.data_as(_I32P), smp.ctypes.data_as(_I32P))
+        a, b = self._buffers(self.max_seqs if self.max_seqs > 0 else max(1, st["running"] + st["waiting"]))
         _check(self._l, self._l.pa_sched_schedule(self._h, ctypes.byref(b)))
         n, t = b.num_seqs, b.num_tokens
         self._last = n
-        return Batch(ids[:n].copy(), qsl[:n + 1].copy(), sl[:n].copy(), bt[:n].copy(), slots[:t].copy(),
-                     toks[:t].copy(), pos[:t].copy(), smp[:n].copy())
+        return Batch(a["ids"][:n].copy(), a["qsl"][:n + 1].copy(), a["sl"][:n].copy(), a["bt"][:n].copy(),
+                     a["slots"][:t].copy(), a["toks"][:t].copy(), a["pos"][:t].copy(), a["smp"][:n].copy())
+
+    def schedule_views(self, cap_seqs):
+        """Plans one step into the planner's own buffers (no copies; valid until the next call).
+        Returns (num_seqs, num_tokens, arrays)."""
+        a, b = self._buffers(cap_seqs)
+        _check(self._l, self._l.pa_sched_schedule(self._h, ctypes.byref(b)))
+        return b.num_seqs, b.num_tokens, a
 
     def commit(self, next_tokens, stop=None):
         nt = np.ascontiguousarray(next_tokens if len(next_tokens) else [0], dtype=np.int32)
@@ -165,3 +178,43 @@ class Planner:
         buf = np.zeros(4096, np.int64)
         _check(self._l, self._l.pa_sched_preempted(self._h, buf.ctypes.data_as(_I64P), 4096, ctypes.byref(n)))
         return [int(x) for x in buf[:min(n.value, 4096)]]
+
+
+def bench_planner(decodes=30, prompt=30000, budget=2048, wide=256, wide_ctx=2048):
+    """Host cost of the C++ planner, in microseconds per schedule + commit (median over steps, the
+    planner writing into preallocated host arrays), for two step shapes: P4's mixed step
+    (`decodes` users decoding while a `prompt`-token prompt goes through in `budget`-token chunks)
+    and a wide decode batch (`wide` requests of `wide_ctx` tokens)."""
+    import time
+
+    def timed_steps(p, cap, stop_when=None, n=None):
+        nt = np.full(max(cap, 1), 7, np.int32)
+        nt_p = nt.ctypes.data_as(_I32P)
+        times, k = [], 0
+        while True:
+            t0 = time.perf_counter()
+            ns, _, a = p.schedule_views(cap)
+            _check(p._l, p._l.pa_sched_commit(p._h, nt_p, None))
+            times.append(time.perf_counter() - t0)
+            k += 1
+            if (stop_when and stop_when(ns, a)) or (n and k == n):
+                return 1e6 * float(np.median(times)), k
+
+    out = {}
+    p = Planner(8192, 4096, budget)
+    for i in range(decodes):
+        p.add(i, [1000 + i] * 8, 60000)
+    timed_steps(p, 64, n=3)
+    p.add(10 ** 6, list(range(prompt)), 4)
+    big = lambda ns, a: any(a["ids"][j] == 10 ** 6 and a["smp"][j] == 1 for j in range(ns))
+    out["mixed_chunked_us_per_step"], out["mixed_chunked_steps"] = timed_steps(p, 64, stop_when=big)
+    mb = wide_ctx // 16 + 16
+    q = Planner(wide * mb, mb, wide * 8)
+    for i in range(wide):
+        q.add(i, [i % 97 + 1] * wide_ctx, 200)
+    while q.stats()["waiting"]:
+        timed_steps(q, wide, n=1)
+    timed_steps(q, wide, n=3)
+    out["decode_batch_us_per_step"], _ = timed_steps(q, wide, n=50)
+    out["decode_batch_seqs"] = wide
+    return out

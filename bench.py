@@ -280,6 +280,8 @@ def main():
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(w, steps, is_decode, kv_bytes, win)
+    from attention_paged_kv_amd.sched import bench_planner
+    planner = {k: (round(v, 2) if isinstance(v, float) else v) for k, v in bench_planner().items()}
 
     res = {
         "metric": METRIC,
@@ -302,6 +304,7 @@ def main():
         "kernels": {k: {kk: round(vv, 3) for kk, vv in v.items()} for k, v in kern.items()},
         "roofline": roof,
         "cpu_baseline": cpu,
+        "host_planner": planner,
     }
     print(json.dumps(res), flush=True)
 
