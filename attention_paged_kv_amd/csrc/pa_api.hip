@@ -123,7 +123,7 @@ struct Plan {
   bool i8 = false;        // int8 cache
   int head_dim = 0, group = 0, heads_per_wg = 0;
   bool run_decode = false, run_tiles = false;
-  int rows = 0, per_token = 0, split = 0, max_splits = 0;
+  int rows = 0, per_token = 0, qmax = 1, split = 0, max_splits = 0;
   int pos_per_tile = 0, num_slots = 0;
   size_t off_o = 0, off_ml = 0, off_tiles = 0, off_ntiles = 0, total = 0;
 };
@@ -157,9 +157,13 @@ int make_plan(int32_t B, int32_t T, int32_t MB, int32_t Hq, const pa_cache_desc*
   p.bf16 = c->dtype == PA_DTYPE_BF16 || p.i8;
   p.head_dim = c->head_dim;
   p.group = Hq / c->num_kv_heads;
-  // bf16 decode holds up to 16 query heads of a KV head per wave (the MFMA column count); the
-  // fp32 vector-ALU decode holds a divisor of the group size up to 8.
-  if (p.bf16) p.heads_per_wg = p.group < 16 ? p.group : 16;
+  // A bf16 request row carries up to qmax positions: min(kVerifyMax, the longest q_len the sizes
+  // allow); int8 and fp32 rows carry one.  bf16 decode holds up to 16 (position, query head)
+  // columns of a KV head per wave (the MFMA column count); the fp32 vector-ALU decode holds a
+  // divisor of the group size up to 8.
+  const int longest = T - B + 1;
+  p.qmax = (c->dtype == PA_DTYPE_BF16) ? (longest < pa::kVerifyMax ? longest : pa::kVerifyMax) : 1;
+  if (p.bf16) p.heads_per_wg = p.qmax * p.group < 16 ? p.qmax * p.group : 16;
   else p.heads_per_wg = (p.group % 8 == 0) ? 8 : (p.group % 4 == 0) ? 4 : (p.group % 2 == 0) ? 2 : 1;
   if (p.bf16 && p.group > pa::kTileRows)
     return fail(PA_ERR_UNSUPPORTED, "query heads per KV head (%d) above %d", p.group, pa::kTileRows);
@@ -171,8 +175,8 @@ int make_plan(int32_t B, int32_t T, int32_t MB, int32_t Hq, const pa_cache_desc*
   if (p.bf16) {
     p.per_token = 0;
     p.rows = B;
-    p.run_decode = !(B == 1 && T >= 2);          // some request may have q_len == 1
-    p.run_tiles = T > B;                         // some request has q_len >= 2
+    p.run_decode = !(B == 1 && T > p.qmax);      // some request may have q_len <= qmax
+    p.run_tiles = longest > p.qmax;              // some request may have q_len > qmax
     p.pos_per_tile = pa::kTileRows / p.group;
     p.num_slots = (T + p.pos_per_tile - 1) / p.pos_per_tile + B;
     if (p.i8 && p.run_tiles)
@@ -185,7 +189,7 @@ int make_plan(int32_t B, int32_t T, int32_t MB, int32_t Hq, const pa_cache_desc*
   }
   size_t off = 0;
   if (p.run_decode && p.max_splits > 1) {
-    const size_t units = (size_t)p.rows * p.max_splits * Hq;
+    const size_t units = (size_t)p.rows * p.qmax * p.max_splits * Hq;
     p.off_o = off;
     off = align256(off + units * p.head_dim * sizeof(float));
     p.off_ml = off;
@@ -198,7 +202,7 @@ int make_plan(int32_t B, int32_t T, int32_t MB, int32_t Hq, const pa_cache_desc*
     off = align256(off + sizeof(int));
   }
   p.total = off;
-  const int64_t nzh = (p.group + p.heads_per_wg - 1) / p.heads_per_wg;
+  const int64_t nzh = ((int64_t)p.qmax * p.group + p.heads_per_wg - 1) / p.heads_per_wg;
   const int64_t heads = p.bf16 ? (c->num_kv_heads + 3) / 4 : c->num_kv_heads;
   const int64_t dec_grid = heads * nzh * p.max_splits * p.rows;
   if (p.run_decode && dec_grid > 0x7FFFFFFF) return fail(PA_ERR_UNSUPPORTED, "batch too large for one launch");
@@ -388,6 +392,7 @@ int pa_attention_ex(const void* q, int32_t num_q_tokens, int32_t num_q_heads, co
     d.num_seqs = num_seqs;
     d.num_rows = p.rows;
     d.per_token = p.per_token;
+    d.qmax = p.qmax;
     d.num_q_heads = num_q_heads;
     d.num_kv_heads = cache->num_kv_heads;
     d.group = p.group;
@@ -412,7 +417,7 @@ int pa_attention_ex(const void* q, int32_t num_q_tokens, int32_t num_q_heads, co
     int4* tiles = reinterpret_cast<int4*>(ws + p.off_tiles);
     int* ntiles = reinterpret_cast<int*>(ws + p.off_ntiles);
     hipError_t e = timed("plan", s, [&] {
-      return pa::launch_plan_tiles(query_start_loc, num_seqs, p.pos_per_tile, tiles, ntiles, s);
+      return pa::launch_plan_tiles(query_start_loc, num_seqs, p.pos_per_tile, p.qmax + 1, tiles, ntiles, s);
     });
     if (e != hipSuccess) return device_fail(e, "plan launch");
     pa::TileArgs t{};

@@ -81,7 +81,8 @@ __device__ __forceinline__ bool get_unit(const DecodeArgs& a, int nzh, Unit& u) 
   u.split = i % a.max_splits;
   u.row = i / a.max_splits;
   if (u.row >= a.num_rows) return false;
-  if (!resolve_row(a, u.row, u.b, u.t, u.n_keys)) return false;
+  int ql;
+  if (!resolve_row(a, u.row, u.b, u.t, u.n_keys, ql)) return false;   // per-token rows: ql == 1
   u.lo = first_visible(a, u.n_keys);
   const int kbeg = u.lo & ~(kBlock - 1);
   u.k0 = kbeg + u.split * a.split;
@@ -99,14 +100,24 @@ __device__ __forceinline__ bool get_unit(const DecodeArgs& a, int nzh, Unit& u) 
 
 // ------------------------------------------------------------------------------------------
 // bf16: matrix-core split kernel.  A workgroup covers four adjacent KV heads of the
-// same query row and split (one wave each), so together its waves read contiguous 4 x 256-byte
+// same request and split (one wave each), so together its waves read contiguous 4 x 256-byte
 // spans of every token row.  Each wave streams all blocks of the split for its head: K goes from
 // HBM straight into A-operand registers (one block ahead), V is copied by direct global->LDS loads
 // into a per-wave double buffer (rows' 16-byte chunks XOR-swizzled so the transpose reads are free
-// of bank conflicts).  Columns beyond the heads of the workgroup's group are zero.
+// of bank conflicts).  The MFMA columns are (position, query head) pairs of the request: a decode
+// row has one position, a row of a few tokens to verify (P4 "一步的 token 预算": speculative
+// verification advances several tokens in one step) has q_len of them, each masked to its own
+// causal (and window) range, so the K/V of the request are read once for all of them.  Unused
+// columns are zero.
 // ------------------------------------------------------------------------------------------
 namespace {
-__device__ __forceinline__ int dswz(int r) { return 2 * (r & 7); }
+// Physical 16-byte chunk of logical chunk q in staged V row r is q ^ dswz<D>(r): a permutation of the
+// row's D/8 chunks that keeps the transpose reads of a wave on distinct LDS banks.
+template <int D>
+__device__ __forceinline__ int dswz(int r) {
+  if constexpr (D == 128) return 2 * (r & 7);
+  else return (((r ^ (r >> 2)) & 1) << 1) | (((r >> 1) & 1) << 2);
+}
 }
 
 template <int D>
@@ -121,201 +132,205 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
   __shared__ __align__(16) char sV0[4 * VB];  // [wave] buffer 0
   __shared__ __align__(16) char sV1[4 * VB];  // [wave] buffer 1
 
-  // unit: (row, split, head quad, query-head column group); the wave's KV head is 4 * quad + w
-  const int nzh = (a.group + a.heads_per_wg - 1) / a.heads_per_wg;
+  // unit: (row, split, head quad), the quad fastest; the wave's KV head is 4 * quad + w.  A row
+  // with more (position, head) columns than one MFMA holds runs its column groups one after the
+  // other in the same workgroup (the K/V re-read comes straight after the first), so the grid has
+  // no workgroups that find nothing to do.
   const int nq = (a.num_kv_heads + 3) / 4;
-  const int nz = nq * nzh;
   int ib = blockIdx.x;
-  const int z = ib % nz;
-  ib /= nz;
+  const int quad = ib % nq;
+  ib /= nq;
   const int split = ib % a.max_splits;
   const int row = ib / a.max_splits;
   if (row >= a.num_rows) return;
-  int b, t, n_keys;
-  if (!resolve_row(a, row, b, t, n_keys)) return;
-  const int lo = first_visible(a, n_keys);                 // keys before lo are outside the window
-  const int kbeg = lo & ~(kBlock - 1);
+  int b, t0, n_keys, ql;
+  if (!resolve_row(a, row, b, t0, n_keys, ql)) return;
+  const int ctx = n_keys - ql;                             // keys before the request's first position
+  const int lo_min = first_visible(a, ctx + 1);            // oldest key any position sees
+  const int lo_max = first_visible(a, n_keys);             // oldest key the last position sees
+  const int kbeg = lo_min & ~(kBlock - 1);
   const int k0 = kbeg + split * a.split;
   if (k0 >= n_keys) return;
   const int k1 = min(k0 + a.split, n_keys);
   const int n_splits = (n_keys - kbeg + a.split - 1) / a.split;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int g = 4 * (z / nzh) + w;
+  const int g = 4 * quad + w;
   if (g >= a.num_kv_heads) return;                         // waves are independent: no barriers
-  const int zh = z % nzh;
-  const int h0 = g * a.group + zh * a.heads_per_wg;
-  const int ncols = min(a.heads_per_wg, a.group - zh * a.heads_per_wg);
+  for (int zh = 0; zh * a.heads_per_wg < ql * a.group; ++zh) {
+    const int c0 = zh * a.heads_per_wg;                      // first (position, head) column of the group
+    const int ncols = min(a.heads_per_wg, ql * a.group - c0);
 
-  const int lane = threadIdx.x & (kWave - 1);
-  const int col = lane & 15;                  // S^T / O^T column = query head; also the K row loaded
-  const int grp = lane >> 4;                  // 4-key group of the accumulator layout
-  const float c = a.scale_log2;
-
-  // Q^T as the B operand: lane holds d = 32kk + 8grp .. +8 of head h0 + col
-  bf16x8 qb[NKK];
-  {
+    const int lane = threadIdx.x & (kWave - 1);
+    const int col = lane & 15;                  // S^T / O^T column; also the K row loaded
+    const int grp = lane >> 4;                  // 4-key group of the accumulator layout
+    const float c = a.scale_log2;
     const bool on = col < ncols;
-    const char* qp = reinterpret_cast<const char*>(a.q) +
-                     (((int64_t)t * a.num_q_heads + h0 + (on ? col : 0)) * D + 8 * grp) * 2;
-#pragma unroll
-    for (int kk = 0; kk < NKK; ++kk) {
-      const uint4 v = on ? *reinterpret_cast<const uint4*>(qp + kk * 64) : make_uint4(0, 0, 0, 0);
-      qb[kk] = __builtin_bit_cast(bf16x8, v);
-    }
-  }
+    const int cr = on ? (c0 + col) / a.group : 0;            // this column's position in the request
+    const int h = g * a.group + (on ? (c0 + col) % a.group : 0);
+    const int nvis = ctx + cr + 1;                           // keys [lo_c, nvis) are this column's
+    const int lo_c = first_visible(a, nvis);
 
-  const int64_t rs = (int64_t)a.num_kv_heads * D;            // elements per cache token row
-  const int64_t blkbytes = kBlock * rs * 2;
-  const char* kbase = reinterpret_cast<const char*>(a.k_cache) + (int64_t)g * ROWB;
-  const char* vbase = reinterpret_cast<const char*>(a.v_cache) + (int64_t)g * ROWB;
-  const int32_t* table = a.block_tables + (int64_t)b * a.max_blocks;
-  const int kb0 = k0 / kBlock;
-  const int nb = (k1 + kBlock - 1) / kBlock - kb0;        // <= 64: splits are at most 1024 keys
-  const int ids = lane < nb ? table[kb0 + lane] : 0;       // lane i: id of the split's i-th block
-
-  // K operand: key row `col`, d = 32kk + 8grp: byte offset within the block
-  const uint32_t k_lane = (uint32_t)(col * rs * 2) + 16 * grp;
-  // V copy: copy i covers rows RPI*i ..; lane -> (row RPI*i + lane / CPR, physical chunk lane % CPR)
-  uint32_t v_lane[IPB];
-#pragma unroll
-  for (int i = 0; i < IPB; ++i) {
-    const int r = RPI * i + lane / CPR;
-    v_lane[i] = (uint32_t)(r * rs * 2) + (((lane % CPR) ^ dswz(r)) * 16);
-  }
-  // transpose read: group grp, lane j = 4e + cq reads row 4grp + e, columns 16tt + 4cq .. +3,
-  // i.e. logical chunk 2tt + cq / 2, byte half cq & 1
-  uint32_t tr_off[NT];
-#pragma unroll
-  for (int tt = 0; tt < NT; ++tt) {
-    const int r = 4 * grp + (col >> 2);
-    const int lq = 2 * tt + ((col & 3) >> 1);
-    tr_off[tt] = r * ROWB + ((lq ^ dswz(r)) * 16) + (col & 1) * 8;
-  }
-
-  float m = -INFINITY, lsum = 0.f;
-  floatx4 O[NT];
-#pragma unroll
-  for (int tt = 0; tt < NT; ++tt) O[tt] = floatx4{0.f, 0.f, 0.f, 0.f};
-
-  auto issue = [&](int i, uint4* kr, char* vdst) {        // block kb0 + i: K to registers, V to LDS
-    const char* kb = kbase + (int64_t)__builtin_amdgcn_readlane(ids, i) * blkbytes;
-    const char* vb = vbase + (kb - kbase);
-#pragma unroll
-    for (int kk = 0; kk < NKK; ++kk) kr[kk] = *reinterpret_cast<const uint4*>(kb + k_lane + kk * 64);
-#pragma unroll
-    for (int j = 0; j < IPB; ++j)
-      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(vb + v_lane[j]),
-                                       (__attribute__((address_space(3))) void*)(vdst + w * VB + 1024 * j), 16, 0, 0);
-  };
-
-  // one block; EDGE: the block holds keys outside [lo, k1) -- past the last visible one (the
-  // split's last block) or before a sliding window (the first block of split 0)
-  auto consume = [&](auto edge_tag, int i, const uint4* kr, const char* vsrc) {
-    constexpr bool EDGE = decltype(edge_tag)::value;
-    floatx4 s = floatx4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int kk = 0; kk < NKK; ++kk)
-      s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kr[kk]), qb[kk], s, 0, 0, 0);
-    const int nvis = k1 - (kb0 + i) * kBlock;               // keys of this block below k1
-    const int nlo = lo - (kb0 + i) * kBlock;                // keys of this block below lo
-    if constexpr (EDGE) {
-#pragma unroll
-      for (int v = 0; v < 4; ++v)
-        if (4 * grp + v >= nvis || 4 * grp + v < nlo) s[v] = -INFINITY;
-    }
-    float bm = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
-    bm = xor16_max(bm);
-    bm = xor32_max(bm);
-    const float mn = fmaxf(m, bm);
-    const float alpha = (m == -INFINITY) ? 0.f : fast_exp2((m - mn) * c);
-    const float mc = mn * c;
-    float p[4];
-#pragma unroll
-    for (int v = 0; v < 4; ++v) p[v] = fast_exp2(fmaf(s[v], c, -mc));
-    lsum = lsum * alpha + ((p[0] + p[1]) + (p[2] + p[3]));
-    m = mn;
-    bf16x4 pb;
-#pragma unroll
-    for (int v = 0; v < 4; ++v) pb[v] = (__bf16)p[v];
-#pragma unroll
-    for (int tt = 0; tt < NT; ++tt) O[tt] *= alpha;
-    const char* vw = vsrc + w * VB;
-    bf16x4 vt[NT];
-#pragma unroll
-    for (int tt = 0; tt < NT; ++tt) vt[tt] = lds_read_tr(reinterpret_cast<const uint16_t*>(vw + tr_off[tt]));
-    if constexpr (EDGE) {
-      // rows outside [lo, k1) may hold poison under p = 0: zero them
-#pragma unroll
-      for (int tt = 0; tt < NT; ++tt)
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          if (4 * grp + e >= nvis || 4 * grp + e < nlo) vt[tt][e] = (__bf16)0.f;
-    }
-#pragma unroll
-    for (int tt = 0; tt < NT; ++tt) O[tt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vt[tt], pb, O[tt], 0, 0, 0);
-  };
-  using Full = std::integral_constant<bool, false>;
-  using Edge = std::integral_constant<bool, true>;
-  const bool last_partial = (kb0 + nb) * kBlock > k1;
-  const bool first_cut = kb0 * kBlock < lo;                // split 0 of a row whose window starts mid-block
-
-  {
-    uint4 kA[NKK], kB[NKK];
-    issue(0, kA, sV0);
-    int i = 0;
-    if (first_cut && nb > 2) {                             // peel the first pair: block 0 is an edge
-      issue(1, kB, sV1);
-      consume(Edge{}, 0, kA, sV0);
-      issue(2, kA, sV0);
-      consume(Full{}, 1, kB, sV1);
-      i = 2;
-    }
-    for (; i + 2 < nb; i += 2) {                           // steady state: next block always exists
-      issue(i + 1, kB, sV1);
-      consume(Full{}, i, kA, sV0);
-      issue(i + 2, kA, sV0);                               // sV0 reads above are ahead in the LDS queue
-      consume(Full{}, i + 1, kB, sV1);
-    }
-    const bool head_cut = first_cut && i == 0;            // block i is still the first one
-    if (i + 1 < nb) {                                      // two blocks left
-      issue(i + 1, kB, sV1);
-      if (head_cut) consume(Edge{}, i, kA, sV0);
-      else consume(Full{}, i, kA, sV0);
-      if (last_partial) consume(Edge{}, i + 1, kB, sV1);
-      else consume(Full{}, i + 1, kB, sV1);
-    } else {                                               // one block left
-      if (last_partial || head_cut) consume(Edge{}, i, kA, sV0);
-      else consume(Full{}, i, kA, sV0);
-    }
-  }
-  lsum = xor16_sum(lsum);
-  lsum = xor32_sum(lsum);
-
-  // this wave holds the whole split for its head: write the row or the split's partial
-  if (col < ncols) {
-    const int h = h0 + col;
-    if (n_splits == 1) {
-      const float inv = 1.f / lsum;
-      uint16_t* op = reinterpret_cast<uint16_t*>(a.out) + ((int64_t)t * a.num_q_heads + h) * D;
-#pragma unroll
-      for (int tt = 0; tt < NT; ++tt) {
-        uint2 pk;
-        pk.x = pack_bf16x2(O[tt][0] * inv, O[tt][1] * inv);
-        pk.y = pack_bf16x2(O[tt][2] * inv, O[tt][3] * inv);
-        *reinterpret_cast<uint2*>(op + 16 * tt + 4 * grp) = pk;
-      }
-    } else {
-      const int64_t pidx = ((int64_t)row * a.max_splits + split) * a.num_q_heads + h;
-      float* po = a.part_o + pidx * D;
-#pragma unroll
-      for (int tt = 0; tt < NT; ++tt)
-        *reinterpret_cast<float4*>(po + 16 * tt + 4 * grp) = make_float4(O[tt][0], O[tt][1], O[tt][2], O[tt][3]);
-      if (grp == 0) {
-        a.part_ml[pidx * 2] = m * c;     // log2 units
-        a.part_ml[pidx * 2 + 1] = lsum;
+    // Q^T as the B operand: lane holds d = 32kk + 8grp .. +8 of its column's (token, head)
+    bf16x8 qb[NKK];
+    {
+      const char* qp = reinterpret_cast<const char*>(a.q) +
+                       (((int64_t)(t0 + cr) * a.num_q_heads + h) * D + 8 * grp) * 2;
+  #pragma unroll
+      for (int kk = 0; kk < NKK; ++kk) {
+        const uint4 v = on ? *reinterpret_cast<const uint4*>(qp + kk * 64) : make_uint4(0, 0, 0, 0);
+        qb[kk] = __builtin_bit_cast(bf16x8, v);
       }
     }
+
+    const int64_t rs = (int64_t)a.num_kv_heads * D;            // elements per cache token row
+    const int64_t blkbytes = kBlock * rs * 2;
+    const char* kbase = reinterpret_cast<const char*>(a.k_cache) + (int64_t)g * ROWB;
+    const char* vbase = reinterpret_cast<const char*>(a.v_cache) + (int64_t)g * ROWB;
+    const int32_t* table = a.block_tables + (int64_t)b * a.max_blocks;
+    const int kb0 = k0 / kBlock;
+    const int nb = (k1 + kBlock - 1) / kBlock - kb0;        // <= 64: splits are at most 1024 keys
+    const int ids = lane < nb ? table[kb0 + lane] : 0;       // lane i: id of the split's i-th block
+
+    // K operand: key row `col`, d = 32kk + 8grp: byte offset within the block
+    const uint32_t k_lane = (uint32_t)(col * rs * 2) + 16 * grp;
+    // V copy: copy i covers rows RPI*i ..; lane -> (row RPI*i + lane / CPR, physical chunk lane % CPR)
+    uint32_t v_lane[IPB];
+  #pragma unroll
+    for (int i = 0; i < IPB; ++i) {
+      const int r = RPI * i + lane / CPR;
+      v_lane[i] = (uint32_t)(r * rs * 2) + (((lane % CPR) ^ dswz<D>(r)) * 16);
+    }
+    // transpose read: group grp, lane j = 4e + cq reads row 4grp + e, columns 16tt + 4cq .. +3,
+    // i.e. logical chunk 2tt + cq / 2, byte half cq & 1
+    uint32_t tr_off[NT];
+  #pragma unroll
+    for (int tt = 0; tt < NT; ++tt) {
+      const int r = 4 * grp + (col >> 2);
+      const int lq = 2 * tt + ((col & 3) >> 1);
+      tr_off[tt] = r * ROWB + ((lq ^ dswz<D>(r)) * 16) + (col & 1) * 8;
+    }
+
+    float m = -INFINITY, lsum = 0.f;
+    floatx4 O[NT];
+  #pragma unroll
+    for (int tt = 0; tt < NT; ++tt) O[tt] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+    auto issue = [&](int i, uint4* kr, char* vdst) {        // block kb0 + i: K to registers, V to LDS
+      const char* kb = kbase + (int64_t)__builtin_amdgcn_readlane(ids, i) * blkbytes;
+      const char* vb = vbase + (kb - kbase);
+  #pragma unroll
+      for (int kk = 0; kk < NKK; ++kk) kr[kk] = *reinterpret_cast<const uint4*>(kb + k_lane + kk * 64);
+  #pragma unroll
+      for (int j = 0; j < IPB; ++j)
+        __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(vb + v_lane[j]),
+                                         (__attribute__((address_space(3))) void*)(vdst + w * VB + 1024 * j), 16, 0, 0);
+    };
+
+    // one block.  EDGE blocks hold keys some column must not see -- before its window or after its
+    // position (the split's last blocks, and the first blocks of split 0 under a window).  The
+    // test is uniform across the wave and picks one of two compiled copies, so other blocks carry
+    // no masking at all.
+    auto consume_as = [&](auto edge_tag, int i, const uint4* kr, const char* vsrc) {
+      constexpr bool EDGE = decltype(edge_tag)::value;
+      const int s0 = (kb0 + i) * kBlock;
+      floatx4 s = floatx4{0.f, 0.f, 0.f, 0.f};
+  #pragma unroll
+      for (int kk = 0; kk < NKK; ++kk)
+        s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kr[kk]), qb[kk], s, 0, 0, 0);
+      if constexpr (EDGE) {
+  #pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const int key = s0 + 4 * grp + v;
+          if (key >= nvis || key < lo_c) s[v] = -INFINITY;
+        }
+      }
+      float bm = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
+      bm = xor16_max(bm);
+      bm = xor32_max(bm);
+      const float mn = fmaxf(m, bm);
+      const float alpha = (m == -INFINITY) ? 0.f : fast_exp2((m - mn) * c);
+      const float mc = (mn == -INFINITY) ? 0.f : mn * c;       // a column with no key yet: p = 0
+      float p[4];
+  #pragma unroll
+      for (int v = 0; v < 4; ++v) p[v] = fast_exp2(fmaf(s[v], c, -mc));
+      lsum = lsum * alpha + ((p[0] + p[1]) + (p[2] + p[3]));
+      m = mn;
+      bf16x4 pb;
+  #pragma unroll
+      for (int v = 0; v < 4; ++v) pb[v] = (__bf16)p[v];
+  #pragma unroll
+      for (int tt = 0; tt < NT; ++tt) O[tt] *= alpha;
+      const char* vw = vsrc + w * VB;
+      bf16x4 vt[NT];
+  #pragma unroll
+      for (int tt = 0; tt < NT; ++tt) vt[tt] = lds_read_tr(reinterpret_cast<const uint16_t*>(vw + tr_off[tt]));
+      if constexpr (EDGE) {
+        // rows no column may see (before the first window, past the last position) may hold poison
+        // under p = 0: zero them
+  #pragma unroll
+        for (int tt = 0; tt < NT; ++tt)
+  #pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int key = s0 + 4 * grp + e;
+            if (key >= n_keys || key < lo_min) vt[tt][e] = (__bf16)0.f;
+          }
+      }
+  #pragma unroll
+      for (int tt = 0; tt < NT; ++tt) O[tt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vt[tt], pb, O[tt], 0, 0, 0);
+    };
+    auto consume = [&](int i, const uint4* kr, const char* vsrc) {
+      const int s0 = (kb0 + i) * kBlock;
+      if (s0 < lo_max || s0 + kBlock > ctx + 1) consume_as(std::true_type{}, i, kr, vsrc);
+      else consume_as(std::false_type{}, i, kr, vsrc);
+    };
+
+    {
+      uint4 kA[NKK], kB[NKK];
+      issue(0, kA, sV0);
+      int i = 0;
+      for (; i + 2 < nb; i += 2) {                           // steady state: next block always exists
+        issue(i + 1, kB, sV1);
+        consume(i, kA, sV0);
+        issue(i + 2, kA, sV0);                               // sV0 reads above are ahead in the LDS queue
+        consume(i + 1, kB, sV1);
+      }
+      if (i + 1 < nb) {                                      // two blocks left
+        issue(i + 1, kB, sV1);
+        consume(i, kA, sV0);
+        consume(i + 1, kB, sV1);
+      } else {                                               // one block left
+        consume(i, kA, sV0);
+      }
+    }
+    lsum = xor16_sum(lsum);
+    lsum = xor32_sum(lsum);
+
+    // this wave holds the whole split for its head: write each column's row or the split's partial
+    if (on) {
+      if (n_splits == 1) {
+        const float inv = 1.f / lsum;
+        uint16_t* op = reinterpret_cast<uint16_t*>(a.out) + ((int64_t)(t0 + cr) * a.num_q_heads + h) * D;
+  #pragma unroll
+        for (int tt = 0; tt < NT; ++tt) {
+          uint2 pk;
+          pk.x = pack_bf16x2(O[tt][0] * inv, O[tt][1] * inv);
+          pk.y = pack_bf16x2(O[tt][2] * inv, O[tt][3] * inv);
+          *reinterpret_cast<uint2*>(op + 16 * tt + 4 * grp) = pk;
+        }
+      } else {
+        const int64_t pidx = partial_index(a, row, cr, split, h);
+        float* po = a.part_o + pidx * D;
+  #pragma unroll
+        for (int tt = 0; tt < NT; ++tt)
+          *reinterpret_cast<float4*>(po + 16 * tt + 4 * grp) = make_float4(O[tt][0], O[tt][1], O[tt][2], O[tt][3]);
+        if (grp == 0) {
+          a.part_ml[pidx * 2] = m * c;     // log2 units
+          a.part_ml[pidx * 2 + 1] = lsum;
+        }
+      }
+    }
   }
+
 }
 
 // ------------------------------------------------------------------------------------------
@@ -477,7 +492,7 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeArgs a) {
     if (u.n_splits == 1) {
       IO::store(a.out, ((int64_t)u.t * a.num_q_heads + h) * D + dd, o / ll);
     } else {
-      const int64_t pidx = ((int64_t)u.row * a.max_splits + u.split) * a.num_q_heads + h;
+      const int64_t pidx = partial_index(a, u.row, 0, u.split, h);
       a.part_o[pidx * D + dd] = o;
       if (dd == 0) {
         a.part_ml[pidx * 2] = mm;
@@ -488,7 +503,7 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeArgs a) {
 }
 
 // ------------------------------------------------------------------------------------------
-// Cross-split merge: one workgroup per (row, query head); splits are read in parallel.
+// Cross-split merge: one workgroup per (row, position, query head); splits are read in parallel.
 // ------------------------------------------------------------------------------------------
 template <int D, bool BF16>
 __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a) {
@@ -500,15 +515,17 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a) {
   __shared__ float4 racc[NG][CH];
   __shared__ float s_m, s_l;
 
-  const int row = blockIdx.x / a.num_q_heads;
   const int h = blockIdx.x % a.num_q_heads;
-  int b, t, n_keys;
-  if (!resolve_row(a, row, b, t, n_keys)) return;
-  const int n = (n_keys - split_origin(a, n_keys) + a.split - 1) / a.split;
+  const int r = (blockIdx.x / a.num_q_heads) % a.qmax;
+  const int row = blockIdx.x / (a.num_q_heads * a.qmax);
+  int b, t0, n_keys, ql;
+  if (!resolve_row(a, row, b, t0, n_keys, ql) || r >= ql) return;
+  const int t = t0 + r;
+  const int n = (n_keys - split_origin(a, n_keys, ql) + a.split - 1) / a.split;
   if (n <= 1) return;                                       // written directly by the split kernel
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1), w = tid >> 6;
-  const int64_t pbase = (int64_t)row * a.max_splits * a.num_q_heads + h;
+  const int64_t pbase = partial_index(a, row, r, 0, h);    // split s adds s * num_q_heads
   const float* ml = a.part_ml;
 
   float mx = -INFINITY;
@@ -590,9 +607,10 @@ hipError_t valu_dispatch(const DecodeArgs& a, dim3 g, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_decode_split(const DecodeArgs& a, int head_dim, bool bf16, hipStream_t s) {
-  const int64_t nzh = (a.group + a.heads_per_wg - 1) / a.heads_per_wg;
+  const int64_t nzh = ((int64_t)a.qmax * a.group + a.heads_per_wg - 1) / a.heads_per_wg;
   const int64_t heads = bf16 ? (a.num_kv_heads + 3) / 4 : a.num_kv_heads;   // MFMA: 4 KV heads per WG
-  const int64_t grid = heads * nzh * a.max_splits * a.num_rows;
+  // MFMA: column groups loop inside the workgroup; fp32: one workgroup per group
+  const int64_t grid = heads * (bf16 ? 1 : nzh) * a.max_splits * a.num_rows;
   if (grid <= 0 || grid > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
   const dim3 g((unsigned)grid);
   if (bf16) {
@@ -606,7 +624,7 @@ hipError_t launch_decode_split(const DecodeArgs& a, int head_dim, bool bf16, hip
 }
 
 hipError_t launch_decode_merge(const DecodeArgs& a, int head_dim, bool bf16, hipStream_t s) {
-  const int64_t grid = (int64_t)a.num_rows * a.num_q_heads;
+  const int64_t grid = (int64_t)a.num_rows * a.qmax * a.num_q_heads;
   if (grid <= 0 || grid > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
   const dim3 g((unsigned)grid), blk(256);
   if (head_dim == 128) {

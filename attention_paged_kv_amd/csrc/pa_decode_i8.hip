@@ -102,8 +102,8 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 3 : 2) void decode_i8_kernel(Dec
   const int split = ib % a.max_splits;
   const int row = ib / a.max_splits;
   if (row >= a.num_rows) return;
-  int b, t, n_keys;
-  if (!resolve_row(a, row, b, t, n_keys)) return;
+  int b, t, n_keys, ql;
+  if (!resolve_row(a, row, b, t, n_keys, ql) || ql != 1) return;   // int8 rows are single positions
   const int lo = first_visible(a, n_keys);
   const int kbeg = lo & ~(kBlock - 1);
   const int k0 = kbeg + split * a.split;
@@ -344,7 +344,7 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 3 : 2) void decode_i8_kernel(Dec
         *reinterpret_cast<uint2*>(op + 16 * tt + 4 * grp) = pk;
       }
     } else {
-      const int64_t pidx = ((int64_t)row * a.max_splits + split) * a.num_q_heads + h;
+      const int64_t pidx = partial_index(a, row, 0, split, h);
       float* po = a.part_o + pidx * D;
 #pragma unroll
       for (int tt = 0; tt < NT; ++tt)

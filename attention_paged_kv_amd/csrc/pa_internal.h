@@ -6,12 +6,14 @@
 
 namespace pa {
 
-// Query rows with q_len == 1 (and, for fp32 caches, every query row) run on the split-KV
-// decode kernels; bf16 requests with q_len >= 2 run on the MFMA tile kernel.
+// bf16 requests with q_len <= kVerifyMax (decode, and a few tokens to verify), int8 requests with
+// q_len == 1, and every query row of an fp32 batch run on the split-KV decode kernels; longer bf16
+// requests run on the MFMA tile kernel.
 constexpr int kDefaultSplitTokens = 256;   // keys per decode split (multiple of 16, at most 1024)
 constexpr int kTileRows = 128;             // query rows (position x head-in-group) per MFMA tile
 constexpr int kTileKeys = 64;              // keys per MFMA K/V tile
 constexpr int kNoWindow = 1 << 30;         // window value meaning "every earlier key"
+constexpr int kVerifyMax = 8;              // bf16 requests with q_len <= this run on the split-KV pass
 
 struct AppendArgs {
   const void* k;
@@ -33,15 +35,16 @@ struct DecodeArgs {
   const int32_t* seq_lens;
   const int32_t* qsl;
   void* out;
-  float* part_o;          // [rows][max_splits][Hq][d]   unnormalised partial outputs
-  float* part_ml;         // [rows][max_splits][Hq][2]   (running max in log2 units, sum)
+  float* part_o;          // [rows][qmax][max_splits][Hq][d]   unnormalised partial outputs
+  float* part_ml;         // [rows][qmax][max_splits][Hq][2]   (running max in log2 units, sum)
   int num_seqs;
-  int num_rows;           // row slots: requests (bf16) or tokens (fp32)
-  int per_token;          // 1: row slot = token index; 0: row slot = request with q_len == 1
+  int num_rows;           // row slots: requests (bf16, int8) or tokens (fp32)
+  int per_token;          // 1: row slot = token index; 0: row slot = request with q_len <= qmax
+  int qmax;               // positions a request row may carry (1 for per-token rows)
   int num_q_heads;
   int num_kv_heads;
   int group;              // Hq / Hkv
-  int heads_per_wg;       // query heads of one group handled by one workgroup
+  int heads_per_wg;       // columns per workgroup: (position, query head) pairs of one KV head
   int max_blocks;
   int split;              // keys per split
   int max_splits;
@@ -90,8 +93,8 @@ hipError_t launch_append(const AppendArgs& a, hipStream_t s);
 hipError_t launch_decode_split(const DecodeArgs& a, int head_dim, bool bf16, hipStream_t s);
 hipError_t launch_decode_split_i8(const DecodeArgs& a, int head_dim, hipStream_t s);
 hipError_t launch_decode_merge(const DecodeArgs& a, int head_dim, bool bf16, hipStream_t s);
-hipError_t launch_plan_tiles(const int32_t* qsl, int num_seqs, int pos_per_tile, int4* tiles, int* num_tiles,
-                             hipStream_t s);
+hipError_t launch_plan_tiles(const int32_t* qsl, int num_seqs, int pos_per_tile, int min_q, int4* tiles,
+                             int* num_tiles, hipStream_t s);
 hipError_t launch_prefill_tile(const TileArgs& a, int head_dim, hipStream_t s);
 hipError_t launch_check(const CheckArgs& a, hipStream_t s);
 

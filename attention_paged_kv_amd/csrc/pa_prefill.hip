@@ -305,10 +305,11 @@ __global__ __launch_bounds__(256, 2) void prefill_tile_kernel(TileArgs a) {
   }
 }
 
-// One workgroup: per request, ceil(q_len / pos_per_tile) tiles for every request with q_len >= 2,
-// written with the last (longest) row block of each request first.
+// One workgroup: per request, ceil(q_len / pos_per_tile) tiles for every request with
+// q_len >= min_q (shorter ones are rows of the split-KV decode pass), written with the last
+// (longest) row block of each request first.
 __global__ __launch_bounds__(256) void plan_tiles_kernel(const int32_t* qsl, int num_seqs, int pos_per_tile,
-                                                         int4* tiles, int* num_tiles) {
+                                                         int min_q, int4* tiles, int* num_tiles) {
   __shared__ int scan[256];
   __shared__ int base;
   const int tid = threadIdx.x;
@@ -319,7 +320,7 @@ __global__ __launch_bounds__(256) void plan_tiles_kernel(const int32_t* qsl, int
     int ql = 0, cnt = 0;
     if (b < num_seqs) {
       ql = qsl[b + 1] - qsl[b];
-      cnt = ql >= 2 ? (ql + pos_per_tile - 1) / pos_per_tile : 0;
+      cnt = ql >= min_q ? (ql + pos_per_tile - 1) / pos_per_tile : 0;
     }
     scan[tid] = cnt;
     __syncthreads();
@@ -341,9 +342,9 @@ __global__ __launch_bounds__(256) void plan_tiles_kernel(const int32_t* qsl, int
   if (tid == 0) *num_tiles = base;
 }
 
-hipError_t launch_plan_tiles(const int32_t* qsl, int num_seqs, int pos_per_tile, int4* tiles, int* num_tiles,
-                             hipStream_t s) {
-  plan_tiles_kernel<<<dim3(1), dim3(256), 0, s>>>(qsl, num_seqs, pos_per_tile, tiles, num_tiles);
+hipError_t launch_plan_tiles(const int32_t* qsl, int num_seqs, int pos_per_tile, int min_q, int4* tiles,
+                             int* num_tiles, hipStream_t s) {
+  plan_tiles_kernel<<<dim3(1), dim3(256), 0, s>>>(qsl, num_seqs, pos_per_tile, min_q, tiles, num_tiles);
   return hipGetLastError();
 }
 

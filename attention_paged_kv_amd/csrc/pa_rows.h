@@ -6,9 +6,10 @@
 
 namespace pa {
 
-// Resolve a row slot to (request, token, causal keys).  Returns false if the slot is not a
-// row of this pass (bf16 and int8 requests with q_len != 1 go to the tile kernel).
-__device__ __forceinline__ bool resolve_row(const DecodeArgs& a, int row, int& b, int& t, int& n_keys) {
+// Resolve a row slot to (request, first token, causal keys of its last position, positions).
+// Per-token rows (fp32) are one position each.  Request rows carry q_len <= a.qmax positions
+// (decode, or a few tokens to verify); others are not rows of this pass (the tile kernel's).
+__device__ __forceinline__ bool resolve_row(const DecodeArgs& a, int row, int& b, int& t, int& n_keys, int& ql) {
   if (a.per_token) {
     t = row;
     int lo = 0, hi = a.num_seqs;                       // qsl[lo] <= t < qsl[hi]
@@ -17,22 +18,30 @@ __device__ __forceinline__ bool resolve_row(const DecodeArgs& a, int row, int& b
       if (a.qsl[mid] <= t) lo = mid; else hi = mid;
     }
     b = lo;
-  } else {
-    b = row;
-    if (a.qsl[b + 1] - a.qsl[b] != 1) return false;
-    t = a.qsl[b];
+    const int q0 = a.qsl[b];
+    n_keys = a.seq_lens[b] - (a.qsl[b + 1] - q0) + (t - q0) + 1;   // keys 0 .. position of this token
+    ql = 1;
+    return true;
   }
-  const int q0 = a.qsl[b];
-  const int ql = a.qsl[b + 1] - q0;
-  n_keys = a.seq_lens[b] - ql + (t - q0) + 1;          // keys 0 .. position of this row
+  b = row;
+  ql = a.qsl[b + 1] - a.qsl[b];
+  if (ql < 1 || ql > a.qmax) return false;
+  t = a.qsl[b];
+  n_keys = a.seq_lens[b];                              // keys of the last position
   return true;
 }
 
-// First key a row with `n_keys` causal keys sees (a sliding window drops the older ones), and the
-// block-aligned key where its splits begin.  Every kernel of the pass derives its ranges from these.
-__device__ __forceinline__ int first_visible(const DecodeArgs& a, int n_keys) { return max(0, n_keys - a.window); }
-__device__ __forceinline__ int split_origin(const DecodeArgs& a, int n_keys) {
-  return first_visible(a, n_keys) & ~(kBlock - 1);
+// First key a position with `n` causal keys sees (a sliding window drops the older ones), and the
+// block-aligned key where a row's splits begin: that of its first position, whose window starts
+// earliest.  Every kernel of the pass derives its ranges from these.
+__device__ __forceinline__ int first_visible(const DecodeArgs& a, int n) { return max(0, n - a.window); }
+__device__ __forceinline__ int split_origin(const DecodeArgs& a, int n_keys, int ql) {
+  return first_visible(a, n_keys - ql + 1) & ~(kBlock - 1);
+}
+
+// Index of the split partial of (row, position r, split, query head h).
+__device__ __forceinline__ int64_t partial_index(const DecodeArgs& a, int row, int r, int split, int h) {
+  return (((int64_t)row * a.qmax + r) * a.max_splits + split) * a.num_q_heads + h;
 }
 
 }  // namespace pa

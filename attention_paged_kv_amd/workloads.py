@@ -390,6 +390,35 @@ def config5(values: bool = True, seed: int = 5, cache: str = "") -> Workload:
 CONFIGS = {"c1": config1, "c2": config2, "c3": config3, "c4": config4, "c5": config5}
 
 
+def verify_variant(w: Workload, k: int) -> Workload:
+    """A decode workload turned into a verification step: each request's last k tokens are the
+    step's new tokens (q_len = k, same seq_len), the rest stays cached.  Same seed and draw order
+    as the decode workload (lengths and placements identical)."""
+    st = w.steps[0]
+    assert len(w.steps) == 1 and np.all(st.q_lens == 1)
+    B = st.num_seqs
+    q_lens = np.minimum(k, st.seq_lens.astype(np.int64))
+    v = make_batch(w.seed, st.seq_lens, q_lens, w.num_q_heads, w.num_kv_heads, w.head_dim, w.dtype,
+                   num_blocks=w.num_blocks, max_blocks=st.block_tables.shape[1], rng=_replay_rng(w),
+                   name=f"{w.name}-v{k}", description=w.description + f", verifying {k} tokens per request",
+                   cache=w.kv_dtype)
+    assert v.steps[0].num_seqs == B
+    return v
+
+
+def _replay_rng(w: Workload) -> np.random.Generator:
+    """The generator state a config function hands to make_batch (it draws the lengths first)."""
+    rng = np.random.default_rng(w.seed)
+    name = w.name.split("-")[0]
+    if name == "c2_decode_b32":
+        rng.integers(512, 4096, size=32, endpoint=True)
+    elif name == "c5_skewed_decode":
+        rng.uniform(math.log(3277), math.log(32768), size=16)
+    else:
+        raise ValueError(f"no verify variant for {w.name}")
+    return rng
+
+
 def chunked_steps(w: Workload, chunk_sizes: Sequence[int]) -> Workload:
     """Re-express a single-request prefill workload (q_len == seq_len) as successive chunks.
 

@@ -6,14 +6,15 @@ then causal attention of every query row (decode splits + merge, and prefill/chu
 the batch has them).  Inputs are seeded synthetic tensors already resident in HBM.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--config c2|c3|c4|c5|c1] [--window N]
-                    [--kv bf16|i8] [--no-cpu-baseline]
+                    [--kv bf16|i8] [--verify K] [--no-cpu-baseline]
 
 Prints one JSON line.  The default workload is the 32-request bf16 decode batch (32/32 heads,
 d=128, contexts U[512, 4096], 16384-block pool); its metric is KV-read GB/s.  --window N runs the
 same workload with a sliding window of N keys per query row; work counts then cover only the keys
 and pairs inside the windows.  --kv i8 keeps the workload's shapes and lengths over an 8-bit cache
 (int8 codes, fp32 scale per KV head and channel; decode workloads only): KV bytes count 1 byte per
-element.
+element.  --verify K turns a decode workload into a verification step: each request appends and
+attends its last K tokens (same lengths and tables), still one read of every visible key.
 """
 import argparse
 import json
@@ -122,6 +123,7 @@ def main():
     ap.add_argument("--config", default="c2", choices=["c1", "c2", "c3", "c4", "c5"])
     ap.add_argument("--window", type=int, default=0, help="sliding window in keys (0: none)")
     ap.add_argument("--kv", default="bf16", choices=["bf16", "i8"], help="cache element type")
+    ap.add_argument("--verify", type=int, default=0, help="tokens per request to verify (decode workloads)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-ref-mib", type=int, default=0,
                     help="instead of the hot path, time a plain device copy of this many MiB "
@@ -170,6 +172,11 @@ def main():
         sys.exit(2)
     t0 = time.time()
     w = W.CONFIGS[args.config](cache="i8") if args.kv == "i8" else W.CONFIGS[args.config]()
+    if args.verify > 1:
+        if args.config not in ("c2", "c5") or args.kv == "i8":
+            print("--verify serves the bf16 decode workloads (c2, c5)", file=sys.stderr)
+            sys.exit(2)
+        w = W.verify_variant(w, args.verify)
     log(f"generated {w.name} in {time.time() - t0:.1f}s")
     tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
 

@@ -63,6 +63,9 @@ SMALL = [
     ([400, 129], [129, 129], 16, 1, 64, "bf16"),
     ([260, 90], [3, 90], 2, 2, 64, "bf16"),
     ([1030, 1030], [1, 7], 32, 32, 128, "bf16"),
+    # bf16 head_dim 64 decode rows, one KV head: staged V rows are 128 bytes (8 chunks) wide
+    ([15, 16, 17, 31, 32, 33, 700], [1, 1, 1, 1, 1, 1, 1], 8, 1, 64, "bf16"),
+    ([300, 2000], [1, 1], 4, 4, 64, "bf16"),
 ]
 
 
