@@ -6,6 +6,7 @@
 #include <atomic>
 #include <cmath>
 #include <cstdarg>
+#include <cstdint>
 #include <cstdio>
 #include <cstdlib>
 #include <mutex>
@@ -128,6 +129,9 @@ struct Plan {
   size_t off_o = 0, off_ml = 0, off_tiles = 0, off_ntiles = 0, total = 0;
 };
 
+// The kernels move data in 16-byte vectors.
+bool misaligned(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) != 0; }
+
 int validate_desc(const pa_cache_desc* c) {
   if (!c) return fail(PA_ERR_INVALID_ARG, "cache descriptor is NULL");
   if (c->block_size != PA_BLOCK_SIZE) return fail(PA_ERR_INVALID_ARG, "block_size must be 16 (got %d)", c->block_size);
@@ -139,6 +143,8 @@ int validate_desc(const pa_cache_desc* c) {
     return fail(PA_ERR_INVALID_ARG, "an int8 cache needs k_scale and v_scale");
   if (c->dtype != PA_DTYPE_I8 && (c->k_scale || c->v_scale))
     return fail(PA_ERR_INVALID_ARG, "k_scale / v_scale are for int8 caches only");
+  if (misaligned(c->k_scale) || misaligned(c->v_scale))
+    return fail(PA_ERR_INVALID_ARG, "k_scale / v_scale must be 16-byte aligned");
   if (c->head_dim != 64 && c->head_dim != 128) return fail(PA_ERR_UNSUPPORTED, "head_dim must be 64 or 128 (got %d)", c->head_dim);
   return PA_OK;
 }
@@ -179,8 +185,6 @@ int make_plan(int32_t B, int32_t T, int32_t MB, int32_t Hq, const pa_cache_desc*
     p.run_tiles = longest > p.qmax;              // some request may have q_len > qmax
     p.pos_per_tile = pa::kTileRows / p.group;
     p.num_slots = (T + p.pos_per_tile - 1) / p.pos_per_tile + B;
-    if (p.i8 && p.run_tiles)
-      return fail(PA_ERR_UNSUPPORTED, "int8 caches serve q_len == 1 rows only (num_q_tokens %d > num_seqs %d)", T, B);
   } else {
     p.per_token = 1;
     p.rows = T;
@@ -285,6 +289,8 @@ int pa_append_kv(const void* k, const void* v, const int32_t* slot_mapping, int3
   if (num_tokens == 0) return PA_OK;
   if (!k || !v || !slot_mapping || !k_cache || !v_cache) return fail(PA_ERR_INVALID_ARG, "null pointer argument");
   if (k_cache == v_cache) return fail(PA_ERR_INVALID_ARG, "k_cache and v_cache must differ");
+  if (misaligned(k) || misaligned(v) || misaligned(k_cache) || misaligned(v_cache))
+    return fail(PA_ERR_INVALID_ARG, "k, v and the caches must be 16-byte aligned");
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const int64_t esz = cache->dtype == PA_DTYPE_F32 ? 4 : 2;         // input rows (bf16 for int8 caches)
   if (check_on()) {
@@ -331,6 +337,8 @@ int pa_attention_ex(const void* q, int32_t num_q_tokens, int32_t num_q_heads, co
   if (!q || !k_cache || !v_cache || !block_tables || !seq_lens || !query_start_loc || !out)
     return fail(PA_ERR_INVALID_ARG, "null pointer argument");
   if (out == q || out == k_cache || out == v_cache) return fail(PA_ERR_INVALID_ARG, "out must not alias inputs");
+  if (misaligned(q) || misaligned(k_cache) || misaligned(v_cache) || misaligned(out) || misaligned(workspace))
+    return fail(PA_ERR_INVALID_ARG, "q, the caches, out and the workspace must be 16-byte aligned");
   // the kernels track the running max of raw scores and apply the scale afterwards, which needs
   // scale > 0
   if (!std::isfinite(scale) || !(scale > 0.f))
@@ -438,7 +446,9 @@ int pa_attention_ex(const void* q, int32_t num_q_tokens, int32_t num_q_heads, co
     t.max_blocks = max_blocks_per_seq;
     t.window = window;
     t.scale_log2 = scale_log2;
-    e = timed("prefill_tile", s, [&] { return pa::launch_prefill_tile(t, p.head_dim, s); });
+    t.k_scale = cache->k_scale;
+    t.v_scale = cache->v_scale;
+    e = timed("prefill_tile", s, [&] { return pa::launch_prefill_tile(t, p.head_dim, p.i8, s); });
     if (e != hipSuccess) return device_fail(e, "prefill tile launch");
   }
   return PA_OK;

@@ -8,8 +8,7 @@
 //
 // 8-bit caches (P2 §4.3, §5.4: INT8 KV with per-channel calibration): the append quantises
 // instead of copying.  Element c of a token row (c = head * d + channel) becomes
-// clamp(rne(x / s_c), -127, 127) with the division rounded to fp32 and NaN mapped to 0; a lane
-// handles 8 elements (16 bytes of bf16 in, 8 bytes of codes out).
+// clamp(rne(x / s_c), -127, 127) with the division rounded to fp32 and NaN mapped to 0.
 #include "pa_common.h"
 #include "pa_internal.h"
 
@@ -49,8 +48,10 @@ __device__ __forceinline__ uint2 quantize8(const uint4& x, const float4& s0, con
   return o;
 }
 
+// One lane: 16 elements (two 16-byte loads per tensor in, one 16-byte store of codes out).  All
+// loads are taken into registers before either store, so the stores cannot serialise them.
 __global__ __launch_bounds__(256) void append_i8_kernel(AppendArgs a) {
-  const int64_t per_row = a.row_bytes >> 4;                 // 8-element pieces per token row
+  const int64_t per_row = a.row_bytes >> 5;                 // 16-element pieces per token row
   const int64_t total = a.num_tokens * per_row;
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
   for (int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; c < total; c += stride) {
@@ -58,17 +59,23 @@ __global__ __launch_bounds__(256) void append_i8_kernel(AppendArgs a) {
     const int64_t piece = c - tok * per_row;
     const int32_t slot = a.slot_mapping[tok];
     if (slot < 0) continue;
-    const int64_t src = tok * per_row + piece;
+    const uint4* kin = reinterpret_cast<const uint4*>(a.k) + 2 * c;
+    const uint4* vin = reinterpret_cast<const uint4*>(a.v) + 2 * c;
+    const float4* ksp = reinterpret_cast<const float4*>(a.k_scale) + 4 * piece;
+    const float4* vsp = reinterpret_cast<const float4*>(a.v_scale) + 4 * piece;
+    const uint4 k0 = kin[0], k1 = kin[1], v0 = vin[0], v1 = vin[1];
+    const float4 ks0 = ksp[0], ks1 = ksp[1], ks2 = ksp[2], ks3 = ksp[3];
+    const float4 vs0 = vsp[0], vs1 = vsp[1], vs2 = vsp[2], vs3 = vsp[3];
+    const uint2 ka = quantize8(k0, ks0, ks1), kb = quantize8(k1, ks2, ks3);
+    const uint2 va = quantize8(v0, vs0, vs1), vb = quantize8(v1, vs2, vs3);
     const int64_t dst = (int64_t)slot * per_row + piece;
-    const float4* ks = reinterpret_cast<const float4*>(a.k_scale) + 2 * piece;
-    const float4* vs = reinterpret_cast<const float4*>(a.v_scale) + 2 * piece;
-    reinterpret_cast<uint2*>(a.k_cache)[dst] = quantize8(reinterpret_cast<const uint4*>(a.k)[src], ks[0], ks[1]);
-    reinterpret_cast<uint2*>(a.v_cache)[dst] = quantize8(reinterpret_cast<const uint4*>(a.v)[src], vs[0], vs[1]);
+    reinterpret_cast<uint4*>(a.k_cache)[dst] = make_uint4(ka.x, ka.y, kb.x, kb.y);
+    reinterpret_cast<uint4*>(a.v_cache)[dst] = make_uint4(va.x, va.y, vb.x, vb.y);
   }
 }
 
 hipError_t launch_append(const AppendArgs& a, hipStream_t s) {
-  const int64_t total = a.num_tokens * (a.row_bytes >> 4);
+  const int64_t total = a.num_tokens * (a.row_bytes >> (a.k_scale ? 5 : 4));
   int64_t blocks = (total + 255) / 256;
   if (blocks > 65536) blocks = 65536;
   if (blocks < 1) blocks = 1;

@@ -72,6 +72,8 @@ struct TileArgs {
   int max_blocks;
   int window;             // as in DecodeArgs
   float scale_log2;
+  const float* k_scale;   // int8 caches: [Hkv][d]
+  const float* v_scale;
 };
 
 struct CheckArgs {
@@ -95,7 +97,7 @@ hipError_t launch_decode_split_i8(const DecodeArgs& a, int head_dim, hipStream_t
 hipError_t launch_decode_merge(const DecodeArgs& a, int head_dim, bool bf16, hipStream_t s);
 hipError_t launch_plan_tiles(const int32_t* qsl, int num_seqs, int pos_per_tile, int min_q, int4* tiles,
                              int* num_tiles, hipStream_t s);
-hipError_t launch_prefill_tile(const TileArgs& a, int head_dim, hipStream_t s);
+hipError_t launch_prefill_tile(const TileArgs& a, int head_dim, bool kv8, hipStream_t s);
 hipError_t launch_check(const CheckArgs& a, hipStream_t s);
 
 }  // namespace pa

@@ -29,6 +29,12 @@
 // request's first window are never read (their blocks may be gone), a valid row stands in.  The running max is only moved (and O rescaled)
 // when some row's max grows by more than 2^8; between moves, probabilities may exceed 1 by at most
 // 2^8.
+//
+// 8-bit caches (P2 §4.3, §5.4: int8 codes with a scale per KV head and channel): the cache blocks
+// are copied to int8 staging buffers the same way, then the workgroup converts each tile once into
+// the bf16 tile layout above (exact: |code| <= 127), so the tile math is unchanged; the K scale is
+// folded into the query (q * k_scale rounded to bf16) and the V scale multiplies O at the end.  One
+// more barrier per tile separates the conversion from the math.
 #include "pa_common.h"
 #include "pa_internal.h"
 
@@ -43,9 +49,10 @@ __device__ __forceinline__ int swz(int r) {
 }
 }  // namespace
 
-template <int D>
+template <int D, bool KV8>
 __global__ __launch_bounds__(256, 2) void prefill_tile_kernel(TileArgs a) {
-  constexpr int ROWB = D * 2;               // bytes per K/V row
+  constexpr int ESZ = KV8 ? 1 : 2;          // bytes per cache element
+  constexpr int ROWB = D * 2;               // bytes per bf16 K/V row in LDS
   constexpr int CPR = D / 8;                // 16-byte chunks per row
   constexpr int RPI = 1024 / ROWB;          // rows per wave-wide 1 KiB load
   constexpr int IPB = kBlock / RPI;         // loads per 16-key block (per tensor)
@@ -53,12 +60,6 @@ __global__ __launch_bounds__(256, 2) void prefill_tile_kernel(TileArgs a) {
   constexpr int NKK = D / 16;               // MFMA k-steps over d
   constexpr int NDT = D / 32;               // 32-wide d tiles of O^T
   static_assert(kTileKeys == 4 * kBlock, "one cache block per wave and tile");
-  // one LDS variable per buffer and tensor: the compiler then knows that loads landing in one
-  // buffer never alias reads of the other, and does not wait for them before those reads
-  __shared__ __align__(16) char sK0[TILEB];
-  __shared__ __align__(16) char sV0[TILEB];
-  __shared__ __align__(16) char sK1[TILEB];
-  __shared__ __align__(16) char sV1[TILEB];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -104,7 +105,17 @@ __global__ __launch_bounds__(256, 2) void prefill_tile_kernel(TileArgs a) {
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk) {
       const uint4 v = row_ok ? *reinterpret_cast<const uint4*>(qp + kk * 32) : make_uint4(0, 0, 0, 0);
-      qreg[kk] = __builtin_bit_cast(bf16x8, v);
+      if constexpr (KV8) {                       // q * k_scale of channels 16kk + 8half .. +7
+        const float* ks = a.k_scale + (int64_t)g * D + 16 * kk + 8 * half;
+        const float4 s0 = *reinterpret_cast<const float4*>(ks);
+        const float4 s1 = *reinterpret_cast<const float4*>(ks + 4);
+        const float f[8] = {bf16_lo(v.x) * s0.x, bf16_hi(v.x) * s0.y, bf16_lo(v.y) * s0.z, bf16_hi(v.y) * s0.w,
+                            bf16_lo(v.z) * s1.x, bf16_hi(v.z) * s1.y, bf16_lo(v.w) * s1.z, bf16_hi(v.w) * s1.w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) qreg[kk][e] = (__bf16)f[e];
+      } else {
+        qreg[kk] = __builtin_bit_cast(bf16x8, v);
+      }
     }
   }
 
@@ -117,52 +128,14 @@ __global__ __launch_bounds__(256, 2) void prefill_tile_kernel(TileArgs a) {
   const int low_edge = last_pos - a.window + 1;      // tiles starting below this need the window mask
   const float c = a.scale_log2;
   const int64_t rs = (int64_t)a.num_kv_heads * D;    // elements per cache token row
-  const char* kbase = reinterpret_cast<const char*>(a.k_cache) + (int64_t)g * D * 2;
-  const char* vbase = reinterpret_cast<const char*>(a.v_cache) + (int64_t)g * D * 2;
+  const char* kbase = reinterpret_cast<const char*>(a.k_cache) + (int64_t)g * D * ESZ;
+  const char* vbase = reinterpret_cast<const char*>(a.v_cache) + (int64_t)g * D * ESZ;
   const int32_t* table = a.block_tables + (int64_t)b * a.max_blocks;
 
-  // ---- staging: wave w loads key rows 16w..16w+15 of the tile (one cache block) ----
-  // load i of the block covers rows RPI*i .. RPI*i + RPI - 1; lane -> (row lane / CPR, physical
-  // chunk lane % CPR), which holds logical chunk (lane % CPR) ^ swz(row).
-  // wave w visits blocks 4kt + w; those entirely below the length are taken from a window
+  // blocks of the request's wave: wave w visits blocks 4kt + w; those entirely below the length
+  // are taken from a window of table entries
   const int n_full = (sl / kBlock - w + 3) / 4;   // count of kt with (4kt + w + 1) * 16 <= sl
   BlockWindow win;
-  uint32_t lane_off[IPB];                         // byte offset within the block, per load
-#pragma unroll
-  for (int i = 0; i < IPB; ++i) {
-    const int rr = RPI * i + lane / CPR;          // row within the block (and within the wave's 16)
-    const int q = (lane % CPR) ^ swz<D>(16 * w + rr);
-    lane_off[i] = (uint32_t)(rr * rs * 2) + q * 16;
-  }
-  auto stage = [&](int kt, char* kdst, char* vdst) {
-    char* kl = kdst + 16 * w * ROWB;
-    char* vl = vdst + 16 * w * ROWB;
-    const int blk = 4 * kt + w;
-    if ((blk + 1) * kBlock <= sl && blk * kBlock >= lo_req) {   // whole block valid: one table entry
-      const int64_t boff = (int64_t)win.get(table, w, 4, n_full, kt) * (kBlock * rs * 2);
-      const char* kb = kbase + boff;               // uniform block base; lanes add 32-bit offsets
-      const char* vb = vbase + boff;
-#pragma unroll
-      for (int i = 0; i < IPB; ++i) {
-        __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(kb + lane_off[i]),
-                                         (__attribute__((address_space(3))) void*)(kl + 1024 * i), 16, 0, 0);
-        __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(vb + lane_off[i]),
-                                         (__attribute__((address_space(3))) void*)(vl + 1024 * i), 16, 0, 0);
-      }
-    } else {                                      // edge block: clamp rows into [lo_req, sl)
-#pragma unroll
-      for (int i = 0; i < IPB; ++i) {
-        const int rr = RPI * i + lane / CPR;
-        const int j = min(max(blk * kBlock + rr, lo_req), sl - 1);
-        const int q = (lane % CPR) ^ swz<D>(16 * w + rr);
-        const int64_t off = (((int64_t)table[j >> 4] * kBlock + (j & 15)) * rs) * 2 + q * 16;
-        __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(kbase + off),
-                                         (__attribute__((address_space(3))) void*)(kl + 1024 * i), 16, 0, 0);
-        __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(vbase + off),
-                                         (__attribute__((address_space(3))) void*)(vl + 1024 * i), 16, 0, 0);
-      }
-    }
-  };
 
   float m_run = -INFINITY, l_run = 0.f;
   floatx16 O[NDT];
@@ -270,21 +243,157 @@ __global__ __launch_bounds__(256, 2) void prefill_tile_kernel(TileArgs a) {
     }
   };
 
-  stage(kt_lo, sK0, sV0);
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();
+  if constexpr (!KV8) {
+    // one LDS variable per buffer and tensor: the compiler then knows that loads landing in one
+    // buffer never alias reads of the other, and does not wait for them before those reads
+    __shared__ __align__(16) char sK0[TILEB];
+    __shared__ __align__(16) char sV0[TILEB];
+    __shared__ __align__(16) char sK1[TILEB];
+    __shared__ __align__(16) char sV1[TILEB];
+    // ---- staging: wave w loads key rows 16w..16w+15 of the tile (one cache block) ----
+    // load i of the block covers rows RPI*i .. RPI*i + RPI - 1; lane -> (row lane / CPR, physical
+    // chunk lane % CPR), which holds logical chunk (lane % CPR) ^ swz(row).
+    uint32_t lane_off[IPB];                         // byte offset within the block, per load
+#pragma unroll
+    for (int i = 0; i < IPB; ++i) {
+      const int rr = RPI * i + lane / CPR;          // row within the block (and within the wave's 16)
+      const int q = (lane % CPR) ^ swz<D>(16 * w + rr);
+      lane_off[i] = (uint32_t)(rr * rs * 2) + q * 16;
+    }
+    auto stage = [&](int kt, char* kdst, char* vdst) {
+      char* kl = kdst + 16 * w * ROWB;
+      char* vl = vdst + 16 * w * ROWB;
+      const int blk = 4 * kt + w;
+      if ((blk + 1) * kBlock <= sl && blk * kBlock >= lo_req) {   // whole block valid: one table entry
+        const int64_t boff = (int64_t)win.get(table, w, 4, n_full, kt) * (kBlock * rs * 2);
+        const char* kb = kbase + boff;               // uniform block base; lanes add 32-bit offsets
+        const char* vb = vbase + boff;
+#pragma unroll
+        for (int i = 0; i < IPB; ++i) {
+          __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(kb + lane_off[i]),
+                                           (__attribute__((address_space(3))) void*)(kl + 1024 * i), 16, 0, 0);
+          __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(vb + lane_off[i]),
+                                           (__attribute__((address_space(3))) void*)(vl + 1024 * i), 16, 0, 0);
+        }
+      } else {                                      // edge block: clamp rows into [lo_req, sl)
+#pragma unroll
+        for (int i = 0; i < IPB; ++i) {
+          const int rr = RPI * i + lane / CPR;
+          const int j = min(max(blk * kBlock + rr, lo_req), sl - 1);
+          const int q = (lane % CPR) ^ swz<D>(16 * w + rr);
+          const int64_t off = (((int64_t)table[j >> 4] * kBlock + (j & 15)) * rs) * 2 + q * 16;
+          __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(kbase + off),
+                                           (__attribute__((address_space(3))) void*)(kl + 1024 * i), 16, 0, 0);
+          __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(vbase + off),
+                                           (__attribute__((address_space(3))) void*)(vl + 1024 * i), 16, 0, 0);
+        }
+      }
+    };
 
-  // two tiles per iteration so that each buffer is a fixed LDS variable
-  for (int kt = kt_lo; kt < n_kt; kt += 2) {
-    if (kt + 1 < n_kt) stage(kt + 1, sK1, sV1);     // in flight during this tile's math
-    tile_math(kt, sK0, sV0);
+    stage(kt_lo, sK0, sV0);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    if (kt + 1 >= n_kt) break;
-    if (kt + 2 < n_kt) stage(kt + 2, sK0, sV0);
-    tile_math(kt + 1, sK1, sV1);
+
+    // two tiles per iteration so that each buffer is a fixed LDS variable
+    for (int kt = kt_lo; kt < n_kt; kt += 2) {
+      if (kt + 1 < n_kt) stage(kt + 1, sK1, sV1);     // in flight during this tile's math
+      tile_math(kt, sK0, sV0);
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
+      if (kt + 1 >= n_kt) break;
+      if (kt + 2 < n_kt) stage(kt + 2, sK0, sV0);
+      tile_math(kt + 1, sK1, sV1);
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
+    }
+
+
+  } else {
+    constexpr int CPR8 = D / 16;                  // 16-byte chunks per int8 row
+    constexpr int RPI8 = 1024 / D;                // int8 rows per wave-wide 1 KiB load
+    constexpr int IPB8 = kBlock / RPI8;
+    constexpr int TILE8 = kTileKeys * D;          // bytes per staged int8 tile
+    __shared__ __align__(16) char sK[TILEB];       // bf16 tiles the math reads
+    __shared__ __align__(16) char sV[TILEB];
+    __shared__ __align__(16) char sK8a[TILE8];     // int8 staging, double buffered
+    __shared__ __align__(16) char sV8a[TILE8];
+    __shared__ __align__(16) char sK8b[TILE8];
+    __shared__ __align__(16) char sV8b[TILE8];
+    // staging: plain row-major int8 rows; load i of wave w's block covers rows RPI8*i + lane/CPR8
+    uint32_t lane_off8[IPB8];
+#pragma unroll
+    for (int i = 0; i < IPB8; ++i) {
+      const int rr = RPI8 * i + lane / CPR8;
+      lane_off8[i] = (uint32_t)(rr * rs) + (lane % CPR8) * 16;
+    }
+    auto stage8 = [&](int kt, char* kdst, char* vdst) {
+      char* kl = kdst + 16 * w * D;
+      char* vl = vdst + 16 * w * D;
+      const int blk = 4 * kt + w;
+      if ((blk + 1) * kBlock <= sl && blk * kBlock >= lo_req) {
+        const int64_t boff = (int64_t)win.get(table, w, 4, n_full, kt) * (kBlock * rs);
+#pragma unroll
+        for (int i = 0; i < IPB8; ++i) {
+          __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(kbase + boff + lane_off8[i]),
+                                           (__attribute__((address_space(3))) void*)(kl + 1024 * i), 16, 0, 0);
+          __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(vbase + boff + lane_off8[i]),
+                                           (__attribute__((address_space(3))) void*)(vl + 1024 * i), 16, 0, 0);
+        }
+      } else {                                    // edge block: clamp rows into [lo_req, sl)
+#pragma unroll
+        for (int i = 0; i < IPB8; ++i) {
+          const int rr = RPI8 * i + lane / CPR8;
+          const int j = min(max(blk * kBlock + rr, lo_req), sl - 1);
+          const int64_t off = ((int64_t)table[j >> 4] * kBlock + (j & 15)) * rs + (lane % CPR8) * 16;
+          __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(kbase + off),
+                                           (__attribute__((address_space(3))) void*)(kl + 1024 * i), 16, 0, 0);
+          __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(vbase + off),
+                                           (__attribute__((address_space(3))) void*)(vl + 1024 * i), 16, 0, 0);
+        }
+      }
+    };
+    // conversion: thread -> (row tid / 4, quarter tid % 4 of its channels); 16 codes -> two bf16 chunks
+    const int crow = tid >> 2, cq = tid & 3;
+    auto convert = [&](const char* k8, const char* v8) {
+#pragma unroll
+      for (int u = 0; u < D / 64; ++u) {
+        const int c16 = (D / 64) * cq + u;                    // 16-code piece of the row
+        const uint4 xk = *reinterpret_cast<const uint4*>(k8 + crow * D + 16 * c16);
+        const uint4 xv = *reinterpret_cast<const uint4*>(v8 + crow * D + 16 * c16);
+        const uint32_t wk[4] = {xk.x, xk.y, xk.z, xk.w}, wv[4] = {xv.x, xv.y, xv.z, xv.w};
+#pragma unroll
+        for (int hq = 0; hq < 2; ++hq) {                      // logical bf16 chunk 2 * c16 + hq
+          bf16x8 ok, ov;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            ok[e] = (__bf16)(float)(signed char)(wk[2 * hq + e / 4] >> (8 * (e & 3)));
+            ov[e] = (__bf16)(float)(signed char)(wv[2 * hq + e / 4] >> (8 * (e & 3)));
+          }
+          const int off = crow * ROWB + (((2 * c16 + hq) ^ swz<D>(crow)) * 16);
+          *reinterpret_cast<bf16x8*>(sK + off) = ok;
+          *reinterpret_cast<bf16x8*>(sV + off) = ov;
+        }
+      }
+    };
+
+    stage8(kt_lo, sK8a, sV8a);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
+    for (int kt = kt_lo; kt < n_kt; kt += 2) {
+      convert(sK8a, sV8a);
+      __syncthreads();
+      if (kt + 1 < n_kt) stage8(kt + 1, sK8b, sV8b);
+      tile_math(kt, sK, sV);
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
+      if (kt + 1 >= n_kt) break;
+      convert(sK8b, sV8b);
+      __syncthreads();
+      if (kt + 2 < n_kt) stage8(kt + 2, sK8a, sV8a);
+      tile_math(kt + 1, sK, sV);
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
+    }
   }
 
   // ---- epilogue: O / l, round to bf16, store (lane holds 4 consecutive d per group) ----
@@ -297,9 +406,14 @@ __global__ __launch_bounds__(256, 2) void prefill_tile_kernel(TileArgs a) {
 #pragma unroll
       for (int grp = 0; grp < 4; ++grp) {
         const int dd = 32 * dt + 8 * grp + 4 * half;
+        float4 sc = make_float4(inv, inv, inv, inv);
+        if constexpr (KV8) {                       // v_scale of channels dd .. dd + 3
+          const float4 vs = *reinterpret_cast<const float4*>(a.v_scale + (int64_t)g * D + dd);
+          sc = make_float4(inv * vs.x, inv * vs.y, inv * vs.z, inv * vs.w);
+        }
         uint2 pk;
-        pk.x = pack_bf16x2(O[dt][4 * grp + 0] * inv, O[dt][4 * grp + 1] * inv);
-        pk.y = pack_bf16x2(O[dt][4 * grp + 2] * inv, O[dt][4 * grp + 3] * inv);
+        pk.x = pack_bf16x2(O[dt][4 * grp + 0] * sc.x, O[dt][4 * grp + 1] * sc.y);
+        pk.y = pack_bf16x2(O[dt][4 * grp + 2] * sc.z, O[dt][4 * grp + 3] * sc.w);
         *reinterpret_cast<uint2*>(op + dd * 2) = pk;
       }
   }
@@ -348,12 +462,19 @@ hipError_t launch_plan_tiles(const int32_t* qsl, int num_seqs, int pos_per_tile,
   return hipGetLastError();
 }
 
-hipError_t launch_prefill_tile(const TileArgs& a, int head_dim, hipStream_t s) {
+hipError_t launch_prefill_tile(const TileArgs& a, int head_dim, bool kv8, hipStream_t s) {
   const int64_t grid = (int64_t)a.num_slots * a.num_kv_heads;
   if (grid <= 0 || grid > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
-  if (head_dim == 128) prefill_tile_kernel<128><<<dim3((unsigned)grid), dim3(256), 0, s>>>(a);
-  else if (head_dim == 64) prefill_tile_kernel<64><<<dim3((unsigned)grid), dim3(256), 0, s>>>(a);
-  else return hipErrorInvalidValue;
+  const dim3 g((unsigned)grid), blk(256);
+  if (head_dim == 128) {
+    if (kv8) prefill_tile_kernel<128, true><<<g, blk, 0, s>>>(a);
+    else prefill_tile_kernel<128, false><<<g, blk, 0, s>>>(a);
+  } else if (head_dim == 64) {
+    if (kv8) prefill_tile_kernel<64, true><<<g, blk, 0, s>>>(a);
+    else prefill_tile_kernel<64, false><<<g, blk, 0, s>>>(a);
+  } else {
+    return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 

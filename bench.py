@@ -12,7 +12,7 @@ Prints one JSON line.  The default workload is the 32-request bf16 decode batch 
 d=128, contexts U[512, 4096], 16384-block pool); its metric is KV-read GB/s.  --window N runs the
 same workload with a sliding window of N keys per query row; work counts then cover only the keys
 and pairs inside the windows.  --kv i8 keeps the workload's shapes and lengths over an 8-bit cache
-(int8 codes, fp32 scale per KV head and channel; decode workloads only): KV bytes count 1 byte per
+(int8 codes, fp32 scale per KV head and channel; c2 .. c5): KV bytes count 1 byte per
 element.  --verify K turns a decode workload into a verification step: each request appends and
 attends its last K tokens (same lengths and tables), still one read of every visible key.
 """
@@ -167,8 +167,8 @@ def main():
         print("--window must be >= 0", file=sys.stderr)
         sys.exit(2)
     win = args.window
-    if args.kv == "i8" and args.config not in ("c2", "c5"):
-        print("--kv i8 serves the decode workloads (c2, c5)", file=sys.stderr)
+    if args.kv == "i8" and args.config == "c1":
+        print("--kv i8 serves the bf16-activation workloads (c2 .. c5)", file=sys.stderr)
         sys.exit(2)
     t0 = time.time()
     w = W.CONFIGS[args.config](cache="i8") if args.kv == "i8" else W.CONFIGS[args.config]()

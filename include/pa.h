@@ -40,7 +40,7 @@ extern "C" {
 
 typedef enum {
   PA_OK = 0,
-  PA_ERR_INVALID_ARG = 1,   /* null pointer, bad size or descriptor                        */
+  PA_ERR_INVALID_ARG = 1,   /* null or misaligned pointer, bad size or descriptor          */
   PA_ERR_UNSUPPORTED = 2,   /* valid but not implemented (head_dim, dtype, group size)     */
   PA_ERR_DEVICE = 3,        /* a HIP call or launch failed; pa_last_error() has its text    */
   PA_ERR_WORKSPACE = 4,     /* caller workspace smaller than pa_attention_workspace_size()  */
@@ -54,7 +54,9 @@ typedef enum { PA_DTYPE_F32 = 0, PA_DTYPE_BF16 = 1, PA_DTYPE_I8 = 2 } pa_dtype;
 
 /* Describes both caches.  block_size must be 16 (P1 §2.3: 16 tokens per block, a 4096-token
  * prompt takes 256 blocks).  head_dim must be 64 or 128.  For F32 and BF16 caches the same dtype
- * is used for q, k, v, both caches and out; for I8 caches q, k, v and out are bf16. */
+ * is used for q, k, v, both caches and out; for I8 caches q, k, v and out are bf16.
+ * Every device buffer passed to this library (tensors, caches, scales, workspace) must be 16-byte
+ * aligned; a misaligned one is refused with PA_ERR_INVALID_ARG before anything is launched. */
 typedef struct {
   int32_t num_blocks;     /* NB: physical blocks in the pool                                */
   int32_t block_size;     /* must be PA_BLOCK_SIZE                                          */

@@ -98,6 +98,25 @@ def test_bad_sizes_rejected_before_launch(lib):
     assert lib.pa_append_kv(None, None, None, 0, None, None, ctypes.byref(d), None) == 0     # empty append
 
 
+def test_misaligned_buffers_rejected_before_launch(lib):
+    d = _desc()
+    p, o, c2, bad = (ctypes.c_void_p(x) for x in (16, 48, 4096, 4104))
+    for args in ((bad, 4, 8, p, c2), (p, 4, 8, bad, c2), (p, 4, 8, p, bad)):
+        q, T, H, kc, vc = args
+        assert lib.pa_attention(q, T, H, kc, vc, ctypes.byref(d), p, 4, 16, p, p, ctypes.c_float(1), o, None, 0,
+                                None) == 1
+        assert b"aligned" in lib.pa_last_error()
+    assert lib.pa_attention(p, 4, 8, p, c2, ctypes.byref(d), p, 4, 16, p, p, ctypes.c_float(1), bad, None, 0,
+                            None) == 1
+    assert lib.pa_attention(p, 4, 8, p, c2, ctypes.byref(d), p, 4, 64, p, p, ctypes.c_float(1), o, bad, 1 << 20,
+                            None) == 1
+    assert lib.pa_append_kv(bad, p, p, 4, o, c2, ctypes.byref(d), None) == 1
+    assert lib.pa_append_kv(p, p, p, 4, o, bad, ctypes.byref(d), None) == 1
+    i8 = pa._CacheDesc(8, 16, 2, 128, 2, c2, bad)
+    assert lib.pa_append_kv(p, p, p, 4, o, c2, ctypes.byref(i8), None) == 1
+    assert b"aligned" in lib.pa_last_error()
+
+
 def test_window_option_rejected_when_negative_before_launch(lib):
     d = _desc()
     p = ctypes.c_void_p(16)
@@ -125,10 +144,10 @@ def test_int8_descriptor_rules_checked_before_launch(lib):
     assert lib.pa_attention(p, 4, 8, p, p, ctypes.byref(stray), p, 4, 16, p, p, ctypes.c_float(1), o, None, 0,
                             None) == 1
     i8 = pa._CacheDesc(8, 16, 2, 128, 2, sc, sc)
-    # q_len >= 2 somewhere (5 tokens over 4 requests): not served on int8 caches, refused before launch
-    assert lib.pa_attention(p, 5, 8, p, p, ctypes.byref(i8), p, 4, 16, p, p, ctypes.c_float(1), o, None, 0,
-                            None) == 2
-    assert b"int8" in lib.pa_last_error()
+    # q_len >= 2 somewhere (5 tokens over 4 requests) runs on the tile pass, which needs a tile list
+    # in the workspace: an 8-byte one is refused before launch
+    assert lib.pa_attention(p, 5, 8, p, p, ctypes.byref(i8), p, 4, 16, p, p, ctypes.c_float(1), o,
+                            ctypes.c_void_p(256), 8, None) == 4
     assert lib.pa_attention_workspace_size(4, 4, 64, 8, ctypes.byref(i8)) > 0
 
 

@@ -1,6 +1,7 @@
 """GPU parity of the 8-bit KV cache (P2 §4.3, §5.4: INT8 codes with per-channel calibration) against
 the CPU oracle: quantising append bit for bit over the whole cache, attention within the bf16
-tolerances, dequantised argmax probes bit-exact."""
+tolerances (decode rows, prompts, chunks over cached context, mixed steps), dequantised argmax
+probes bit-exact."""
 import numpy as np
 import pytest
 
@@ -108,15 +109,47 @@ def test_int8_repeat_runs_bitwise_identical():
     assert np.array_equal(a, b)
 
 
-def test_int8_rejects_prefill_rows():
-    import torch
-    w = W.make_batch(711, [40, 20], [40, 1], 8, 2, 128, "bf16", num_blocks=8, cache="i8")
-    g = GpuState(w)
-    x = g.inputs(w.steps[0])
-    out = torch.empty_like(x["q"])
-    with pytest.raises(pa.PAError) as e:
-        pa.attention(x["q"], g.kc, g.vc, x["bt"], x["sl"], x["qsl"], w.scale, out, k_scale=g.ks, v_scale=g.vs)
-    assert e.value.code == 2
+PREFILL_CASES = [
+    # seq_lens, q_lens, Hq, Hkv, d: one-shot prompts, chunks over cached context, mixes with decodes
+    ([1, 2, 16, 17], [1, 2, 16, 17], 4, 2, 128),
+    ([40, 20], [40, 1], 8, 2, 128),
+    ([100, 64, 17, 129], [100, 64, 17, 129], 8, 8, 64),
+    ([300, 1000], [37, 129], 16, 4, 128),
+    ([500, 17, 3000, 64, 2], [1, 17, 200, 1, 2], 32, 8, 128),
+    ([700, 257], [300, 256], 16, 1, 64),
+    ([600, 2000, 33, 9], [4, 8, 2, 8], 32, 8, 128),      # verify-sized rows
+]
+
+
+@pytest.mark.parametrize("case", range(len(PREFILL_CASES)))
+def test_int8_prefill_and_chunk_rows(case):
+    seq, ql, Hq, Hkv, d = PREFILL_CASES[case]
+    say(f"int8 prefill case {case}: seq {seq} q {ql} Hq {Hq} Hkv {Hkv} d {d}")
+    w = W.make_batch(720 + case, seq, ql, Hq, Hkv, d, "bf16",
+                     num_blocks=sum((s + 15) // 16 for s in seq) + 3, cache="i8")
+    run_i8(w, what=f"int8 prefill[{case}]")
+
+
+@pytest.mark.parametrize("window", [1, 17, 100])
+def test_int8_chunk_rows_with_window(window):
+    w = W.make_batch(740 + window, [300, 1000, 33, 900], [37, 129, 33, 1], 16, 4, 128, "bf16",
+                     num_blocks=160, cache="i8")
+    run_i8(w, window=window, what=f"int8 chunks W={window}")
+
+
+@pytest.mark.timeout(600)
+def test_int8_c3_prefill_8k_sampled_rows():
+    rows = np.unique(np.concatenate([[0, 1, 2, 15, 16, 127, 128, 129, 4095, 4096, 8190, 8191],
+                                     np.random.default_rng(9).integers(0, 8192, 16)]))
+    run_i8(W.config3(cache="i8"), rows=rows, what="c3 int8 sampled rows")
+
+
+@pytest.mark.timeout(600)
+def test_int8_c4_mixed_chunk():
+    rng = np.random.default_rng(10)
+    chunk_rows = 30 + np.unique(np.concatenate([[0, 1, 31, 32, 2047], rng.integers(0, 2048, 12)]))
+    rows = np.concatenate([np.arange(30), chunk_rows])
+    run_i8(W.config4(cache="i8"), rows=rows, what="c4 int8 decodes + sampled chunk rows")
 
 
 @pytest.mark.timeout(600)
