@@ -91,6 +91,23 @@ __device__ __forceinline__ bf16x4 lds_read_tr(const uint16_t* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)(const __attribute__((address_space(3))) uint16_t*)p);
 }
 
+// 16 bytes per lane from global memory straight into LDS: lane i writes lds + 16 i, reading
+// gbase + voff (gbase uniform across the wave, voff per lane).  Issued as inline assembly so the
+// compiler does not see the copy: it keeps counting its own loads precisely instead of waiting for
+// every outstanding copy before each LDS read.  The caller waits for completion itself
+// (s_waitcnt vmcnt) before the data is read.  M0 is saved and restored around the copy.
+__device__ __forceinline__ uint32_t lds_u32(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+__device__ __forceinline__ void dma16(const void* gbase, uint32_t voff, uint32_t lds) {
+  const uint64_t gb = (uint64_t)(uintptr_t)gbase;          // the address operand must be scalar
+  gbase = (const void*)(uintptr_t)(((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(gb >> 32)) << 32) |
+                                   (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)gb));
+  uint32_t keep;
+  asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %3\n\tglobal_load_lds_dwordx4 %1, %2\n\ts_mov_b32 m0, %0"
+               : "=&s"(keep) : "v"(voff), "s"(gbase), "s"(lds) : "memory");
+}
+
 constexpr float kLog2e = 1.4426950408889634f;
 
 }  // namespace pa

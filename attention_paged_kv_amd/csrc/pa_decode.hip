@@ -101,10 +101,13 @@ __device__ __forceinline__ bool get_unit(const DecodeArgs& a, int nzh, Unit& u) 
 // ------------------------------------------------------------------------------------------
 // bf16: matrix-core split kernel.  A workgroup covers four adjacent KV heads of the
 // same request and split (one wave each), so together its waves read contiguous 4 x 256-byte
-// spans of every token row.  Each wave streams all blocks of the split for its head: K goes from
-// HBM straight into A-operand registers (one block ahead), V is copied by direct global->LDS loads
-// into a per-wave double buffer (rows' 16-byte chunks XOR-swizzled so the transpose reads are free
-// of bank conflicts).  The MFMA columns are (position, query head) pairs of the request: a decode
+// spans of every token row.  Each wave streams all blocks of the split for its head: K and V of a
+// block are copied by direct global->LDS loads into one slot of a per-wave double buffer while the
+// wave computes on the other slot (rows' 16-byte chunks XOR-swizzled so the K operand reads and the
+// V transpose reads are free of bank conflicts).  The copies are issued as inline assembly and
+// waited for with explicit vmcnt counts: with direct-to-LDS loads in view, the compiler waits for
+// every outstanding copy before an LDS read, which would wait for the next block's copies before
+// the current block is computed and leave no load in flight during the arithmetic.  The MFMA columns are (position, query head) pairs of the request: a decode
 // row has one position, a row of a few tokens to verify (P4 "一步的 token 预算": speculative
 // verification advances several tokens in one step) has q_len of them, each masked to its own
 // causal (and window) range, so the K/V of the request are read once for all of them.  Unused
@@ -118,6 +121,13 @@ __device__ __forceinline__ int dswz(int r) {
   if constexpr (D == 128) return 2 * (r & 7);
   else return (((r ^ (r >> 2)) & 1) << 1) | (((r >> 1) & 1) << 2);
 }
+// Same for staged K rows, read as 16-byte A operands by lanes (row = lane % 16, chunk 4kk + lane / 16):
+// the 16 rows of one 16-lane group land on 16 distinct 16-byte bank groups.
+template <int D>
+__device__ __forceinline__ int kswz(int r) {
+  if constexpr (D == 128) return r & 15;
+  else return (r >> 1) & 7;
+}
 }
 
 template <int D>
@@ -128,9 +138,9 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
   constexpr int CPR = D / 8;                  // 16-byte chunks per row
   constexpr int RPI = 64 / CPR;               // rows per wave-wide 1 KiB copy
   constexpr int IPB = kBlock / RPI;           // copies per 16-row block
-  constexpr int VB = kBlock * ROWB;           // bytes per staged V block
-  __shared__ __align__(16) char sV0[4 * VB];  // [wave] buffer 0
-  __shared__ __align__(16) char sV1[4 * VB];  // [wave] buffer 1
+  constexpr int VB = kBlock * ROWB;           // bytes per staged K (or V) block
+  constexpr int NCP = 2 * IPB;                // copies per block (K and V)
+  __shared__ __align__(16) char sKV[2 * 4 * 2 * VB];   // [slot][wave][K block, V block]
 
   // unit: (row, split, head quad), the quad fastest; the wave's KV head is 4 * quad + w.  A row
   // with more (position, head) columns than one MFMA holds runs its column groups one after the
@@ -191,13 +201,17 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
     const int nb = (k1 + kBlock - 1) / kBlock - kb0;        // <= 64: splits are at most 1024 keys
     const int ids = lane < nb ? table[kb0 + lane] : 0;       // lane i: id of the split's i-th block
 
-    // K operand: key row `col`, d = 32kk + 8grp: byte offset within the block
-    const uint32_t k_lane = (uint32_t)(col * rs * 2) + 16 * grp;
-    // V copy: copy i covers rows RPI*i ..; lane -> (row RPI*i + lane / CPR, physical chunk lane % CPR)
-    uint32_t v_lane[IPB];
+    // K operand: key row `col`, d = 32kk + 8grp, i.e. logical chunk 4kk + grp of the staged row
+    uint32_t k_rd[NKK];
+  #pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) k_rd[kk] = col * ROWB + (((4 * kk + grp) ^ kswz<D>(col)) * 16);
+    // copies: copy i covers rows RPI*i ..; lane -> (row RPI*i + lane / CPR, physical chunk lane % CPR),
+    // which holds logical chunk (lane % CPR) ^ swz(row) of the cache row
+    uint32_t k_lane[IPB], v_lane[IPB];
   #pragma unroll
     for (int i = 0; i < IPB; ++i) {
       const int r = RPI * i + lane / CPR;
+      k_lane[i] = (uint32_t)(r * rs * 2) + (((lane % CPR) ^ kswz<D>(r)) * 16);
       v_lane[i] = (uint32_t)(r * rs * 2) + (((lane % CPR) ^ dswz<D>(r)) * 16);
     }
     // transpose read: group grp, lane j = 4e + cq reads row 4grp + e, columns 16tt + 4cq .. +3,
@@ -215,28 +229,30 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
   #pragma unroll
     for (int tt = 0; tt < NT; ++tt) O[tt] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-    auto issue = [&](int i, uint4* kr, char* vdst) {        // block kb0 + i: K to registers, V to LDS
+    char* const mine = sKV + w * 2 * VB;                     // this wave's slot 0; slot 1 is 8 * VB on
+    auto issue = [&](int i, int slot) {                      // block kb0 + i: K and V into the slot
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");    // the slot's earlier reads are done
       const char* kb = kbase + (int64_t)__builtin_amdgcn_readlane(ids, i) * blkbytes;
       const char* vb = vbase + (kb - kbase);
+      const uint32_t l = __builtin_amdgcn_readfirstlane(lds_u32(mine + slot * 8 * VB));
   #pragma unroll
-      for (int kk = 0; kk < NKK; ++kk) kr[kk] = *reinterpret_cast<const uint4*>(kb + k_lane + kk * 64);
+      for (int j = 0; j < IPB; ++j) dma16(kb, k_lane[j], l + 1024 * j);
   #pragma unroll
-      for (int j = 0; j < IPB; ++j)
-        __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(vb + v_lane[j]),
-                                         (__attribute__((address_space(3))) void*)(vdst + w * VB + 1024 * j), 16, 0, 0);
+      for (int j = 0; j < IPB; ++j) dma16(vb, v_lane[j], l + VB + 1024 * j);
     };
 
     // one block.  EDGE blocks hold keys some column must not see -- before its window or after its
     // position (the split's last blocks, and the first blocks of split 0 under a window).  The
     // test is uniform across the wave and picks one of two compiled copies, so other blocks carry
     // no masking at all.
-    auto consume_as = [&](auto edge_tag, int i, const uint4* kr, const char* vsrc) {
+    auto consume_as = [&](auto edge_tag, int i, int slot) {
       constexpr bool EDGE = decltype(edge_tag)::value;
       const int s0 = (kb0 + i) * kBlock;
+      const char* kw = mine + slot * 8 * VB;
       floatx4 s = floatx4{0.f, 0.f, 0.f, 0.f};
   #pragma unroll
       for (int kk = 0; kk < NKK; ++kk)
-        s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kr[kk]), qb[kk], s, 0, 0, 0);
+        s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*reinterpret_cast<const bf16x8*>(kw + k_rd[kk]), qb[kk], s, 0, 0, 0);
       if constexpr (EDGE) {
   #pragma unroll
         for (int v = 0; v < 4; ++v) {
@@ -260,7 +276,7 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
       for (int v = 0; v < 4; ++v) pb[v] = (__bf16)p[v];
   #pragma unroll
       for (int tt = 0; tt < NT; ++tt) O[tt] *= alpha;
-      const char* vw = vsrc + w * VB;
+      const char* vw = kw + VB;
       bf16x4 vt[NT];
   #pragma unroll
       for (int tt = 0; tt < NT; ++tt) vt[tt] = lds_read_tr(reinterpret_cast<const uint16_t*>(vw + tr_off[tt]));
@@ -278,29 +294,23 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
   #pragma unroll
       for (int tt = 0; tt < NT; ++tt) O[tt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vt[tt], pb, O[tt], 0, 0, 0);
     };
-    auto consume = [&](int i, const uint4* kr, const char* vsrc) {
+    auto consume = [&](int i, int slot) {
       const int s0 = (kb0 + i) * kBlock;
-      if (s0 < lo_max || s0 + kBlock > ctx + 1) consume_as(std::true_type{}, i, kr, vsrc);
-      else consume_as(std::false_type{}, i, kr, vsrc);
+      if (s0 < lo_max || s0 + kBlock > ctx + 1) consume_as(std::true_type{}, i, slot);
+      else consume_as(std::false_type{}, i, slot);
     };
 
-    {
-      uint4 kA[NKK], kB[NKK];
-      issue(0, kA, sV0);
-      int i = 0;
-      for (; i + 2 < nb; i += 2) {                           // steady state: next block always exists
-        issue(i + 1, kB, sV1);
-        consume(i, kA, sV0);
-        issue(i + 2, kA, sV0);                               // sV0 reads above are ahead in the LDS queue
-        consume(i + 1, kB, sV1);
+    // one block in flight while the previous one is computed; the wait leaves exactly the next
+    // block's NCP copies outstanding (vector memory operations complete in issue order)
+    issue(0, 0);
+    for (int i = 0; i < nb; ++i) {
+      if (i + 1 < nb) {
+        issue(i + 1, (i + 1) & 1);
+        asm volatile("s_waitcnt vmcnt(%0)" :: "n"(NCP) : "memory");
+      } else {
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       }
-      if (i + 1 < nb) {                                      // two blocks left
-        issue(i + 1, kB, sV1);
-        consume(i, kA, sV0);
-        consume(i + 1, kB, sV1);
-      } else {                                               // one block left
-        consume(i, kA, sV0);
-      }
+      consume(i, i & 1);
     }
     lsum = xor16_sum(lsum);
     lsum = xor32_sum(lsum);

@@ -69,6 +69,14 @@ __device__ __forceinline__ f16x8 codes_f16(uint32_t lo, uint32_t hi) {
   return r;
 }
 
+// Physical 16-byte chunk of logical chunk q in staged K row r (D / 16 chunks per row) is q ^ kswz(r):
+// the 16 rows read by one 16-lane group for the same logical chunk land on distinct bank groups.
+template <int D>
+__device__ __forceinline__ int kswz(int r) {
+  if constexpr (D == 128) return (r >> 1) & 7;
+  else return (r >> 2) & 3;
+}
+
 // 8-bit transpose read: in each 16-lane group, lane 2e + h gives the address of bytes 8h..8h+7 of
 // row e of an 8 x 16-byte tile; lane j receives column j of the tile (rows 0..7).
 typedef __attribute__((address_space(3))) i32x2 lds_i32x2_t;
@@ -79,7 +87,10 @@ __device__ __forceinline__ i32x2 lds_read_tr8(const char* p) {
 }  // namespace
 
 // NW waves per workgroup, one adjacent KV head each: together they read NW * d contiguous bytes of
-// every token row they visit.
+// every token row they visit.  K and V codes of a 32-key unit are copied by direct global->LDS loads
+// into one slot of a per-wave double buffer while the wave computes the other slot; the copies are
+// inline assembly waited for with explicit vmcnt counts (see dma16), so the next unit's copies stay
+// in flight during the arithmetic.
 template <int D, int NW>
 __global__ __launch_bounds__(64 * NW, NW == 4 ? 3 : 2) void decode_i8_kernel(DecodeArgs a) {
   constexpr int NKK = D / 32;                 // 16x16x32 k-steps over d for S^T (8 codes per lane)
@@ -89,8 +100,8 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 3 : 2) void decode_i8_kernel(Dec
   constexpr int RPI = 1024 / D;               // rows per wave-wide 1 KiB copy
   constexpr int IPB = kBlock / RPI;           // copies per 16-row block
   constexpr int UB = 2 * kBlock * D;          // bytes of one staged 32-key unit (two blocks)
-  __shared__ __align__(16) char sV0[NW * UB];  // [wave] buffer 0
-  __shared__ __align__(16) char sV1[NW * UB];  // [wave] buffer 1
+  constexpr int NCP = 4 * IPB;                // copies per unit (two blocks of K and of V)
+  __shared__ __align__(16) char sKV[2 * NW * 2 * UB];   // [slot][wave][K unit, V unit]
 
   // unit: (row, split, head group, query-head column group); the wave's KV head is NW * group + w
   const int nzh = (a.group + a.heads_per_wg - 1) / a.heads_per_wg;
@@ -178,10 +189,18 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 3 : 2) void decode_i8_kernel(Dec
   const int nu = (nb + 1) >> 1;                            // 32-key units
   const int ids = lane < nb ? table[kb0 + lane] : 0;       // lane i: id of the split's i-th block
 
-  // K operand: key row `col`, bytes 64j + 16grp .. +16 of it
-  const uint32_t k_lane = (uint32_t)(col * rs) + 16 * grp;
-  // V copy i of staged block sb: lane -> (row RPI*i + lane / CPR, physical chunk lane % CPR)
-  uint32_t v_lane[2][IPB];
+  // K operand j of a block: key row `col`, logical chunk grp + 4j (bytes 64j + 16grp .. +16)
+  uint32_t k_rd[KL];
+#pragma unroll
+  for (int j = 0; j < KL; ++j) k_rd[j] = col * D + (((grp + 4 * j) ^ kswz<D>(col)) * 16);
+  // copy i of staged block sb: lane -> (row RPI*i + lane / CPR, physical chunk lane % CPR), holding
+  // logical chunk (lane % CPR) ^ swizzle of the cache row
+  uint32_t k_lane[IPB], v_lane[2][IPB];
+#pragma unroll
+  for (int i = 0; i < IPB; ++i) {
+    const int r = RPI * i + lane / CPR;
+    k_lane[i] = (uint32_t)(r * rs) + (((lane % CPR) ^ kswz<D>(r)) * 16);
+  }
 #pragma unroll
   for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
@@ -206,30 +225,36 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 3 : 2) void decode_i8_kernel(Dec
 
   // unit u = blocks 2u and 2u + 1 of the split; a missing second block is replaced by the first
   // (valid memory) and all its keys are masked
-  auto issue = [&](int u, uint4* kr, char* vdst) {
+  char* const mine = sKV + w * 2 * UB;                     // this wave's slot 0; slot 1 is NW * 2 * UB on
+  auto issue = [&](int u, int slot) {
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");    // the slot's earlier reads are done
     const int i1 = min(2 * u + 1, nb - 1);
     const int64_t o0 = (int64_t)__builtin_amdgcn_readlane(ids, 2 * u) * blkbytes;
     const int64_t o1 = (int64_t)__builtin_amdgcn_readlane(ids, i1) * blkbytes;
+    const uint32_t l = __builtin_amdgcn_readfirstlane(lds_u32(mine + slot * NW * 2 * UB));
 #pragma unroll
-    for (int j = 0; j < KL; ++j) {
-      kr[j] = *reinterpret_cast<const uint4*>(kbase + o0 + k_lane + 64 * j);
-      kr[KL + j] = *reinterpret_cast<const uint4*>(kbase + o1 + k_lane + 64 * j);
+    for (int i = 0; i < IPB; ++i) {
+      dma16(kbase + o0, k_lane[i], l + 1024 * i);
+      dma16(kbase + o1, k_lane[i], l + kBlock * D + 1024 * i);
     }
-    char* vw = vdst + w * UB;
 #pragma unroll
-    for (int i = 0; i < IPB; ++i)
-      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(vbase + o0 + v_lane[0][i]),
-                                       (__attribute__((address_space(3))) void*)(vw + 1024 * i), 16, 0, 0);
-#pragma unroll
-    for (int i = 0; i < IPB; ++i)
-      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(vbase + o1 + v_lane[1][i]),
-                                       (__attribute__((address_space(3))) void*)(vw + kBlock * D + 1024 * i), 16, 0, 0);
+    for (int i = 0; i < IPB; ++i) {
+      dma16(vbase + o0, v_lane[0][i], l + UB + 1024 * i);
+      dma16(vbase + o1, v_lane[1][i], l + UB + kBlock * D + 1024 * i);
+    }
   };
 
   // one unit; EDGE: it holds keys outside [lo, k1) (the split's last unit, or its first one when a
   // sliding window starts inside it)
-  auto consume = [&](auto edge_tag, int u, const uint4* kr, const char* vsrc) {
+  auto consume = [&](auto edge_tag, int u, int slot) {
     constexpr bool EDGE = decltype(edge_tag)::value;
+    const char* kw = mine + slot * NW * 2 * UB;
+    uint4 kr[2 * KL];
+#pragma unroll
+    for (int j = 0; j < KL; ++j) {
+      kr[j] = *reinterpret_cast<const uint4*>(kw + k_rd[j]);
+      kr[KL + j] = *reinterpret_cast<const uint4*>(kw + kBlock * D + k_rd[j]);
+    }
     floatx4 sA = floatx4{0.f, 0.f, 0.f, 0.f}, sB = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk) {
@@ -277,7 +302,7 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 3 : 2) void decode_i8_kernel(Dec
       pb[4 + v] = (_Float16)pv;
     }
     lsum += ps;
-    const char* vw = vsrc + w * UB;
+    const char* vw = kw + UB;
 #pragma unroll
     for (int tt = 0; tt < NT; ++tt) {
       const i32x2 x = lds_read_tr8(vw + tr_off[tt]);
@@ -289,34 +314,18 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 3 : 2) void decode_i8_kernel(Dec
   const bool last_partial = (kb0 + 2 * nu) * kBlock > k1;
   const bool first_cut = kb0 * kBlock < lo;                // split 0 of a row whose window starts mid-block
 
-  {
-    uint4 kA[2 * KL], kB[2 * KL];
-    issue(0, kA, sV0);
-    int u = 0;
-    if (first_cut && nu > 2) {                             // peel the first pair: unit 0 is an edge
-      issue(1, kB, sV1);
-      consume(Edge{}, 0, kA, sV0);
-      issue(2, kA, sV0);
-      consume(Full{}, 1, kB, sV1);
-      u = 2;
+  // one unit in flight while the previous one is computed; the wait leaves exactly the next unit's
+  // NCP copies outstanding (vector memory operations complete in issue order)
+  issue(0, 0);
+  for (int u = 0; u < nu; ++u) {
+    if (u + 1 < nu) {
+      issue(u + 1, (u + 1) & 1);
+      asm volatile("s_waitcnt vmcnt(%0)" :: "n"(NCP) : "memory");
+    } else {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     }
-    for (; u + 2 < nu; u += 2) {                           // steady state: next unit always exists
-      issue(u + 1, kB, sV1);
-      consume(Full{}, u, kA, sV0);
-      issue(u + 2, kA, sV0);                               // sV0 reads above are ahead in the LDS queue
-      consume(Full{}, u + 1, kB, sV1);
-    }
-    const bool head_cut = first_cut && u == 0;
-    if (u + 1 < nu) {                                      // two units left
-      issue(u + 1, kB, sV1);
-      if (head_cut) consume(Edge{}, u, kA, sV0);
-      else consume(Full{}, u, kA, sV0);
-      if (last_partial) consume(Edge{}, u + 1, kB, sV1);
-      else consume(Full{}, u + 1, kB, sV1);
-    } else {                                               // one unit left
-      if (last_partial || head_cut) consume(Edge{}, u, kA, sV0);
-      else consume(Full{}, u, kA, sV0);
-    }
+    if ((u == 0 && first_cut) || (u + 1 == nu && last_partial)) consume(Edge{}, u, u & 1);
+    else consume(Full{}, u, u & 1);
   }
   lsum = xor16_sum(lsum);
   lsum = xor32_sum(lsum);
