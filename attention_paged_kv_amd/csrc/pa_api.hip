@@ -109,10 +109,12 @@ hipError_t timed(const char* name, hipStream_t s, F&& launch) {
   }
   hipEvent_t a = take_event(), b = take_event();
   if (!a || !b) return hipErrorOutOfMemory;
-  hipEventRecord(a, s);
-  hipError_t e = launch();
-  hipEventRecord(b, s);
-  g_pending.push_back({name, a, b});
+  hipError_t e = hipEventRecord(a, s);
+  if (e != hipSuccess) return e;
+  e = launch();
+  const hipError_t eb = hipEventRecord(b, s);
+  if (e == hipSuccess) e = eb;
+  if (e == hipSuccess) g_pending.push_back({name, a, b});
   return e;
 }
 
@@ -265,19 +267,19 @@ const char* pa_last_error(void) { return g_err.c_str(); }
 
 void pa_set_check(int on) { g_check.store(on ? 1 : 0); }
 
-void pa_release(void) {
+void pa_release(void) {   // best effort: errors here have nowhere to go
   std::lock_guard<std::mutex> lk(g_dev_mu);
   int cur = 0;
-  hipGetDevice(&cur);
+  (void)hipGetDevice(&cur);
   for (auto& kv : g_dev) {
-    hipSetDevice(kv.first);
-    hipDeviceSynchronize();
-    if (kv.second.ws) hipFree(kv.second.ws);
-    if (kv.second.check) hipFree(kv.second.check);
+    (void)hipSetDevice(kv.first);
+    (void)hipDeviceSynchronize();
+    if (kv.second.ws) (void)hipFree(kv.second.ws);
+    if (kv.second.check) (void)hipFree(kv.second.check);
     kv.second = DevState{};
   }
   g_dev.clear();
-  hipSetDevice(cur);
+  (void)hipSetDevice(cur);
 }
 
 int pa_append_kv(const void* k, const void* v, const int32_t* slot_mapping, int32_t num_tokens, void* k_cache,
@@ -358,10 +360,11 @@ int pa_attention_ex(const void* q, int32_t num_q_tokens, int32_t num_q_heads, co
       DevState& st = g_dev[dev];
       if (st.ws_bytes < p.total) {
         if (st.ws) {
-          hipDeviceSynchronize();
-          hipFree(st.ws);
+          hipError_t e = hipDeviceSynchronize();             // earlier calls may still use it
+          if (e == hipSuccess) e = hipFree(st.ws);
           st.ws = nullptr;
           st.ws_bytes = 0;
+          if (e != hipSuccess) return device_fail(e, "releasing the old workspace");
         }
         hipError_t e = hipMalloc(&st.ws, p.total);
         if (e != hipSuccess) return device_fail(e, "hipMalloc(workspace)");
@@ -492,7 +495,7 @@ int pa_timing_read(const char* name, double* total_ms, int64_t* launches) {
 void pa_timing_reset(void) {
   std::lock_guard<std::mutex> lk(g_t_mu);
   for (auto& t : g_pending) {
-    hipEventSynchronize(t.b);
+    (void)hipEventSynchronize(t.b);                          // best effort: the events are recycled
     g_event_pool.push_back(t.a);
     g_event_pool.push_back(t.b);
   }

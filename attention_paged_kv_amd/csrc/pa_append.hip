@@ -137,14 +137,15 @@ hipError_t launch_check(const CheckArgs& a, hipStream_t s) {
     hipError_t e = hipMalloc(&bitmap, words * sizeof(unsigned));
     if (e != hipSuccess) return e;
     e = hipMemsetAsync(bitmap, 0, words * sizeof(unsigned), s);
-    if (e != hipSuccess) { hipFree(bitmap); return e; }
+    if (e != hipSuccess) { (void)hipFree(bitmap); return e; }
   }
   check_kernel<<<dim3(64), dim3(256), 0, s>>>(a, bitmap);
   hipError_t e = hipGetLastError();
   if (bitmap) {
     hipError_t e2 = hipStreamSynchronize(s);
-    hipFree(bitmap);
+    const hipError_t e3 = hipFree(bitmap);
     if (e == hipSuccess) e = e2;
+    if (e == hipSuccess) e = e3;
   }
   return e;
 }

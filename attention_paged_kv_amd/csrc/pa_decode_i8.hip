@@ -92,7 +92,7 @@ __device__ __forceinline__ i32x2 lds_read_tr8(const char* p) {
 // inline assembly waited for with explicit vmcnt counts (see dma16), so the next unit's copies stay
 // in flight during the arithmetic.
 template <int D, int NW>
-__global__ __launch_bounds__(64 * NW, NW == 4 ? 3 : 2) void decode_i8_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(64 * NW, 2) void decode_i8_kernel(DecodeArgs a) {
   constexpr int NKK = D / 32;                 // 16x16x32 k-steps over d for S^T (8 codes per lane)
   constexpr int NT = D / 16;                  // 16-row d tiles of O^T
   constexpr int KL = D / 64;                  // 16-byte K loads per lane and block
