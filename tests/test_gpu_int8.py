@@ -47,6 +47,7 @@ CASES = [
     ([700, 129, 5], 16, 1, 64),
     ([1030, 300], 24, 3, 128),
     ([4097, 9000], 64, 4, 128),
+    ([2000, 33, 700], 64, 2, 128),          # 32 query heads per KV head
 ]
 
 

@@ -66,6 +66,12 @@ SMALL = [
     # bf16 head_dim 64 decode rows, one KV head: staged V rows are 128 bytes (8 chunks) wide
     ([15, 16, 17, 31, 32, 33, 700], [1, 1, 1, 1, 1, 1, 1], 8, 1, 64, "bf16"),
     ([300, 2000], [1, 1], 4, 4, 64, "bf16"),
+    # more query heads per KV head than one MFMA holds: 32 (two column groups) and the maximum, 128
+    ([3000, 77, 513], [1, 1, 1], 64, 2, 128, "bf16"),
+    ([900, 20, 40], [1, 20, 3], 128, 1, 64, "bf16"),
+    # a wide batch: 200 rows, lengths 1 .. 300, a few prompts among the decode rows
+    ([1 + (37 * i) % 300 for i in range(200)], [1 if i % 50 else 1 + (37 * i) % 300 for i in range(200)],
+     8, 8, 64, "bf16"),
 ]
 
 
