@@ -130,8 +130,11 @@ __device__ __forceinline__ int kswz(int r) {
 }
 }
 
-template <int D>
-__global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
+// NG column groups of 16 (position, head) columns are carried through one pass over the split's
+// keys (NG = 2 when a row has more than 16 columns, e.g. several tokens to verify on a grouped-query
+// model): K and V are read once for all of them.
+template <int D, int NG>
+__global__ __launch_bounds__(256, 2) void decode_mfma_kernel(DecodeArgs a) {
   constexpr int NKK = D / 32;                 // 16x16x32 k-steps over d for S^T
   constexpr int NT = D / 16;                  // 16-row d tiles of O^T
   constexpr int ROWB = D * 2;                 // bytes of one head's K or V row
@@ -143,9 +146,9 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
   __shared__ __align__(16) char sKV[2 * 4 * 2 * VB];   // [slot][wave][K block, V block]
 
   // unit: (row, split, head quad), the quad fastest; the wave's KV head is 4 * quad + w.  A row
-  // with more (position, head) columns than one MFMA holds runs its column groups one after the
-  // other in the same workgroup (the K/V re-read comes straight after the first), so the grid has
-  // no workgroups that find nothing to do.
+  // with more (position, head) columns than NG MFMAs hold runs its column groups NG at a time in
+  // the same workgroup (the K/V re-read comes straight after the first pass), so the grid has no
+  // workgroups that find nothing to do.
   const int nq = (a.num_kv_heads + 3) / 4;
   int ib = blockIdx.x;
   const int quad = ib % nq;
@@ -166,80 +169,88 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int g = 4 * quad + w;
   if (g >= a.num_kv_heads) return;                         // waves are independent: no barriers
-  for (int zh = 0; zh * a.heads_per_wg < ql * a.group; ++zh) {
-    const int c0 = zh * a.heads_per_wg;                      // first (position, head) column of the group
-    const int ncols = min(a.heads_per_wg, ql * a.group - c0);
 
-    const int lane = threadIdx.x & (kWave - 1);
-    const int col = lane & 15;                  // S^T / O^T column; also the K row loaded
-    const int grp = lane >> 4;                  // 4-key group of the accumulator layout
-    const float c = a.scale_log2;
-    const bool on = col < ncols;
-    const int cr = on ? (c0 + col) / a.group : 0;            // this column's position in the request
-    const int h = g * a.group + (on ? (c0 + col) % a.group : 0);
-    const int nvis = ctx + cr + 1;                           // keys [lo_c, nvis) are this column's
-    const int lo_c = first_visible(a, nvis);
+  const int lane = threadIdx.x & (kWave - 1);
+  const int col = lane & 15;                  // S^T / O^T column; also the K row read
+  const int grp = lane >> 4;                  // 4-key group of the accumulator layout
+  const float c = a.scale_log2;
+  const int ncol_all = ql * a.group;          // (position, head) columns of the row
 
-    // Q^T as the B operand: lane holds d = 32kk + 8grp .. +8 of its column's (token, head)
-    bf16x8 qb[NKK];
-    {
+  const int64_t rs = (int64_t)a.num_kv_heads * D;            // elements per cache token row
+  const int64_t blkbytes = kBlock * rs * 2;
+  const char* kbase = reinterpret_cast<const char*>(a.k_cache) + (int64_t)g * ROWB;
+  const char* vbase = reinterpret_cast<const char*>(a.v_cache) + (int64_t)g * ROWB;
+  const int32_t* table = a.block_tables + (int64_t)b * a.max_blocks;
+  const int kb0 = k0 / kBlock;
+  const int nb = (k1 + kBlock - 1) / kBlock - kb0;          // <= 64: splits are at most 1024 keys
+  const int ids = lane < nb ? table[kb0 + lane] : 0;         // lane i: id of the split's i-th block
+
+  // K operand: key row `col`, d = 32kk + 8grp, i.e. logical chunk 4kk + grp of the staged row
+  uint32_t k_rd[NKK];
+#pragma unroll
+  for (int kk = 0; kk < NKK; ++kk) k_rd[kk] = col * ROWB + (((4 * kk + grp) ^ kswz<D>(col)) * 16);
+  // copies: copy i covers rows RPI*i ..; lane -> (row RPI*i + lane / CPR, physical chunk lane % CPR),
+  // which holds logical chunk (lane % CPR) ^ swz(row) of the cache row
+  uint32_t k_lane[IPB], v_lane[IPB];
+#pragma unroll
+  for (int i = 0; i < IPB; ++i) {
+    const int r = RPI * i + lane / CPR;
+    k_lane[i] = (uint32_t)(r * rs * 2) + (((lane % CPR) ^ kswz<D>(r)) * 16);
+    v_lane[i] = (uint32_t)(r * rs * 2) + (((lane % CPR) ^ dswz<D>(r)) * 16);
+  }
+  // transpose read: group grp, lane j = 4e + cq reads row 4grp + e, columns 16tt + 4cq .. +3,
+  // i.e. logical chunk 2tt + cq / 2, byte half cq & 1
+  uint32_t tr_off[NT];
+#pragma unroll
+  for (int tt = 0; tt < NT; ++tt) {
+    const int r = 4 * grp + (col >> 2);
+    const int lq = 2 * tt + ((col & 3) >> 1);
+    tr_off[tt] = r * ROWB + ((lq ^ dswz<D>(r)) * 16) + (col & 1) * 8;
+  }
+
+  char* const mine = sKV + w * 2 * VB;                       // this wave's slot 0; slot 1 is 8 * VB on
+  auto issue = [&](int i, int slot) {                        // block kb0 + i: K and V into the slot
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");      // the slot's earlier reads are done
+    const char* kb = kbase + (int64_t)__builtin_amdgcn_readlane(ids, i) * blkbytes;
+    const char* vb = vbase + (kb - kbase);
+    const uint32_t l = __builtin_amdgcn_readfirstlane(lds_u32(mine + slot * 8 * VB));
+#pragma unroll
+    for (int j = 0; j < IPB; ++j) dma16(kb, k_lane[j], l + 1024 * j);
+#pragma unroll
+    for (int j = 0; j < IPB; ++j) dma16(vb, v_lane[j], l + VB + 1024 * j);
+  };
+
+  for (int zh = 0; zh * a.heads_per_wg < ncol_all; zh += NG) {
+    // this pass's columns: group gi holds columns (zh + gi) * heads_per_wg + col
+    bool on[NG];
+    int cr[NG], h[NG], nvis[NG], lo_c[NG];
+    bf16x8 qb[NG][NKK];                       // Q^T as the B operand: d = 32kk + 8grp .. +8
+#pragma unroll
+    for (int gi = 0; gi < NG; ++gi) {
+      const int c0 = (zh + gi) * a.heads_per_wg;
+      on[gi] = col < min(a.heads_per_wg, ncol_all - c0);
+      cr[gi] = on[gi] ? (c0 + col) / a.group : 0;            // this column's position in the request
+      h[gi] = g * a.group + (on[gi] ? (c0 + col) % a.group : 0);
+      nvis[gi] = ctx + cr[gi] + 1;                           // keys [lo_c, nvis) are this column's
+      lo_c[gi] = first_visible(a, nvis[gi]);
       const char* qp = reinterpret_cast<const char*>(a.q) +
-                       (((int64_t)(t0 + cr) * a.num_q_heads + h) * D + 8 * grp) * 2;
-  #pragma unroll
+                       (((int64_t)(t0 + cr[gi]) * a.num_q_heads + h[gi]) * D + 8 * grp) * 2;
+#pragma unroll
       for (int kk = 0; kk < NKK; ++kk) {
-        const uint4 v = on ? *reinterpret_cast<const uint4*>(qp + kk * 64) : make_uint4(0, 0, 0, 0);
-        qb[kk] = __builtin_bit_cast(bf16x8, v);
+        const uint4 v = on[gi] ? *reinterpret_cast<const uint4*>(qp + kk * 64) : make_uint4(0, 0, 0, 0);
+        qb[gi][kk] = __builtin_bit_cast(bf16x8, v);
       }
     }
 
-    const int64_t rs = (int64_t)a.num_kv_heads * D;            // elements per cache token row
-    const int64_t blkbytes = kBlock * rs * 2;
-    const char* kbase = reinterpret_cast<const char*>(a.k_cache) + (int64_t)g * ROWB;
-    const char* vbase = reinterpret_cast<const char*>(a.v_cache) + (int64_t)g * ROWB;
-    const int32_t* table = a.block_tables + (int64_t)b * a.max_blocks;
-    const int kb0 = k0 / kBlock;
-    const int nb = (k1 + kBlock - 1) / kBlock - kb0;        // <= 64: splits are at most 1024 keys
-    const int ids = lane < nb ? table[kb0 + lane] : 0;       // lane i: id of the split's i-th block
-
-    // K operand: key row `col`, d = 32kk + 8grp, i.e. logical chunk 4kk + grp of the staged row
-    uint32_t k_rd[NKK];
-  #pragma unroll
-    for (int kk = 0; kk < NKK; ++kk) k_rd[kk] = col * ROWB + (((4 * kk + grp) ^ kswz<D>(col)) * 16);
-    // copies: copy i covers rows RPI*i ..; lane -> (row RPI*i + lane / CPR, physical chunk lane % CPR),
-    // which holds logical chunk (lane % CPR) ^ swz(row) of the cache row
-    uint32_t k_lane[IPB], v_lane[IPB];
-  #pragma unroll
-    for (int i = 0; i < IPB; ++i) {
-      const int r = RPI * i + lane / CPR;
-      k_lane[i] = (uint32_t)(r * rs * 2) + (((lane % CPR) ^ kswz<D>(r)) * 16);
-      v_lane[i] = (uint32_t)(r * rs * 2) + (((lane % CPR) ^ dswz<D>(r)) * 16);
+    float m[NG], lsum[NG];
+    floatx4 O[NG][NT];
+#pragma unroll
+    for (int gi = 0; gi < NG; ++gi) {
+      m[gi] = -INFINITY;
+      lsum[gi] = 0.f;
+#pragma unroll
+      for (int tt = 0; tt < NT; ++tt) O[gi][tt] = floatx4{0.f, 0.f, 0.f, 0.f};
     }
-    // transpose read: group grp, lane j = 4e + cq reads row 4grp + e, columns 16tt + 4cq .. +3,
-    // i.e. logical chunk 2tt + cq / 2, byte half cq & 1
-    uint32_t tr_off[NT];
-  #pragma unroll
-    for (int tt = 0; tt < NT; ++tt) {
-      const int r = 4 * grp + (col >> 2);
-      const int lq = 2 * tt + ((col & 3) >> 1);
-      tr_off[tt] = r * ROWB + ((lq ^ dswz<D>(r)) * 16) + (col & 1) * 8;
-    }
-
-    float m = -INFINITY, lsum = 0.f;
-    floatx4 O[NT];
-  #pragma unroll
-    for (int tt = 0; tt < NT; ++tt) O[tt] = floatx4{0.f, 0.f, 0.f, 0.f};
-
-    char* const mine = sKV + w * 2 * VB;                     // this wave's slot 0; slot 1 is 8 * VB on
-    auto issue = [&](int i, int slot) {                      // block kb0 + i: K and V into the slot
-      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");    // the slot's earlier reads are done
-      const char* kb = kbase + (int64_t)__builtin_amdgcn_readlane(ids, i) * blkbytes;
-      const char* vb = vbase + (kb - kbase);
-      const uint32_t l = __builtin_amdgcn_readfirstlane(lds_u32(mine + slot * 8 * VB));
-  #pragma unroll
-      for (int j = 0; j < IPB; ++j) dma16(kb, k_lane[j], l + 1024 * j);
-  #pragma unroll
-      for (int j = 0; j < IPB; ++j) dma16(vb, v_lane[j], l + VB + 1024 * j);
-    };
 
     // one block.  EDGE blocks hold keys some column must not see -- before its window or after its
     // position (the split's last blocks, and the first blocks of split 0 under a window).  The
@@ -249,50 +260,58 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
       constexpr bool EDGE = decltype(edge_tag)::value;
       const int s0 = (kb0 + i) * kBlock;
       const char* kw = mine + slot * 8 * VB;
-      floatx4 s = floatx4{0.f, 0.f, 0.f, 0.f};
-  #pragma unroll
-      for (int kk = 0; kk < NKK; ++kk)
-        s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*reinterpret_cast<const bf16x8*>(kw + k_rd[kk]), qb[kk], s, 0, 0, 0);
-      if constexpr (EDGE) {
-  #pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const int key = s0 + 4 * grp + v;
-          if (key >= nvis || key < lo_c) s[v] = -INFINITY;
+      bf16x8 kop[NKK];
+#pragma unroll
+      for (int kk = 0; kk < NKK; ++kk) kop[kk] = *reinterpret_cast<const bf16x8*>(kw + k_rd[kk]);
+      bf16x4 pb[NG];
+#pragma unroll
+      for (int gi = 0; gi < NG; ++gi) {
+        floatx4 sc = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < NKK; ++kk) sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[kk], qb[gi][kk], sc, 0, 0, 0);
+        if constexpr (EDGE) {
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            const int key = s0 + 4 * grp + v;
+            if (key >= nvis[gi] || key < lo_c[gi]) sc[v] = -INFINITY;
+          }
         }
+        float bm = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
+        bm = xor16_max(bm);
+        bm = xor32_max(bm);
+        const float mn = fmaxf(m[gi], bm);
+        const float alpha = (m[gi] == -INFINITY) ? 0.f : fast_exp2((m[gi] - mn) * c);
+        const float mc = (mn == -INFINITY) ? 0.f : mn * c;   // a column with no key yet: p = 0
+        float p[4];
+#pragma unroll
+        for (int v = 0; v < 4; ++v) p[v] = fast_exp2(fmaf(sc[v], c, -mc));
+        lsum[gi] = lsum[gi] * alpha + ((p[0] + p[1]) + (p[2] + p[3]));
+        m[gi] = mn;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) pb[gi][v] = (__bf16)p[v];
+#pragma unroll
+        for (int tt = 0; tt < NT; ++tt) O[gi][tt] *= alpha;
       }
-      float bm = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
-      bm = xor16_max(bm);
-      bm = xor32_max(bm);
-      const float mn = fmaxf(m, bm);
-      const float alpha = (m == -INFINITY) ? 0.f : fast_exp2((m - mn) * c);
-      const float mc = (mn == -INFINITY) ? 0.f : mn * c;       // a column with no key yet: p = 0
-      float p[4];
-  #pragma unroll
-      for (int v = 0; v < 4; ++v) p[v] = fast_exp2(fmaf(s[v], c, -mc));
-      lsum = lsum * alpha + ((p[0] + p[1]) + (p[2] + p[3]));
-      m = mn;
-      bf16x4 pb;
-  #pragma unroll
-      for (int v = 0; v < 4; ++v) pb[v] = (__bf16)p[v];
-  #pragma unroll
-      for (int tt = 0; tt < NT; ++tt) O[tt] *= alpha;
       const char* vw = kw + VB;
       bf16x4 vt[NT];
-  #pragma unroll
+#pragma unroll
       for (int tt = 0; tt < NT; ++tt) vt[tt] = lds_read_tr(reinterpret_cast<const uint16_t*>(vw + tr_off[tt]));
       if constexpr (EDGE) {
         // rows no column may see (before the first window, past the last position) may hold poison
         // under p = 0: zero them
-  #pragma unroll
+#pragma unroll
         for (int tt = 0; tt < NT; ++tt)
-  #pragma unroll
+#pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int key = s0 + 4 * grp + e;
             if (key >= n_keys || key < lo_min) vt[tt][e] = (__bf16)0.f;
           }
       }
-  #pragma unroll
-      for (int tt = 0; tt < NT; ++tt) O[tt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vt[tt], pb, O[tt], 0, 0, 0);
+#pragma unroll
+      for (int gi = 0; gi < NG; ++gi)
+#pragma unroll
+        for (int tt = 0; tt < NT; ++tt)
+          O[gi][tt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vt[tt], pb[gi], O[gi][tt], 0, 0, 0);
     };
     auto consume = [&](int i, int slot) {
       const int s0 = (kb0 + i) * kBlock;
@@ -312,35 +331,37 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
       }
       consume(i, i & 1);
     }
-    lsum = xor16_sum(lsum);
-    lsum = xor32_sum(lsum);
 
     // this wave holds the whole split for its head: write each column's row or the split's partial
-    if (on) {
+#pragma unroll
+    for (int gi = 0; gi < NG; ++gi) {
+      float ls = xor16_sum(lsum[gi]);
+      ls = xor32_sum(ls);
+      if (!on[gi]) continue;
       if (n_splits == 1) {
-        const float inv = 1.f / lsum;
-        uint16_t* op = reinterpret_cast<uint16_t*>(a.out) + ((int64_t)(t0 + cr) * a.num_q_heads + h) * D;
-  #pragma unroll
+        const float inv = 1.f / ls;
+        uint16_t* op = reinterpret_cast<uint16_t*>(a.out) + ((int64_t)(t0 + cr[gi]) * a.num_q_heads + h[gi]) * D;
+#pragma unroll
         for (int tt = 0; tt < NT; ++tt) {
           uint2 pk;
-          pk.x = pack_bf16x2(O[tt][0] * inv, O[tt][1] * inv);
-          pk.y = pack_bf16x2(O[tt][2] * inv, O[tt][3] * inv);
+          pk.x = pack_bf16x2(O[gi][tt][0] * inv, O[gi][tt][1] * inv);
+          pk.y = pack_bf16x2(O[gi][tt][2] * inv, O[gi][tt][3] * inv);
           *reinterpret_cast<uint2*>(op + 16 * tt + 4 * grp) = pk;
         }
       } else {
-        const int64_t pidx = partial_index(a, row, cr, split, h);
+        const int64_t pidx = partial_index(a, row, cr[gi], split, h[gi]);
         float* po = a.part_o + pidx * D;
-  #pragma unroll
+#pragma unroll
         for (int tt = 0; tt < NT; ++tt)
-          *reinterpret_cast<float4*>(po + 16 * tt + 4 * grp) = make_float4(O[tt][0], O[tt][1], O[tt][2], O[tt][3]);
+          *reinterpret_cast<float4*>(po + 16 * tt + 4 * grp) =
+              make_float4(O[gi][tt][0], O[gi][tt][1], O[gi][tt][2], O[gi][tt][3]);
         if (grp == 0) {
-          a.part_ml[pidx * 2] = m * c;     // log2 units
-          a.part_ml[pidx * 2 + 1] = lsum;
+          a.part_ml[pidx * 2] = m[gi] * c;     // log2 units
+          a.part_ml[pidx * 2 + 1] = ls;
         }
       }
     }
   }
-
 }
 
 // ------------------------------------------------------------------------------------------
@@ -599,7 +620,9 @@ namespace {
 template <int D>
 hipError_t mfma_dispatch(const DecodeArgs& a, dim3 g, hipStream_t s) {
   if (a.heads_per_wg < 1 || a.heads_per_wg > 16) return hipErrorInvalidValue;   // 16 MFMA columns
-  decode_mfma_kernel<D><<<g, dim3(256), 0, s>>>(a);
+  // rows with more columns than one group holds carry two groups per pass over the keys
+  if ((int64_t)a.qmax * a.group > a.heads_per_wg) decode_mfma_kernel<D, 2><<<g, dim3(256), 0, s>>>(a);
+  else decode_mfma_kernel<D, 1><<<g, dim3(256), 0, s>>>(a);
   return hipGetLastError();
 }
 template <int D, bool BF16>
