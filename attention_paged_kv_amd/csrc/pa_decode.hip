@@ -107,11 +107,11 @@ __device__ __forceinline__ bool get_unit(const DecodeArgs& a, int nzh, Unit& u) 
 // V transpose reads are free of bank conflicts).  The copies are issued as inline assembly and
 // waited for with explicit vmcnt counts: with direct-to-LDS loads in view, the compiler waits for
 // every outstanding copy before an LDS read, which would wait for the next block's copies before
-// the current block is computed and leave no load in flight during the arithmetic.  The MFMA columns are (position, query head) pairs of the request: a decode
-// row has one position, a row of a few tokens to verify (P4 "一步的 token 预算": speculative
-// verification advances several tokens in one step) has q_len of them, each masked to its own
-// causal (and window) range, so the K/V of the request are read once for all of them.  Unused
-// columns are zero.
+// the current block is computed and leave no load in flight during the arithmetic.  The MFMA
+// columns are (position, query head) pairs of the request: a decode row has one position, a row of
+// a few tokens to verify (P4 "一步的 token 预算": speculative verification advances several tokens in
+// one step) has q_len of them, each masked to its own causal (and window) range, so the K/V of the
+// request are read once for all of them.  Unused columns are zero.
 // ------------------------------------------------------------------------------------------
 namespace {
 // Physical 16-byte chunk of logical chunk q in staged V row r is q ^ dswz<D>(r): a permutation of the
@@ -130,10 +130,11 @@ __device__ __forceinline__ int kswz(int r) {
 }
 }
 
-// NG column groups of 16 (position, head) columns are carried through one pass over the split's
-// keys (NG = 2 when a row has more than 16 columns, e.g. several tokens to verify on a grouped-query
-// model): K and V are read once for all of them.
-template <int D, int NG>
+// A row with more than 16 (position, head) columns (several tokens to verify on a grouped-query
+// model, or more than 16 query heads per KV head) carries two column groups of 16 through each pass
+// over the split's keys, so K and V are read once for 32 columns; the choice is made per workgroup
+// from its own row, and both forms are compiled into the kernel.
+template <int D>
 __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(DecodeArgs a) {
   constexpr int NKK = D / 32;                 // 16x16x32 k-steps over d for S^T
   constexpr int NT = D / 16;                  // 16-row d tiles of O^T
@@ -170,204 +171,210 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(DecodeArgs a) {
   const int g = 4 * quad + w;
   if (g >= a.num_kv_heads) return;                         // waves are independent: no barriers
 
-  const int lane = threadIdx.x & (kWave - 1);
-  const int col = lane & 15;                  // S^T / O^T column; also the K row read
-  const int grp = lane >> 4;                  // 4-key group of the accumulator layout
-  const float c = a.scale_log2;
   const int ncol_all = ql * a.group;          // (position, head) columns of the row
+  auto run = [&](auto ng_tag) {
+    constexpr int NG = decltype(ng_tag)::value;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int col = lane & 15;                  // S^T / O^T column; also the K row read
+    const int grp = lane >> 4;                  // 4-key group of the accumulator layout
+    const float c = a.scale_log2;
 
-  const int64_t rs = (int64_t)a.num_kv_heads * D;            // elements per cache token row
-  const int64_t blkbytes = kBlock * rs * 2;
-  const char* kbase = reinterpret_cast<const char*>(a.k_cache) + (int64_t)g * ROWB;
-  const char* vbase = reinterpret_cast<const char*>(a.v_cache) + (int64_t)g * ROWB;
-  const int32_t* table = a.block_tables + (int64_t)b * a.max_blocks;
-  const int kb0 = k0 / kBlock;
-  const int nb = (k1 + kBlock - 1) / kBlock - kb0;          // <= 64: splits are at most 1024 keys
-  const int ids = lane < nb ? table[kb0 + lane] : 0;         // lane i: id of the split's i-th block
+    const int64_t rs = (int64_t)a.num_kv_heads * D;            // elements per cache token row
+    const int64_t blkbytes = kBlock * rs * 2;
+    const char* kbase = reinterpret_cast<const char*>(a.k_cache) + (int64_t)g * ROWB;
+    const char* vbase = reinterpret_cast<const char*>(a.v_cache) + (int64_t)g * ROWB;
+    const int32_t* table = a.block_tables + (int64_t)b * a.max_blocks;
+    const int kb0 = k0 / kBlock;
+    const int nb = (k1 + kBlock - 1) / kBlock - kb0;          // <= 64: splits are at most 1024 keys
+    const int ids = lane < nb ? table[kb0 + lane] : 0;         // lane i: id of the split's i-th block
 
-  // K operand: key row `col`, d = 32kk + 8grp, i.e. logical chunk 4kk + grp of the staged row
-  uint32_t k_rd[NKK];
+    // K operand: key row `col`, d = 32kk + 8grp, i.e. logical chunk 4kk + grp of the staged row
+    uint32_t k_rd[NKK];
 #pragma unroll
-  for (int kk = 0; kk < NKK; ++kk) k_rd[kk] = col * ROWB + (((4 * kk + grp) ^ kswz<D>(col)) * 16);
-  // copies: copy i covers rows RPI*i ..; lane -> (row RPI*i + lane / CPR, physical chunk lane % CPR),
-  // which holds logical chunk (lane % CPR) ^ swz(row) of the cache row
-  uint32_t k_lane[IPB], v_lane[IPB];
+    for (int kk = 0; kk < NKK; ++kk) k_rd[kk] = col * ROWB + (((4 * kk + grp) ^ kswz<D>(col)) * 16);
+    // copies: copy i covers rows RPI*i ..; lane -> (row RPI*i + lane / CPR, physical chunk lane % CPR),
+    // which holds logical chunk (lane % CPR) ^ swz(row) of the cache row
+    uint32_t k_lane[IPB], v_lane[IPB];
 #pragma unroll
-  for (int i = 0; i < IPB; ++i) {
-    const int r = RPI * i + lane / CPR;
-    k_lane[i] = (uint32_t)(r * rs * 2) + (((lane % CPR) ^ kswz<D>(r)) * 16);
-    v_lane[i] = (uint32_t)(r * rs * 2) + (((lane % CPR) ^ dswz<D>(r)) * 16);
-  }
-  // transpose read: group grp, lane j = 4e + cq reads row 4grp + e, columns 16tt + 4cq .. +3,
-  // i.e. logical chunk 2tt + cq / 2, byte half cq & 1
-  uint32_t tr_off[NT];
+    for (int i = 0; i < IPB; ++i) {
+      const int r = RPI * i + lane / CPR;
+      k_lane[i] = (uint32_t)(r * rs * 2) + (((lane % CPR) ^ kswz<D>(r)) * 16);
+      v_lane[i] = (uint32_t)(r * rs * 2) + (((lane % CPR) ^ dswz<D>(r)) * 16);
+    }
+    // transpose read: group grp, lane j = 4e + cq reads row 4grp + e, columns 16tt + 4cq .. +3,
+    // i.e. logical chunk 2tt + cq / 2, byte half cq & 1
+    uint32_t tr_off[NT];
 #pragma unroll
-  for (int tt = 0; tt < NT; ++tt) {
-    const int r = 4 * grp + (col >> 2);
-    const int lq = 2 * tt + ((col & 3) >> 1);
-    tr_off[tt] = r * ROWB + ((lq ^ dswz<D>(r)) * 16) + (col & 1) * 8;
-  }
-
-  char* const mine = sKV + w * 2 * VB;                       // this wave's slot 0; slot 1 is 8 * VB on
-  auto issue = [&](int i, int slot) {                        // block kb0 + i: K and V into the slot
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");      // the slot's earlier reads are done
-    const char* kb = kbase + (int64_t)__builtin_amdgcn_readlane(ids, i) * blkbytes;
-    const char* vb = vbase + (kb - kbase);
-    const uint32_t l = __builtin_amdgcn_readfirstlane(lds_u32(mine + slot * 8 * VB));
-#pragma unroll
-    for (int j = 0; j < IPB; ++j) dma16(kb, k_lane[j], l + 1024 * j);
-#pragma unroll
-    for (int j = 0; j < IPB; ++j) dma16(vb, v_lane[j], l + VB + 1024 * j);
-  };
-
-  for (int zh = 0; zh * a.heads_per_wg < ncol_all; zh += NG) {
-    // this pass's columns: group gi holds columns (zh + gi) * heads_per_wg + col
-    bool on[NG];
-    int cr[NG], h[NG], nvis[NG], lo_c[NG];
-    bf16x8 qb[NG][NKK];                       // Q^T as the B operand: d = 32kk + 8grp .. +8
-#pragma unroll
-    for (int gi = 0; gi < NG; ++gi) {
-      const int c0 = (zh + gi) * a.heads_per_wg;
-      on[gi] = col < min(a.heads_per_wg, ncol_all - c0);
-      cr[gi] = on[gi] ? (c0 + col) / a.group : 0;            // this column's position in the request
-      h[gi] = g * a.group + (on[gi] ? (c0 + col) % a.group : 0);
-      nvis[gi] = ctx + cr[gi] + 1;                           // keys [lo_c, nvis) are this column's
-      lo_c[gi] = first_visible(a, nvis[gi]);
-      const char* qp = reinterpret_cast<const char*>(a.q) +
-                       (((int64_t)(t0 + cr[gi]) * a.num_q_heads + h[gi]) * D + 8 * grp) * 2;
-#pragma unroll
-      for (int kk = 0; kk < NKK; ++kk) {
-        const uint4 v = on[gi] ? *reinterpret_cast<const uint4*>(qp + kk * 64) : make_uint4(0, 0, 0, 0);
-        qb[gi][kk] = __builtin_bit_cast(bf16x8, v);
-      }
+    for (int tt = 0; tt < NT; ++tt) {
+      const int r = 4 * grp + (col >> 2);
+      const int lq = 2 * tt + ((col & 3) >> 1);
+      tr_off[tt] = r * ROWB + ((lq ^ dswz<D>(r)) * 16) + (col & 1) * 8;
     }
 
-    float m[NG], lsum[NG];
-    floatx4 O[NG][NT];
+    char* const mine = sKV + w * 2 * VB;                       // this wave's slot 0; slot 1 is 8 * VB on
+    auto issue = [&](int i, int slot) {                        // block kb0 + i: K and V into the slot
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");      // the slot's earlier reads are done
+      const char* kb = kbase + (int64_t)__builtin_amdgcn_readlane(ids, i) * blkbytes;
+      const char* vb = vbase + (kb - kbase);
+      const uint32_t l = __builtin_amdgcn_readfirstlane(lds_u32(mine + slot * 8 * VB));
 #pragma unroll
-    for (int gi = 0; gi < NG; ++gi) {
-      m[gi] = -INFINITY;
-      lsum[gi] = 0.f;
+      for (int j = 0; j < IPB; ++j) dma16(kb, k_lane[j], l + 1024 * j);
 #pragma unroll
-      for (int tt = 0; tt < NT; ++tt) O[gi][tt] = floatx4{0.f, 0.f, 0.f, 0.f};
-    }
+      for (int j = 0; j < IPB; ++j) dma16(vb, v_lane[j], l + VB + 1024 * j);
+    };
 
-    // one block.  EDGE blocks hold keys some column must not see -- before its window or after its
-    // position (the split's last blocks, and the first blocks of split 0 under a window).  The
-    // test is uniform across the wave and picks one of two compiled copies, so other blocks carry
-    // no masking at all.
-    auto consume_as = [&](auto edge_tag, int i, int slot) {
-      constexpr bool EDGE = decltype(edge_tag)::value;
-      const int s0 = (kb0 + i) * kBlock;
-      const char* kw = mine + slot * 8 * VB;
-      bf16x8 kop[NKK];
-#pragma unroll
-      for (int kk = 0; kk < NKK; ++kk) kop[kk] = *reinterpret_cast<const bf16x8*>(kw + k_rd[kk]);
-      bf16x4 pb[NG];
+    for (int zh = 0; zh * a.heads_per_wg < ncol_all; zh += NG) {
+      // this pass's columns: group gi holds columns (zh + gi) * heads_per_wg + col
+      bool on[NG];
+      int cr[NG], h[NG], nvis[NG], lo_c[NG];
+      bf16x8 qb[NG][NKK];                       // Q^T as the B operand: d = 32kk + 8grp .. +8
 #pragma unroll
       for (int gi = 0; gi < NG; ++gi) {
-        floatx4 sc = floatx4{0.f, 0.f, 0.f, 0.f};
+        const int c0 = (zh + gi) * a.heads_per_wg;
+        on[gi] = col < min(a.heads_per_wg, ncol_all - c0);
+        cr[gi] = on[gi] ? (c0 + col) / a.group : 0;            // this column's position in the request
+        h[gi] = g * a.group + (on[gi] ? (c0 + col) % a.group : 0);
+        nvis[gi] = ctx + cr[gi] + 1;                           // keys [lo_c, nvis) are this column's
+        lo_c[gi] = first_visible(a, nvis[gi]);
+        const char* qp = reinterpret_cast<const char*>(a.q) +
+                         (((int64_t)(t0 + cr[gi]) * a.num_q_heads + h[gi]) * D + 8 * grp) * 2;
 #pragma unroll
-        for (int kk = 0; kk < NKK; ++kk) sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[kk], qb[gi][kk], sc, 0, 0, 0);
+        for (int kk = 0; kk < NKK; ++kk) {
+          const uint4 v = on[gi] ? *reinterpret_cast<const uint4*>(qp + kk * 64) : make_uint4(0, 0, 0, 0);
+          qb[gi][kk] = __builtin_bit_cast(bf16x8, v);
+        }
+      }
+
+      float m[NG], lsum[NG];
+      floatx4 O[NG][NT];
+#pragma unroll
+      for (int gi = 0; gi < NG; ++gi) {
+        m[gi] = -INFINITY;
+        lsum[gi] = 0.f;
+#pragma unroll
+        for (int tt = 0; tt < NT; ++tt) O[gi][tt] = floatx4{0.f, 0.f, 0.f, 0.f};
+      }
+
+      // one block.  EDGE blocks hold keys some column must not see -- before its window or after its
+      // position (the split's last blocks, and the first blocks of split 0 under a window).  The
+      // test is uniform across the wave and picks one of two compiled copies, so other blocks carry
+      // no masking at all.
+      auto consume_as = [&](auto edge_tag, int i, int slot) {
+        constexpr bool EDGE = decltype(edge_tag)::value;
+        const int s0 = (kb0 + i) * kBlock;
+        const char* kw = mine + slot * 8 * VB;
+        bf16x8 kop[NKK];
+#pragma unroll
+        for (int kk = 0; kk < NKK; ++kk) kop[kk] = *reinterpret_cast<const bf16x8*>(kw + k_rd[kk]);
+        bf16x4 pb[NG];
+#pragma unroll
+        for (int gi = 0; gi < NG; ++gi) {
+          floatx4 sc = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int kk = 0; kk < NKK; ++kk)
+            sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[kk], qb[gi][kk], sc, 0, 0, 0);
+          if constexpr (EDGE) {
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+              const int key = s0 + 4 * grp + v;
+              if (key >= nvis[gi] || key < lo_c[gi]) sc[v] = -INFINITY;
+            }
+          }
+          float bm = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
+          bm = xor16_max(bm);
+          bm = xor32_max(bm);
+          const float mn = fmaxf(m[gi], bm);
+          const float alpha = (m[gi] == -INFINITY) ? 0.f : fast_exp2((m[gi] - mn) * c);
+          const float mc = (mn == -INFINITY) ? 0.f : mn * c;   // a column with no key yet: p = 0
+          float p[4];
+#pragma unroll
+          for (int v = 0; v < 4; ++v) p[v] = fast_exp2(fmaf(sc[v], c, -mc));
+          lsum[gi] = lsum[gi] * alpha + ((p[0] + p[1]) + (p[2] + p[3]));
+          m[gi] = mn;
+#pragma unroll
+          for (int v = 0; v < 4; ++v) pb[gi][v] = (__bf16)p[v];
+#pragma unroll
+          for (int tt = 0; tt < NT; ++tt) O[gi][tt] *= alpha;
+        }
+        const char* vw = kw + VB;
+        bf16x4 vt[NT];
+#pragma unroll
+        for (int tt = 0; tt < NT; ++tt) vt[tt] = lds_read_tr(reinterpret_cast<const uint16_t*>(vw + tr_off[tt]));
         if constexpr (EDGE) {
+          // rows no column may see (before the first window, past the last position) may hold poison
+          // under p = 0: zero them
 #pragma unroll
-          for (int v = 0; v < 4; ++v) {
-            const int key = s0 + 4 * grp + v;
-            if (key >= nvis[gi] || key < lo_c[gi]) sc[v] = -INFINITY;
-          }
+          for (int tt = 0; tt < NT; ++tt)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int key = s0 + 4 * grp + e;
+              if (key >= n_keys || key < lo_min) vt[tt][e] = (__bf16)0.f;
+            }
         }
-        float bm = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
-        bm = xor16_max(bm);
-        bm = xor32_max(bm);
-        const float mn = fmaxf(m[gi], bm);
-        const float alpha = (m[gi] == -INFINITY) ? 0.f : fast_exp2((m[gi] - mn) * c);
-        const float mc = (mn == -INFINITY) ? 0.f : mn * c;   // a column with no key yet: p = 0
-        float p[4];
 #pragma unroll
-        for (int v = 0; v < 4; ++v) p[v] = fast_exp2(fmaf(sc[v], c, -mc));
-        lsum[gi] = lsum[gi] * alpha + ((p[0] + p[1]) + (p[2] + p[3]));
-        m[gi] = mn;
+        for (int gi = 0; gi < NG; ++gi)
 #pragma unroll
-        for (int v = 0; v < 4; ++v) pb[gi][v] = (__bf16)p[v];
-#pragma unroll
-        for (int tt = 0; tt < NT; ++tt) O[gi][tt] *= alpha;
-      }
-      const char* vw = kw + VB;
-      bf16x4 vt[NT];
-#pragma unroll
-      for (int tt = 0; tt < NT; ++tt) vt[tt] = lds_read_tr(reinterpret_cast<const uint16_t*>(vw + tr_off[tt]));
-      if constexpr (EDGE) {
-        // rows no column may see (before the first window, past the last position) may hold poison
-        // under p = 0: zero them
-#pragma unroll
-        for (int tt = 0; tt < NT; ++tt)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int key = s0 + 4 * grp + e;
-            if (key >= n_keys || key < lo_min) vt[tt][e] = (__bf16)0.f;
-          }
-      }
-#pragma unroll
-      for (int gi = 0; gi < NG; ++gi)
-#pragma unroll
-        for (int tt = 0; tt < NT; ++tt)
-          O[gi][tt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vt[tt], pb[gi], O[gi][tt], 0, 0, 0);
-    };
-    auto consume = [&](int i, int slot) {
-      const int s0 = (kb0 + i) * kBlock;
-      if (s0 < lo_max || s0 + kBlock > ctx + 1) consume_as(std::true_type{}, i, slot);
-      else consume_as(std::false_type{}, i, slot);
-    };
+          for (int tt = 0; tt < NT; ++tt)
+            O[gi][tt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vt[tt], pb[gi], O[gi][tt], 0, 0, 0);
+      };
+      auto consume = [&](int i, int slot) {
+        const int s0 = (kb0 + i) * kBlock;
+        if (s0 < lo_max || s0 + kBlock > ctx + 1) consume_as(std::true_type{}, i, slot);
+        else consume_as(std::false_type{}, i, slot);
+      };
 
-    // one block in flight while the previous one is computed; the wait leaves exactly the next
-    // block's NCP copies outstanding (vector memory operations complete in issue order)
-    issue(0, 0);
-    for (int i = 0; i < nb; ++i) {
-      if (i + 1 < nb) {
-        issue(i + 1, (i + 1) & 1);
-        asm volatile("s_waitcnt vmcnt(%0)" :: "n"(NCP) : "memory");
-      } else {
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      }
-      consume(i, i & 1);
-    }
-
-    // this wave holds the whole split for its head: write each column's row or the split's partial
-#pragma unroll
-    for (int gi = 0; gi < NG; ++gi) {
-      float ls = xor16_sum(lsum[gi]);
-      ls = xor32_sum(ls);
-      if (!on[gi]) continue;
-      if (n_splits == 1) {
-        const float inv = 1.f / ls;
-        uint16_t* op = reinterpret_cast<uint16_t*>(a.out) + ((int64_t)(t0 + cr[gi]) * a.num_q_heads + h[gi]) * D;
-#pragma unroll
-        for (int tt = 0; tt < NT; ++tt) {
-          uint2 pk;
-          pk.x = pack_bf16x2(O[gi][tt][0] * inv, O[gi][tt][1] * inv);
-          pk.y = pack_bf16x2(O[gi][tt][2] * inv, O[gi][tt][3] * inv);
-          *reinterpret_cast<uint2*>(op + 16 * tt + 4 * grp) = pk;
+      // one block in flight while the previous one is computed; the wait leaves exactly the next
+      // block's NCP copies outstanding (vector memory operations complete in issue order)
+      issue(0, 0);
+      for (int i = 0; i < nb; ++i) {
+        if (i + 1 < nb) {
+          issue(i + 1, (i + 1) & 1);
+          asm volatile("s_waitcnt vmcnt(%0)" :: "n"(NCP) : "memory");
+        } else {
+          asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         }
-      } else {
-        const int64_t pidx = partial_index(a, row, cr[gi], split, h[gi]);
-        float* po = a.part_o + pidx * D;
+        consume(i, i & 1);
+      }
+
+      // this wave holds the whole split for its head: write each column's row or the split's partial
 #pragma unroll
-        for (int tt = 0; tt < NT; ++tt)
-          *reinterpret_cast<float4*>(po + 16 * tt + 4 * grp) =
-              make_float4(O[gi][tt][0], O[gi][tt][1], O[gi][tt][2], O[gi][tt][3]);
-        if (grp == 0) {
-          a.part_ml[pidx * 2] = m[gi] * c;     // log2 units
-          a.part_ml[pidx * 2 + 1] = ls;
+      for (int gi = 0; gi < NG; ++gi) {
+        float ls = xor16_sum(lsum[gi]);
+        ls = xor32_sum(ls);
+        if (!on[gi]) continue;
+        if (n_splits == 1) {
+          const float inv = 1.f / ls;
+          uint16_t* op = reinterpret_cast<uint16_t*>(a.out) + ((int64_t)(t0 + cr[gi]) * a.num_q_heads + h[gi]) * D;
+#pragma unroll
+          for (int tt = 0; tt < NT; ++tt) {
+            uint2 pk;
+            pk.x = pack_bf16x2(O[gi][tt][0] * inv, O[gi][tt][1] * inv);
+            pk.y = pack_bf16x2(O[gi][tt][2] * inv, O[gi][tt][3] * inv);
+            *reinterpret_cast<uint2*>(op + 16 * tt + 4 * grp) = pk;
+          }
+        } else {
+          const int64_t pidx = partial_index(a, row, cr[gi], split, h[gi]);
+          float* po = a.part_o + pidx * D;
+#pragma unroll
+          for (int tt = 0; tt < NT; ++tt)
+            *reinterpret_cast<float4*>(po + 16 * tt + 4 * grp) =
+                make_float4(O[gi][tt][0], O[gi][tt][1], O[gi][tt][2], O[gi][tt][3]);
+          if (grp == 0) {
+            a.part_ml[pidx * 2] = m[gi] * c;     // log2 units
+            a.part_ml[pidx * 2 + 1] = ls;
+          }
         }
       }
     }
-  }
+  };
+  if (ncol_all > a.heads_per_wg) run(std::integral_constant<int, 2>{});
+  else run(std::integral_constant<int, 1>{});
 }
 
 // ------------------------------------------------------------------------------------------
-// Vector-ALU split kernel for fp32 caches.  GT query heads per workgroup (GT divides the group size).  Each K/V row is read by a 16-lane
-// (bf16, d=128) row group with 16-byte loads; q.k is reduced across the group with DPP, and every
-// row group keeps its own running max / sum / accumulator.
+// Vector-ALU split kernel for fp32 caches.  GT query heads per workgroup (GT divides the group
+// size).  Each K/V row is read by a row group of lanes with 16-byte loads; q.k is reduced across the
+// group with DPP, and every row group keeps its own running max / sum / accumulator.
 // ------------------------------------------------------------------------------------------
 template <int D, int GT, bool BF16>
 __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeArgs a) {
@@ -620,9 +627,7 @@ namespace {
 template <int D>
 hipError_t mfma_dispatch(const DecodeArgs& a, dim3 g, hipStream_t s) {
   if (a.heads_per_wg < 1 || a.heads_per_wg > 16) return hipErrorInvalidValue;   // 16 MFMA columns
-  // rows with more columns than one group holds carry two groups per pass over the keys
-  if ((int64_t)a.qmax * a.group > a.heads_per_wg) decode_mfma_kernel<D, 2><<<g, dim3(256), 0, s>>>(a);
-  else decode_mfma_kernel<D, 1><<<g, dim3(256), 0, s>>>(a);
+  decode_mfma_kernel<D><<<g, dim3(256), 0, s>>>(a);
   return hipGetLastError();
 }
 template <int D, bool BF16>

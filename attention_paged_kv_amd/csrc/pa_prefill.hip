@@ -26,9 +26,9 @@
 // instead (finite data under a zero probability).  With a sliding window (P2 §5.2, P3 §6.3: only
 // the most recent W keys count) the key loop starts at the tile holding the first row's oldest
 // visible key, and tiles crossing the window's lower edge are masked as well; keys older than the
-// request's first window are never read (their blocks may be gone), a valid row stands in.  The running max is only moved (and O rescaled)
-// when some row's max grows by more than 2^8; between moves, probabilities may exceed 1 by at most
-// 2^8.
+// request's first window are never read (their blocks may be gone), a valid row stands in.  The
+// running max is only moved (and O rescaled) when some row's max grows by more than 2^8; between
+// moves, probabilities may exceed 1 by at most 2^8.
 //
 // 8-bit caches (P2 §4.3, §5.4: int8 codes with a scale per KV head and channel): the cache blocks
 // are copied to int8 staging buffers the same way, then the workgroup converts each tile once into
