@@ -173,8 +173,8 @@ int make_plan(int32_t B, int32_t T, int32_t MB, int32_t Hq, const pa_cache_desc*
   p.qmax = (c->dtype == PA_DTYPE_BF16) ? (longest < pa::kVerifyMax ? longest : pa::kVerifyMax) : 1;
   if (p.bf16) p.heads_per_wg = p.qmax * p.group < 16 ? p.qmax * p.group : 16;
   else p.heads_per_wg = (p.group % 8 == 0) ? 8 : (p.group % 4 == 0) ? 4 : (p.group % 2 == 0) ? 2 : 1;
-  if (p.bf16 && p.group > pa::kTileRows)
-    return fail(PA_ERR_UNSUPPORTED, "query heads per KV head (%d) above %d", p.group, pa::kTileRows);
+  if (p.bf16 && p.group > pa::kMaxTileGroup)
+    return fail(PA_ERR_UNSUPPORTED, "query heads per KV head (%d) above %d", p.group, pa::kMaxTileGroup);
   p.split = split_tokens();
   // a row's splits cover keys from the block holding its oldest visible key: at most
   // min(MB * 16, window + 15) keys

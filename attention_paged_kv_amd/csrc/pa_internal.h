@@ -10,7 +10,8 @@ namespace pa {
 // q_len == 1, and every query row of an fp32 batch run on the split-KV decode kernels; longer bf16
 // requests run on the MFMA tile kernel.
 constexpr int kDefaultSplitTokens = 256;   // keys per decode split (multiple of 16, at most 1024)
-constexpr int kTileRows = 128;             // query rows (position x head-in-group) per MFMA tile
+constexpr int kTileRows = 256;             // query rows (position x head-in-group) per prefill workgroup
+constexpr int kMaxTileGroup = 128;         // query heads per KV head the prefill tiles accept
 constexpr int kTileKeys = 64;              // keys per MFMA K/V tile
 constexpr int kNoWindow = 1 << 30;         // window value meaning "every earlier key"
 constexpr int kVerifyMax = 8;              // bf16 requests with q_len <= this run on the split-KV pass

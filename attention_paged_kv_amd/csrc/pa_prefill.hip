@@ -8,7 +8,8 @@
 // idea; the tiling here is CDNA4's own).  Arithmetic intensity is ~S FLOP/byte, so this part is a
 // dense contraction and runs on the matrix cores.
 //
-// Tile shape: 128 query rows x 64 keys per step, four waves of 32 rows.  A query row is a
+// Tile shape: 256 query rows x 64 keys per step, eight waves of 32 rows (two per SIMD, one
+// workgroup per CU), so each K/V tile staged in LDS serves 256 rows.  A query row is a
 // (position, query head) pair; the Hq/Hkv heads of one KV group are packed into the rows of the
 // same tile so that each K/V tile is loaded once for the whole group.  Per wave and key tile:
 //   S^T (64 keys x 32 rows) = K (64 x d) . Q^T (d x 32)     -- v_mfma_f32_32x32x16_bf16
@@ -50,7 +51,7 @@ __device__ __forceinline__ int swz(int r) {
 }  // namespace
 
 template <int D, bool KV8>
-__global__ __launch_bounds__(256, 2) void prefill_tile_kernel(TileArgs a) {
+__global__ __launch_bounds__(512, 1) void prefill_tile_kernel(TileArgs a) {
   constexpr int ESZ = KV8 ? 1 : 2;          // bytes per cache element
   constexpr int ROWB = D * 2;               // bytes per bf16 K/V row in LDS
   constexpr int CPR = D / 8;                // 16-byte chunks per row
@@ -132,9 +133,12 @@ __global__ __launch_bounds__(256, 2) void prefill_tile_kernel(TileArgs a) {
   const char* vbase = reinterpret_cast<const char*>(a.v_cache) + (int64_t)g * D * ESZ;
   const int32_t* table = a.block_tables + (int64_t)b * a.max_blocks;
 
-  // blocks of the request's wave: wave w visits blocks 4kt + w; those entirely below the length
-  // are taken from a window of table entries
-  const int n_full = (sl / kBlock - w + 3) / 4;   // count of kt with (4kt + w + 1) * 16 <= sl
+  // staging: waves 0-3 copy the tile's four K blocks, waves 4-7 its four V blocks; wave w takes
+  // block 4kt + (w & 3), and those entirely below the length come from a window of table entries
+  const int bw = w & 3;
+  const bool is_v = w >= 4;
+  const char* tbase = is_v ? vbase : kbase;
+  const int n_full = (sl / kBlock - bw + 3) / 4;  // count of kt with (4kt + bw + 1) * 16 <= sl
   BlockWindow win;
 
   float m_run = -INFINITY, l_run = 0.f;
@@ -250,42 +254,34 @@ __global__ __launch_bounds__(256, 2) void prefill_tile_kernel(TileArgs a) {
     __shared__ __align__(16) char sV0[TILEB];
     __shared__ __align__(16) char sK1[TILEB];
     __shared__ __align__(16) char sV1[TILEB];
-    // ---- staging: wave w loads key rows 16w..16w+15 of the tile (one cache block) ----
+    // ---- staging: the wave copies key rows 16bw..16bw+15 of its tensor's tile (one cache block) ----
     // load i of the block covers rows RPI*i .. RPI*i + RPI - 1; lane -> (row lane / CPR, physical
     // chunk lane % CPR), which holds logical chunk (lane % CPR) ^ swz(row).
     uint32_t lane_off[IPB];                         // byte offset within the block, per load
 #pragma unroll
     for (int i = 0; i < IPB; ++i) {
-      const int rr = RPI * i + lane / CPR;          // row within the block (and within the wave's 16)
-      const int q = (lane % CPR) ^ swz<D>(16 * w + rr);
+      const int rr = RPI * i + lane / CPR;          // row within the block
+      const int q = (lane % CPR) ^ swz<D>(16 * bw + rr);
       lane_off[i] = (uint32_t)(rr * rs * 2) + q * 16;
     }
     auto stage = [&](int kt, char* kdst, char* vdst) {
-      char* kl = kdst + 16 * w * ROWB;
-      char* vl = vdst + 16 * w * ROWB;
-      const int blk = 4 * kt + w;
+      char* dl = (is_v ? vdst : kdst) + 16 * bw * ROWB;
+      const int blk = 4 * kt + bw;
       if ((blk + 1) * kBlock <= sl && blk * kBlock >= lo_req) {   // whole block valid: one table entry
-        const int64_t boff = (int64_t)win.get(table, w, 4, n_full, kt) * (kBlock * rs * 2);
-        const char* kb = kbase + boff;               // uniform block base; lanes add 32-bit offsets
-        const char* vb = vbase + boff;
+        const char* tb = tbase + (int64_t)win.get(table, bw, 4, n_full, kt) * (kBlock * rs * 2);
 #pragma unroll
-        for (int i = 0; i < IPB; ++i) {
-          __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(kb + lane_off[i]),
-                                           (__attribute__((address_space(3))) void*)(kl + 1024 * i), 16, 0, 0);
-          __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(vb + lane_off[i]),
-                                           (__attribute__((address_space(3))) void*)(vl + 1024 * i), 16, 0, 0);
-        }
+        for (int i = 0; i < IPB; ++i)
+          __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(tb + lane_off[i]),
+                                           (__attribute__((address_space(3))) void*)(dl + 1024 * i), 16, 0, 0);
       } else {                                      // edge block: clamp rows into [lo_req, sl)
 #pragma unroll
         for (int i = 0; i < IPB; ++i) {
           const int rr = RPI * i + lane / CPR;
           const int j = min(max(blk * kBlock + rr, lo_req), sl - 1);
-          const int q = (lane % CPR) ^ swz<D>(16 * w + rr);
+          const int q = (lane % CPR) ^ swz<D>(16 * bw + rr);
           const int64_t off = (((int64_t)table[j >> 4] * kBlock + (j & 15)) * rs) * 2 + q * 16;
-          __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(kbase + off),
-                                           (__attribute__((address_space(3))) void*)(kl + 1024 * i), 16, 0, 0);
-          __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(vbase + off),
-                                           (__attribute__((address_space(3))) void*)(vl + 1024 * i), 16, 0, 0);
+          __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(tbase + off),
+                                           (__attribute__((address_space(3))) void*)(dl + 1024 * i), 16, 0, 0);
         }
       }
     };
@@ -319,7 +315,7 @@ __global__ __launch_bounds__(256, 2) void prefill_tile_kernel(TileArgs a) {
     __shared__ __align__(16) char sV8a[TILE8];
     __shared__ __align__(16) char sK8b[TILE8];
     __shared__ __align__(16) char sV8b[TILE8];
-    // staging: plain row-major int8 rows; load i of wave w's block covers rows RPI8*i + lane/CPR8
+    // staging: plain row-major int8 rows; load i of the wave's block covers rows RPI8*i + lane/CPR8
     uint32_t lane_off8[IPB8];
 #pragma unroll
     for (int i = 0; i < IPB8; ++i) {
@@ -327,51 +323,42 @@ __global__ __launch_bounds__(256, 2) void prefill_tile_kernel(TileArgs a) {
       lane_off8[i] = (uint32_t)(rr * rs) + (lane % CPR8) * 16;
     }
     auto stage8 = [&](int kt, char* kdst, char* vdst) {
-      char* kl = kdst + 16 * w * D;
-      char* vl = vdst + 16 * w * D;
-      const int blk = 4 * kt + w;
+      char* dl = (is_v ? vdst : kdst) + 16 * bw * D;
+      const int blk = 4 * kt + bw;
       if ((blk + 1) * kBlock <= sl && blk * kBlock >= lo_req) {
-        const int64_t boff = (int64_t)win.get(table, w, 4, n_full, kt) * (kBlock * rs);
+        const char* tb = tbase + (int64_t)win.get(table, bw, 4, n_full, kt) * (kBlock * rs);
 #pragma unroll
-        for (int i = 0; i < IPB8; ++i) {
-          __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(kbase + boff + lane_off8[i]),
-                                           (__attribute__((address_space(3))) void*)(kl + 1024 * i), 16, 0, 0);
-          __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(vbase + boff + lane_off8[i]),
-                                           (__attribute__((address_space(3))) void*)(vl + 1024 * i), 16, 0, 0);
-        }
+        for (int i = 0; i < IPB8; ++i)
+          __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(tb + lane_off8[i]),
+                                           (__attribute__((address_space(3))) void*)(dl + 1024 * i), 16, 0, 0);
       } else {                                    // edge block: clamp rows into [lo_req, sl)
 #pragma unroll
         for (int i = 0; i < IPB8; ++i) {
           const int rr = RPI8 * i + lane / CPR8;
           const int j = min(max(blk * kBlock + rr, lo_req), sl - 1);
           const int64_t off = ((int64_t)table[j >> 4] * kBlock + (j & 15)) * rs + (lane % CPR8) * 16;
-          __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(kbase + off),
-                                           (__attribute__((address_space(3))) void*)(kl + 1024 * i), 16, 0, 0);
-          __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(vbase + off),
-                                           (__attribute__((address_space(3))) void*)(vl + 1024 * i), 16, 0, 0);
+          __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(tbase + off),
+                                           (__attribute__((address_space(3))) void*)(dl + 1024 * i), 16, 0, 0);
         }
       }
     };
-    // conversion: thread -> (row tid / 4, quarter tid % 4 of its channels); 16 codes -> two bf16 chunks
-    const int crow = tid >> 2, cq = tid & 3;
+    // conversion: threads 0-255 widen K, 256-511 V (whole waves each); thread -> (row t / 4,
+    // quarter t % 4 of its channels); 16 codes -> two bf16 chunks
+    const int ct = tid & 255, crow = ct >> 2, cq = ct & 3;
+    char* const cdst = is_v ? sV : sK;
     auto convert = [&](const char* k8, const char* v8) {
+      const char* src = is_v ? v8 : k8;
 #pragma unroll
       for (int u = 0; u < D / 64; ++u) {
         const int c16 = (D / 64) * cq + u;                    // 16-code piece of the row
-        const uint4 xk = *reinterpret_cast<const uint4*>(k8 + crow * D + 16 * c16);
-        const uint4 xv = *reinterpret_cast<const uint4*>(v8 + crow * D + 16 * c16);
-        const uint32_t wk[4] = {xk.x, xk.y, xk.z, xk.w}, wv[4] = {xv.x, xv.y, xv.z, xv.w};
+        const uint4 x = *reinterpret_cast<const uint4*>(src + crow * D + 16 * c16);
+        const uint32_t wx[4] = {x.x, x.y, x.z, x.w};
 #pragma unroll
         for (int hq = 0; hq < 2; ++hq) {                      // logical bf16 chunk 2 * c16 + hq
-          bf16x8 ok, ov;
+          bf16x8 o;
 #pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            ok[e] = (__bf16)(float)(signed char)(wk[2 * hq + e / 4] >> (8 * (e & 3)));
-            ov[e] = (__bf16)(float)(signed char)(wv[2 * hq + e / 4] >> (8 * (e & 3)));
-          }
-          const int off = crow * ROWB + (((2 * c16 + hq) ^ swz<D>(crow)) * 16);
-          *reinterpret_cast<bf16x8*>(sK + off) = ok;
-          *reinterpret_cast<bf16x8*>(sV + off) = ov;
+          for (int e = 0; e < 8; ++e) o[e] = (__bf16)(float)(signed char)(wx[2 * hq + e / 4] >> (8 * (e & 3)));
+          *reinterpret_cast<bf16x8*>(cdst + crow * ROWB + (((2 * c16 + hq) ^ swz<D>(crow)) * 16)) = o;
         }
       }
     };
@@ -465,7 +452,7 @@ hipError_t launch_plan_tiles(const int32_t* qsl, int num_seqs, int pos_per_tile,
 hipError_t launch_prefill_tile(const TileArgs& a, int head_dim, bool kv8, hipStream_t s) {
   const int64_t grid = (int64_t)a.num_slots * a.num_kv_heads;
   if (grid <= 0 || grid > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
-  const dim3 g((unsigned)grid), blk(256);
+  const dim3 g((unsigned)grid), blk(512);
   if (head_dim == 128) {
     if (kv8) prefill_tile_kernel<128, true><<<g, blk, 0, s>>>(a);
     else prefill_tile_kernel<128, false><<<g, blk, 0, s>>>(a);
