@@ -74,6 +74,7 @@ struct DevState {
   void* ws = nullptr;
   size_t ws_bytes = 0;
   int* check = nullptr;
+  int cus = 0;            // compute units
 };
 std::mutex g_dev_mu;
 std::unordered_map<int, DevState> g_dev;
@@ -127,6 +128,8 @@ struct Plan {
   int head_dim = 0, group = 0, heads_per_wg = 0;
   bool run_decode = false, run_tiles = false;
   int rows = 0, per_token = 0, qmax = 1, split = 0, max_splits = 0;
+  bool stream = false;    // bf16 cache, rows of several positions: balanced runs instead of splits
+  int span_blocks = 0;    // most 16-key blocks one row's decode pass covers
   int pos_per_tile = 0, num_slots = 0;
   size_t off_o = 0, off_ml = 0, off_tiles = 0, off_ntiles = 0, total = 0;
 };
@@ -176,10 +179,24 @@ int make_plan(int32_t B, int32_t T, int32_t MB, int32_t Hq, const pa_cache_desc*
   if (p.bf16 && p.group > pa::kMaxTileGroup)
     return fail(PA_ERR_UNSUPPORTED, "query heads per KV head (%d) above %d", p.group, pa::kMaxTileGroup);
   p.split = split_tokens();
-  // a row's splits cover keys from the block holding its oldest visible key: at most
-  // min(MB * 16, window + 15) keys
-  const int64_t span = std::min<int64_t>((int64_t)MB * PA_BLOCK_SIZE, (int64_t)window + PA_BLOCK_SIZE - 1);
-  p.max_splits = (int)((span + p.split - 1) / p.split);
+  // A row's pass covers keys from the block holding the oldest key its first position sees (that
+  // position's window reaches qmax - 1 keys further back than the last one's) to its last key:
+  // at most min(MB * 16, window + qmax - 1 + 15) keys, and min(MB, ceil((window + qmax - 1) / 16) + 1)
+  // blocks.
+  const int64_t reach = (int64_t)window + p.qmax - 1;
+  const int64_t span = std::min<int64_t>((int64_t)MB * PA_BLOCK_SIZE, reach + PA_BLOCK_SIZE - 1);
+  p.span_blocks = (int)std::min<int64_t>(MB, (reach + PA_BLOCK_SIZE - 1) / PA_BLOCK_SIZE + 1);
+  // Rows of several positions (verification) make uneven work per split (more columns on some
+  // rows, longer merges); they are dealt out in balanced runs.  Plain decode rows measure best on
+  // fixed splits, which the hardware schedules dynamically.
+  p.stream = c->dtype == PA_DTYPE_BF16 && p.qmax > 1;
+  if (p.stream) {
+    // a row meets at most ceil(blocks / run) + 1 runs, and runs hold at least `split` keys
+    p.max_splits = (int)(((int64_t)p.span_blocks * PA_BLOCK_SIZE + p.split - 1) / p.split) + 1;
+    if ((int64_t)B * p.span_blocks > 0x7FFFFFFF) return fail(PA_ERR_UNSUPPORTED, "batch too large for one launch");
+  } else {
+    p.max_splits = (int)((span + p.split - 1) / p.split);
+  }
   if (p.bf16) {
     p.per_token = 0;
     p.rows = B;
@@ -211,13 +228,42 @@ int make_plan(int32_t B, int32_t T, int32_t MB, int32_t Hq, const pa_cache_desc*
   const int64_t nzh = ((int64_t)p.qmax * p.group + p.heads_per_wg - 1) / p.heads_per_wg;
   const int64_t heads = p.bf16 ? (c->num_kv_heads + 3) / 4 : c->num_kv_heads;
   const int64_t dec_grid = heads * nzh * p.max_splits * p.rows;
-  if (p.run_decode && dec_grid > 0x7FFFFFFF) return fail(PA_ERR_UNSUPPORTED, "batch too large for one launch");
+  if (p.run_decode && !p.stream && dec_grid > 0x7FFFFFFF) return fail(PA_ERR_UNSUPPORTED, "batch too large for one launch");
   return PA_OK;
 }
 
 int get_device(int& dev) {
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return device_fail(e, "hipGetDevice");
+  return PA_OK;
+}
+
+// Stream-mode workgroups per four KV heads: the decode kernel keeps two workgroups resident per
+// compute unit, so two per CU over all head quads make one full wave of the chip; never more than
+// the rows' blocks fill with runs of `split` keys.  PA_DECODE_WGS overrides the chip-wide count.
+int stream_wgs(const Plan& p, int num_kv_heads, int& out) {
+  int dev = 0;
+  int rc = get_device(dev);
+  if (rc) return rc;
+  int cus = 0;
+  {
+    std::lock_guard<std::mutex> lk(g_dev_mu);
+    cus = g_dev[dev].cus;
+  }
+  if (cus == 0) {
+    hipError_t e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess || cus < 1) return device_fail(e != hipSuccess ? e : hipErrorInvalidValue, "compute unit count");
+    std::lock_guard<std::mutex> lk(g_dev_mu);
+    g_dev[dev].cus = cus;
+  }
+  static const int over = [] {
+    const char* e = std::getenv("PA_DECODE_WGS");
+    return e ? std::atoi(e) : 0;
+  }();
+  const int64_t nq = (num_kv_heads + 3) / 4;
+  const int64_t chip = over > 0 ? over : 2 * (int64_t)cus;
+  const int64_t fill = ((int64_t)p.rows * p.span_blocks * PA_BLOCK_SIZE + p.split - 1) / p.split;
+  out = (int)std::max<int64_t>(1, std::min<int64_t>(std::max<int64_t>(1, chip / nq), fill));
   return PA_OK;
 }
 
@@ -411,6 +457,11 @@ int pa_attention_ex(const void* q, int32_t num_q_tokens, int32_t num_q_heads, co
     d.max_blocks = max_blocks_per_seq;
     d.split = p.split;
     d.max_splits = p.max_splits;
+    d.stream_wgs = 0;
+    if (p.stream) {
+      rc = stream_wgs(p, cache->num_kv_heads, d.stream_wgs);
+      if (rc) return rc;
+    }
     d.window = window;
     d.scale_log2 = scale_log2;
     d.k_scale = cache->k_scale;

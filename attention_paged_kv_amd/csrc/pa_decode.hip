@@ -9,6 +9,9 @@
 //   m = max_s m_s,  l = sum_s 2^(m_s - m) l_s,  o = sum_s 2^(m_s - m) o_s / l
 // (scores are kept in log2 units: x * scale * log2 e).  The pages do not describe how partial
 // softmaxes combine; this is the exact decomposition of the row softmax of P3 §3.1.
+// Batches whose rows may carry several positions (tokens to verify) are instead dealt out in
+// equal runs of blocks across all rows (stream mode, pa_rows.h); a run's piece of a row is merged
+// exactly like a split.
 //
 // bf16 caches: matrix cores do the arithmetic so that the vector ALUs stay idle however many
 // query heads share a KV head.  Per 16-key block and wave:
@@ -130,11 +133,23 @@ __device__ __forceinline__ int kswz(int r) {
 }
 }
 
+namespace {
+// Lane i (active lanes only) loads p[i] and waits for it, in inline assembly: a load the compiler
+// sees inside the block loop makes it wait for every outstanding copy on every block thereafter.
+__device__ __forceinline__ int load_ids_sync(const int32_t* p, int count) {
+  int v = 0;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int32_t* q = p + lane;
+  if (lane < count) asm volatile("global_load_dword %0, %1, off\n\ts_waitcnt vmcnt(0)" : "=v"(v) : "v"(q) : "memory");
+  return v;
+}
+}  // namespace
+
 // A row with more than 16 (position, head) columns (several tokens to verify on a grouped-query
 // model, or more than 16 query heads per KV head) carries two column groups of 16 through each pass
 // over the split's keys, so K and V are read once for 32 columns; the choice is made per workgroup
 // from its own row, and both forms are compiled into the kernel.
-template <int D>
+template <int D, bool STREAM>
 __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(DecodeArgs a) {
   constexpr int NKK = D / 32;                 // 16x16x32 k-steps over d for S^T
   constexpr int NT = D / 16;                  // 16-row d tiles of O^T
@@ -146,32 +161,17 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(DecodeArgs a) {
   constexpr int NCP = 2 * IPB;                // copies per block (K and V)
   __shared__ __align__(16) char sKV[2 * 4 * 2 * VB];   // [slot][wave][K block, V block]
 
-  // unit: (row, split, head quad), the quad fastest; the wave's KV head is 4 * quad + w.  A row
-  // with more (position, head) columns than NG MFMAs hold runs its column groups NG at a time in
-  // the same workgroup (the K/V re-read comes straight after the first pass), so the grid has no
-  // workgroups that find nothing to do.
+  // unit: (row, split) -- or, in stream mode, run pw of the concatenated blocks of all rows, taken
+  // as one piece per row it meets -- for head quad `quad` (the quad fastest); the wave's KV head is
+  // 4 * quad + w.  A row with more (position, head) columns than NG MFMAs hold runs its column
+  // groups NG at a time in the same workgroup (the K/V re-read comes straight after the first pass).
   const int nq = (a.num_kv_heads + 3) / 4;
-  int ib = blockIdx.x;
-  const int quad = ib % nq;
-  ib /= nq;
-  const int split = ib % a.max_splits;
-  const int row = ib / a.max_splits;
-  if (row >= a.num_rows) return;
-  int b, t0, n_keys, ql;
-  if (!resolve_row(a, row, b, t0, n_keys, ql)) return;
-  const int ctx = n_keys - ql;                             // keys before the request's first position
-  const int lo_min = first_visible(a, ctx + 1);            // oldest key any position sees
-  const int lo_max = first_visible(a, n_keys);             // oldest key the last position sees
-  const int kbeg = lo_min & ~(kBlock - 1);
-  const int k0 = kbeg + split * a.split;
-  if (k0 >= n_keys) return;
-  const int k1 = min(k0 + a.split, n_keys);
-  const int n_splits = (n_keys - kbeg + a.split - 1) / a.split;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int quad = blockIdx.x % nq;
   const int g = 4 * quad + w;
   if (g >= a.num_kv_heads) return;                         // waves are independent: no barriers
+  int row, split, b, t0, n_keys, ql, ctx, lo_min, lo_max, k0, k1, n_splits, ncol_all;
 
-  const int ncol_all = ql * a.group;          // (position, head) columns of the row
   auto run = [&](auto ng_tag) {
     constexpr int NG = decltype(ng_tag)::value;
     const int lane = threadIdx.x & (kWave - 1);
@@ -185,8 +185,8 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(DecodeArgs a) {
     const char* vbase = reinterpret_cast<const char*>(a.v_cache) + (int64_t)g * ROWB;
     const int32_t* table = a.block_tables + (int64_t)b * a.max_blocks;
     const int kb0 = k0 / kBlock;
-    const int nb = (k1 + kBlock - 1) / kBlock - kb0;          // <= 64: splits are at most 1024 keys
-    const int ids = lane < nb ? table[kb0 + lane] : 0;         // lane i: id of the split's i-th block
+    const int nb = (k1 + kBlock - 1) / kBlock - kb0;
+    int ids = 0, ids_base = -kWave;                            // lane i: id of block ids_base + i
 
     // K operand: key row `col`, d = 32kk + 8grp, i.e. logical chunk 4kk + grp of the staged row
     uint32_t k_rd[NKK];
@@ -214,7 +214,11 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(DecodeArgs a) {
     char* const mine = sKV + w * 2 * VB;                       // this wave's slot 0; slot 1 is 8 * VB on
     auto issue = [&](int i, int slot) {                        // block kb0 + i: K and V into the slot
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");      // the slot's earlier reads are done
-      const char* kb = kbase + (int64_t)__builtin_amdgcn_readlane(ids, i) * blkbytes;
+      if (i - ids_base >= kWave) {                             // next 64 ids (once per 64 blocks)
+        ids_base = i;
+        ids = load_ids_sync(table + kb0 + i, nb - i);
+      }
+      const char* kb = kbase + (int64_t)__builtin_amdgcn_readlane(ids, i - ids_base) * blkbytes;
       const char* vb = vbase + (kb - kbase);
       const uint32_t l = __builtin_amdgcn_readfirstlane(lds_u32(mine + slot * 8 * VB));
 #pragma unroll
@@ -244,6 +248,9 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(DecodeArgs a) {
           qb[gi][kk] = __builtin_bit_cast(bf16x8, v);
         }
       }
+      // wait for Q here, where nothing else is in flight: left to itself the compiler may put this
+      // wait (a full vmcnt(0)) inside the block loop, where it would also wait for the next block
+      __builtin_amdgcn_s_waitcnt(0x0F70);       // vmcnt(0) only
 
       float m[NG], lsum[NG];
       floatx4 O[NG][NT];
@@ -367,8 +374,55 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(DecodeArgs a) {
       }
     }
   };
-  if (ncol_all > a.heads_per_wg) run(std::integral_constant<int, 2>{});
-  else run(std::integral_constant<int, 1>{});
+  // row fields the unit needs, once (row, keys [k0, k1), piece index and count) are set
+  auto setup = [&]() {
+    resolve_row(a, row, b, t0, n_keys, ql);
+    ctx = n_keys - ql;                                     // keys before the request's first position
+    lo_min = first_visible(a, ctx + 1);                    // oldest key any position sees
+    lo_max = first_visible(a, n_keys);                     // oldest key the last position sees
+    ncol_all = ql * a.group;                               // (position, head) columns of the row
+  };
+  auto go = [&]() {
+    if (ncol_all > a.heads_per_wg) run(std::integral_constant<int, 2>{});
+    else run(std::integral_constant<int, 1>{});
+  };
+  if constexpr (STREAM) {
+    const int pw = blockIdx.x / nq;
+    int unused0, unused1;
+    const int tot = stream_scan(a, -1, unused0, unused1);
+    const int run_len = stream_run(a, tot);
+    if ((int64_t)pw * run_len >= tot) return;
+    const int gbeg = pw * run_len;
+    const int gend = (int)min<int64_t>((int64_t)gbeg + run_len, tot);
+    BlockCursor cur;
+    for (int gb = gbeg; gb < gend;) {
+      int pre, nbr;
+      if (!cur.seek(a, gb, row, pre, nbr)) break;
+      const int seg_end = min(gend, pre + nbr);
+      setup();
+      const int kbeg = lo_min & ~(kBlock - 1);
+      k0 = kbeg + kBlock * (gb - pre);
+      k1 = min(kbeg + kBlock * (seg_end - pre), n_keys);
+      split = pw - pre / run_len;                          // this piece's index among the row's
+      n_splits = stream_pieces(pre, nbr, run_len);
+      gb = seg_end;
+      go();
+    }
+  } else {
+    const int ib = blockIdx.x / nq;
+    split = ib % a.max_splits;
+    row = ib / a.max_splits;
+    if (row >= a.num_rows) return;
+    int b_, t_, n_, q_;
+    if (!resolve_row(a, row, b_, t_, n_, q_)) return;
+    setup();
+    const int kbeg = lo_min & ~(kBlock - 1);
+    k0 = kbeg + split * a.split;
+    if (k0 >= n_keys) return;
+    k1 = min(k0 + a.split, n_keys);
+    n_splits = (n_keys - kbeg + a.split - 1) / a.split;
+    go();
+  }
 }
 
 // ------------------------------------------------------------------------------------------
@@ -559,7 +613,14 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a) {
   int b, t0, n_keys, ql;
   if (!resolve_row(a, row, b, t0, n_keys, ql) || r >= ql) return;
   const int t = t0 + r;
-  const int n = (n_keys - split_origin(a, n_keys, ql) + a.split - 1) / a.split;
+  int n;
+  if (a.stream_wgs > 0) {
+    int pre, nb;
+    const int tot = stream_scan(a, row, pre, nb);
+    n = stream_pieces(pre, nb, stream_run(a, tot));
+  } else {
+    n = (n_keys - split_origin(a, n_keys, ql) + a.split - 1) / a.split;
+  }
   if (n <= 1) return;                                       // written directly by the split kernel
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1), w = tid >> 6;
@@ -627,7 +688,8 @@ namespace {
 template <int D>
 hipError_t mfma_dispatch(const DecodeArgs& a, dim3 g, hipStream_t s) {
   if (a.heads_per_wg < 1 || a.heads_per_wg > 16) return hipErrorInvalidValue;   // 16 MFMA columns
-  decode_mfma_kernel<D><<<g, dim3(256), 0, s>>>(a);
+  if (a.stream_wgs > 0) decode_mfma_kernel<D, true><<<g, dim3(256), 0, s>>>(a);
+  else decode_mfma_kernel<D, false><<<g, dim3(256), 0, s>>>(a);
   return hipGetLastError();
 }
 template <int D, bool BF16>
@@ -647,8 +709,10 @@ hipError_t valu_dispatch(const DecodeArgs& a, dim3 g, hipStream_t s) {
 hipError_t launch_decode_split(const DecodeArgs& a, int head_dim, bool bf16, hipStream_t s) {
   const int64_t nzh = ((int64_t)a.qmax * a.group + a.heads_per_wg - 1) / a.heads_per_wg;
   const int64_t heads = bf16 ? (a.num_kv_heads + 3) / 4 : a.num_kv_heads;   // MFMA: 4 KV heads per WG
-  // MFMA: column groups loop inside the workgroup; fp32: one workgroup per group
-  const int64_t grid = heads * (bf16 ? 1 : nzh) * a.max_splits * a.num_rows;
+  // MFMA: one workgroup per (row, split) or stream_wgs runs, per head quad, column groups looping
+  // inside the workgroup; fp32: one workgroup per (row, split, column group)
+  const int64_t grid = bf16 ? heads * (a.stream_wgs > 0 ? a.stream_wgs : a.max_splits * a.num_rows)
+                            : heads * nzh * a.max_splits * a.num_rows;
   if (grid <= 0 || grid > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
   const dim3 g((unsigned)grid);
   if (bf16) {

@@ -47,8 +47,9 @@ struct DecodeArgs {
   int group;              // Hq / Hkv
   int heads_per_wg;       // columns per workgroup: (position, query head) pairs of one KV head
   int max_blocks;
-  int split;              // keys per split
-  int max_splits;
+  int split;              // keys per split (stream mode: fewest keys per run)
+  int max_splits;         // partial slots per (row, position, head): splits, or pieces in stream mode
+  int stream_wgs;         // > 0: stream mode with this many workgroups per four KV heads; 0: splits
   int window;             // keys a row sees, its own included (kNoWindow: all earlier keys)
   float scale_log2;       // scale * log2(e)
   const float* k_scale;   // int8 caches: [Hkv][d]

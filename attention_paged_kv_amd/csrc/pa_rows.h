@@ -39,6 +39,81 @@ __device__ __forceinline__ int split_origin(const DecodeArgs& a, int n_keys, int
   return first_visible(a, n_keys - ql + 1) & ~(kBlock - 1);
 }
 
+// ---- stream mode (bf16 decode) ----
+// The 16-key blocks that the rows' passes cover, concatenated in row order, are dealt out in equal
+// runs of L blocks to stream_wgs workgroups per four KV heads.  A run may end one row and begin the
+// next; each (row, run) piece is a partial softmax of the row, like a split, and a row's pieces
+// are merged as splits are.  Every workgroup reads the same number of blocks, so the launch has
+// no tail of workgroups still running while the rest of the chip idles.
+
+// Inclusive prefix sum across the wave.
+__device__ __forceinline__ int wave_incl_scan(int x) {
+  const int lane = threadIdx.x & (kWave - 1);
+#pragma unroll
+  for (int d = 1; d < kWave; d <<= 1) {
+    const int y = __shfl_up(x, d, kWave);
+    if (lane >= d) x += y;
+  }
+  return x;
+}
+
+// Blocks a row's pass covers: from the block holding the oldest key its first position sees to
+// the block holding its last key; 0 for rows that are not on this pass.
+__device__ __forceinline__ int row_blocks(const DecodeArgs& a, int row) {
+  int b, t, n_keys, ql;
+  if (row >= a.num_rows || !resolve_row(a, row, b, t, n_keys, ql) || n_keys < 1) return 0;
+  return (n_keys + kBlock - 1) / kBlock - first_visible(a, n_keys - ql + 1) / kBlock;
+}
+
+// Blocks of all rows (the wave's lanes take 64 rows at a time); for row `want` also the blocks
+// before it (pre) and its own (nb).
+__device__ __forceinline__ int stream_scan(const DecodeArgs& a, int want, int& pre, int& nb) {
+  const int lane = threadIdx.x & (kWave - 1);
+  int base = 0;
+  pre = 0;
+  nb = 0;
+  for (int c0 = 0; c0 < a.num_rows; c0 += kWave) {
+    const int v = row_blocks(a, c0 + lane);
+    const int incl = wave_incl_scan(v);
+    if (want >= c0 && want < c0 + kWave) {
+      pre = base + __builtin_amdgcn_readlane(incl - v, want - c0);
+      nb = __builtin_amdgcn_readlane(v, want - c0);
+    }
+    base += __builtin_amdgcn_readlane(incl, kWave - 1);
+  }
+  return base;
+}
+
+// Blocks per run, given the total: an equal share, but at least `split` keys.
+__device__ __forceinline__ int stream_run(const DecodeArgs& a, int tot) {
+  return max((int)(((int64_t)tot + a.stream_wgs - 1) / a.stream_wgs), a.split / kBlock);
+}
+
+// Pieces of a row whose blocks are [pre, pre + nb) of the concatenation: the runs it meets.
+__device__ __forceinline__ int stream_pieces(int pre, int nb, int run) {
+  return nb < 1 ? 0 : (pre + nb - 1) / run - pre / run + 1;
+}
+
+// Walks the concatenation: the row holding block g, for g increasing.
+struct BlockCursor {
+  int c0 = -kWave, base = 0, tot = 0, incl = 0, v = 0;
+  __device__ bool seek(const DecodeArgs& a, int g, int& row, int& pre, int& nb) {
+    while (c0 < 0 || g >= base + tot) {
+      if (c0 + kWave >= a.num_rows) return false;        // g is past the last row
+      if (c0 >= 0) base += tot;
+      c0 += kWave;
+      v = row_blocks(a, c0 + (int)(threadIdx.x & (kWave - 1)));
+      incl = wave_incl_scan(v);
+      tot = __builtin_amdgcn_readlane(incl, kWave - 1);
+    }
+    const int j = __popcll(__ballot(incl <= g - base));   // rows wholly before block g
+    row = c0 + j;
+    pre = base + __builtin_amdgcn_readlane(incl - v, j);
+    nb = __builtin_amdgcn_readlane(v, j);
+    return true;
+  }
+};
+
 // Index of the split partial of (row, position r, split, query head h).
 __device__ __forceinline__ int64_t partial_index(const DecodeArgs& a, int row, int r, int split, int h) {
   return (((int64_t)row * a.qmax + r) * a.max_splits + split) * a.num_q_heads + h;

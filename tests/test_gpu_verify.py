@@ -44,6 +44,11 @@ CASES = [
     ([3000, 777, 64], [4, 8, 2], 32, 8, 128, 17),
     ([500, 500], [8, 8], 8, 2, 128, 1),
     ([9000], [8], 32, 8, 128, 0),
+    # the first position's window reaches q_len - 1 keys further back than the last one's: with
+    # W = 238 and q_len 8 a row's pass spans up to 260 keys, past one 256-key run
+    ([3000, 1243, 250, 5000], [8, 8, 7, 8], 32, 8, 128, 238),
+    # more than 64 rows: the run cursor walks several 64-row chunks of the batch
+    ([100 + 37 * i for i in range(70)], [1 + i % 4 for i in range(70)], 8, 2, 128, 0),
 ]
 
 
