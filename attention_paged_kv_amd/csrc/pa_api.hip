@@ -109,13 +109,18 @@ hipError_t timed(const char* name, hipStream_t s, F&& launch) {
     return launch();
   }
   hipEvent_t a = take_event(), b = take_event();
-  if (!a || !b) return hipErrorOutOfMemory;
-  hipError_t e = hipEventRecord(a, s);
-  if (e != hipSuccess) return e;
-  e = launch();
-  const hipError_t eb = hipEventRecord(b, s);
-  if (e == hipSuccess) e = eb;
-  if (e == hipSuccess) g_pending.push_back({name, a, b});
+  hipError_t e = (a && b) ? hipEventRecord(a, s) : hipErrorOutOfMemory;
+  if (e == hipSuccess) {
+    e = launch();
+    const hipError_t eb = hipEventRecord(b, s);
+    if (e == hipSuccess) e = eb;
+  }
+  if (e == hipSuccess) {
+    g_pending.push_back({name, a, b});
+  } else {                                  // keep the events for later launches
+    if (a) g_event_pool.push_back(a);
+    if (b) g_event_pool.push_back(b);
+  }
   return e;
 }
 
