@@ -173,12 +173,12 @@ int make_plan(int32_t B, int32_t T, int32_t MB, int32_t Hq, const pa_cache_desc*
   p.bf16 = c->dtype == PA_DTYPE_BF16 || p.i8;
   p.head_dim = c->head_dim;
   p.group = Hq / c->num_kv_heads;
-  // A bf16 request row carries up to qmax positions: min(kVerifyMax, the longest q_len the sizes
-  // allow); int8 and fp32 rows carry one.  bf16 decode holds up to 16 (position, query head)
-  // columns of a KV head per wave (the MFMA column count); the fp32 vector-ALU decode holds a
-  // divisor of the group size up to 8.
+  // A request row of bf16 activations (bf16 or int8 cache) carries up to qmax positions:
+  // min(kVerifyMax, the longest q_len the sizes allow); fp32 rows carry one.  The matrix-core
+  // decode kernels hold up to 16 (position, query head) columns of a KV head per wave (the MFMA
+  // column count); the fp32 vector-ALU decode holds a divisor of the group size up to 8.
   const int longest = T - B + 1;
-  p.qmax = (c->dtype == PA_DTYPE_BF16) ? (longest < pa::kVerifyMax ? longest : pa::kVerifyMax) : 1;
+  p.qmax = p.bf16 ? (longest < pa::kVerifyMax ? longest : pa::kVerifyMax) : 1;
   if (p.bf16) p.heads_per_wg = p.qmax * p.group < 16 ? p.qmax * p.group : 16;
   else p.heads_per_wg = (p.group % 8 == 0) ? 8 : (p.group % 4 == 0) ? 4 : (p.group % 2 == 0) ? 2 : 1;
   if (p.bf16 && p.group > pa::kMaxTileGroup)

@@ -1,4 +1,5 @@
-// pa_decode_i8.hip -- split-KV attention for single query rows over an 8-bit cache.
+// pa_decode_i8.hip -- split-KV attention for decode rows (and rows of a few tokens to verify) over
+// an 8-bit cache.
 //
 // The cache holds int8 codes with one fp32 scale per (KV head, channel) for K and for V (P2 §4.3
 // and §5.4: INT8 halves the bytes a decode step must read; calibration is per channel).  The pass
@@ -103,8 +104,11 @@ __global__ __launch_bounds__(64 * NW, 2) void decode_i8_kernel(DecodeArgs a) {
   constexpr int NCP = 4 * IPB;                // copies per unit (two blocks of K and of V)
   __shared__ __align__(16) char sKV[2 * NW * 2 * UB];   // [slot][wave][K unit, V unit]
 
-  // unit: (row, split, head group, query-head column group); the wave's KV head is NW * group + w
-  const int nzh = (a.group + a.heads_per_wg - 1) / a.heads_per_wg;
+  // unit: (row, split, head group, column group); the wave's KV head is NW * group + w.  Columns
+  // are the row's (position, query head) pairs of that KV head, heads_per_wg of them per group: a
+  // decode row has one position, a row of tokens to verify q_len <= qmax of them, each column
+  // masked to its own causal (and window) range.
+  const int nzh = (a.qmax * a.group + a.heads_per_wg - 1) / a.heads_per_wg;
   const int nq = (a.num_kv_heads + NW - 1) / NW;
   const int nz = nq * nzh;
   int ib = blockIdx.x;
@@ -114,9 +118,11 @@ __global__ __launch_bounds__(64 * NW, 2) void decode_i8_kernel(DecodeArgs a) {
   const int row = ib / a.max_splits;
   if (row >= a.num_rows) return;
   int b, t, n_keys, ql;
-  if (!resolve_row(a, row, b, t, n_keys, ql) || ql != 1) return;   // int8 rows are single positions
-  const int lo = first_visible(a, n_keys);
-  const int kbeg = lo & ~(kBlock - 1);
+  if (!resolve_row(a, row, b, t, n_keys, ql)) return;
+  const int ctx = n_keys - ql;                             // keys before the row's first position
+  const int lo_min = first_visible(a, ctx + 1);            // oldest key the first position sees
+  const int lo_max = first_visible(a, n_keys);             // oldest key the last position sees
+  const int kbeg = lo_min & ~(kBlock - 1);
   const int k0 = kbeg + split * a.split;
   if (k0 >= n_keys) return;
   const int k1 = min(k0 + a.split, n_keys);
@@ -124,13 +130,18 @@ __global__ __launch_bounds__(64 * NW, 2) void decode_i8_kernel(DecodeArgs a) {
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int g = NW * (z / nzh) + w;
   if (g >= a.num_kv_heads) return;                         // waves are independent: no barriers
-  const int zh = z % nzh;
-  const int h0 = g * a.group + zh * a.heads_per_wg;
-  const int ncols = min(a.heads_per_wg, a.group - zh * a.heads_per_wg);
+  const int c0 = (z % nzh) * a.heads_per_wg;               // first column of this group
+  const int ncol_all = ql * a.group;
+  if (c0 >= ncol_all) return;
 
   const int lane = threadIdx.x & (kWave - 1);
-  const int col = lane & 15;                  // S^T / O^T column = query head; also the K row loaded
+  const int col = lane & 15;                  // S^T / O^T column; also the K row loaded
   const int grp = lane >> 4;
+  const bool on = col < a.heads_per_wg && c0 + col < ncol_all;
+  const int cr = on ? (c0 + col) / a.group : 0;            // the column's position in the row
+  const int h = g * a.group + (on ? (c0 + col) % a.group : 0);
+  const int nvis = ctx + cr + 1;                           // keys [lo_c, nvis) are the column's
+  const int lo_c = first_visible(a, nvis);
 
   // q' = q * k_scale * 2^-e as the B operand.  Step kk covers channels 64(kk/2) + 16grp + 8(kk%2)
   // + [0, 8) (any order of the channels works as long as K uses the same one).  The four lanes
@@ -138,8 +149,7 @@ __global__ __launch_bounds__(64 * NW, 2) void decode_i8_kernel(DecodeArgs a) {
   f16x8 qb[NKK];
   float c, bias;
   {
-    const bool on = col < ncols;
-    const uint16_t* qp = reinterpret_cast<const uint16_t*>(a.q) + ((int64_t)t * a.num_q_heads + h0 + (on ? col : 0)) * D;
+    const uint16_t* qp = reinterpret_cast<const uint16_t*>(a.q) + ((int64_t)(t + cr) * a.num_q_heads + h) * D;
     const float* ksp = a.k_scale + (int64_t)g * D;
     float qf[NKK][8];
     float mx = 0.f;
@@ -244,8 +254,8 @@ __global__ __launch_bounds__(64 * NW, 2) void decode_i8_kernel(DecodeArgs a) {
     }
   };
 
-  // one unit; EDGE: it holds keys outside [lo, k1) (the split's last unit, or its first one when a
-  // sliding window starts inside it)
+  // one unit; EDGE: it holds keys some column must not see -- past k1 or past a column's position
+  // (the split's last units), or before a column's window (the first unit of split 0)
   auto consume = [&](auto edge_tag, int u, int slot) {
     constexpr bool EDGE = decltype(edge_tag)::value;
     const char* kw = mine + slot * NW * 2 * UB;
@@ -271,12 +281,12 @@ __global__ __launch_bounds__(64 * NW, 2) void decode_i8_kernel(DecodeArgs a) {
     }
     if constexpr (EDGE) {
       const int base = (kb0 + 2 * u) * kBlock;
-      const int nvis = k1 - base, nlo = lo - base;          // keys [nlo, nvis) of the unit are visible
+      const int nhi = min(k1, nvis) - base, nlo = lo_c - base;   // keys [nlo, nhi) of the unit are visible
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
         const int ka = 4 * grp + v, kb = kBlock + 4 * grp + v;
-        if (ka >= nvis || ka < nlo) sA[v] = -INFINITY;
-        if (kb >= nvis || kb < nlo) sB[v] = -INFINITY;
+        if (ka >= nhi || ka < nlo) sA[v] = -INFINITY;
+        if (kb >= nhi || kb < nlo) sB[v] = -INFINITY;
       }
     }
     float bm = fmaxf(fmaxf(fmaxf(sA[0], sA[1]), fmaxf(sA[2], sA[3])), fmaxf(fmaxf(sB[0], sB[1]), fmaxf(sB[2], sB[3])));
@@ -311,8 +321,11 @@ __global__ __launch_bounds__(64 * NW, 2) void decode_i8_kernel(DecodeArgs a) {
   };
   using Full = std::integral_constant<bool, false>;
   using Edge = std::integral_constant<bool, true>;
-  const bool last_partial = (kb0 + 2 * nu) * kBlock > k1;
-  const bool first_cut = kb0 * kBlock < lo;                // split 0 of a row whose window starts mid-block
+  const int edge_hi = min(k1, ctx + 1);                    // units reaching past this need masking,
+  auto edge = [&](int u) {                                 // and so do units starting before lo_max
+    const int base = (kb0 + 2 * u) * kBlock;
+    return base + 2 * kBlock > edge_hi || base < lo_max;
+  };
 
   // one unit in flight while the previous one is computed; the wait leaves exactly the next unit's
   // NCP copies outstanding (vector memory operations complete in issue order)
@@ -324,13 +337,13 @@ __global__ __launch_bounds__(64 * NW, 2) void decode_i8_kernel(DecodeArgs a) {
     } else {
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     }
-    if ((u == 0 && first_cut) || (u + 1 == nu && last_partial)) consume(Edge{}, u, u & 1);
+    if (edge(u)) consume(Edge{}, u, u & 1);
     else consume(Full{}, u, u & 1);
   }
   lsum = xor16_sum(lsum);
   lsum = xor32_sum(lsum);
 
-  if (col < ncols) {
+  if (on) {
     // O^T rows held by this lane are channels 16tt + 4grp + v: apply their V scale
     const float* vsp = a.v_scale + (int64_t)g * D + 4 * grp;
 #pragma unroll
@@ -341,10 +354,9 @@ __global__ __launch_bounds__(64 * NW, 2) void decode_i8_kernel(DecodeArgs a) {
       O[tt][2] *= s.z;
       O[tt][3] *= s.w;
     }
-    const int h = h0 + col;
     if (n_splits == 1) {
       const float inv = 1.f / lsum;
-      uint16_t* op = reinterpret_cast<uint16_t*>(a.out) + ((int64_t)t * a.num_q_heads + h) * D;
+      uint16_t* op = reinterpret_cast<uint16_t*>(a.out) + ((int64_t)(t + cr) * a.num_q_heads + h) * D;
 #pragma unroll
       for (int tt = 0; tt < NT; ++tt) {
         uint2 pk;
@@ -353,7 +365,7 @@ __global__ __launch_bounds__(64 * NW, 2) void decode_i8_kernel(DecodeArgs a) {
         *reinterpret_cast<uint2*>(op + 16 * tt + 4 * grp) = pk;
       }
     } else {
-      const int64_t pidx = partial_index(a, row, 0, split, h);
+      const int64_t pidx = partial_index(a, row, cr, split, h);
       float* po = a.part_o + pidx * D;
 #pragma unroll
       for (int tt = 0; tt < NT; ++tt)
@@ -370,7 +382,7 @@ namespace {
 template <int D, int NW>
 hipError_t i8_dispatch(const DecodeArgs& a, hipStream_t s) {
   if (a.heads_per_wg < 1 || a.heads_per_wg > 16) return hipErrorInvalidValue;   // 16 MFMA columns
-  const int64_t nzh = (a.group + a.heads_per_wg - 1) / a.heads_per_wg;
+  const int64_t nzh = ((int64_t)a.qmax * a.group + a.heads_per_wg - 1) / a.heads_per_wg;
   const int64_t grid = (int64_t)((a.num_kv_heads + NW - 1) / NW) * nzh * a.max_splits * a.num_rows;
   if (grid <= 0 || grid > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
   decode_i8_kernel<D, NW><<<dim3((unsigned)grid), dim3(64 * NW), 0, s>>>(a);

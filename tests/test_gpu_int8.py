@@ -166,3 +166,32 @@ def test_int8_c5_skewed_long_decode():
 @pytest.mark.timeout(600)
 def test_int8_c5_window():
     run_i8(W.config5(cache="i8"), window=4096, what="c5 int8 W=4096")
+
+
+I8_VERIFY_CASES = [
+    # seq_lens, q_lens, Hq, Hkv, d, window: rows of a few tokens to verify on the int8 decode kernel,
+    # each (position, head) column masked to its own causal and window range
+    ([17, 16, 33, 300], [2, 3, 8, 5], 8, 2, 128, 0),
+    ([1000, 2048, 3001, 517], [8, 1, 7, 2], 32, 8, 128, 0),     # several splits, merge per position
+    ([700, 129, 40], [6, 2, 8], 16, 1, 64, 0),                  # 16 heads per KV head: 128 columns
+    ([3000, 777, 64], [4, 8, 2], 32, 8, 128, 100),              # windows start mid-block per column
+    ([3000, 1243, 250, 5000], [8, 8, 7, 8], 32, 8, 128, 238),   # first position reaches past a split
+    ([500, 500], [8, 8], 8, 2, 128, 1),
+    ([1030, 260, 90], [1, 3, 90], 24, 3, 128, 0),              # verify rows beside a prefill
+]
+
+
+@pytest.mark.parametrize("case", range(len(I8_VERIFY_CASES)))
+def test_int8_verify_rows(case):
+    seq, ql, Hq, Hkv, d, win = I8_VERIFY_CASES[case]
+    say(f"int8 verify case {case}: seq {seq} q {ql} Hq {Hq} Hkv {Hkv} d {d} W {win}")
+    w = W.make_batch(760 + case, seq, ql, Hq, Hkv, d, "bf16",
+                     num_blocks=sum((s + 15) // 16 for s in seq) + 3, cache="i8")
+    run_i8(w, window=win, what=f"int8 verify[{case}]")
+
+
+@pytest.mark.timeout(600)
+def test_int8_verify_at_decode_workload_size():
+    w = W.verify_variant(W.CONFIGS["c5"](cache="i8"), 4)
+    say("int8 verify: c5 requests, 4 tokens each")
+    run_i8(w, what="c5 int8 verify 4")
