@@ -16,7 +16,7 @@ from __future__ import annotations
 import ctypes
 import os
 
-ABI_VERSION = 3
+ABI_VERSION = 4
 BLOCK_SIZE = 16
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libpa.so")
@@ -38,7 +38,7 @@ class _CacheDesc(ctypes.Structure):
 
 
 class _AttnOpts(ctypes.Structure):
-    _fields_ = [("sliding_window", ctypes.c_int32)]
+    _fields_ = [("sliding_window", ctypes.c_int32), ("max_q_len", ctypes.c_int32)]
 
 
 def load_library(path: str = LIB_PATH):
@@ -178,11 +178,12 @@ def _workspace(dev, nbytes):
 
 
 def attention(q, k_cache, v_cache, block_tables, seq_lens, query_start_loc, scale, out, workspace=None,
-              window=0, k_scale=None, v_scale=None):
+              window=0, k_scale=None, v_scale=None, max_q_len=0):
     """Causal attention of the varlen batch over the paged cache; writes ``out`` in place.
 
     ``window`` > 0 restricts each query row to its ``window`` most recent keys (pa_attention_ex);
-    int8 caches take their ``k_scale``/``v_scale``."""
+    ``max_q_len`` > 0 promises that no request has a longer q_len (lets decode and verification
+    steps skip the prefill-tile pass); int8 caches take their ``k_scale``/``v_scale``."""
     import torch
     lib = load_library()
     dev = q.device
@@ -204,7 +205,7 @@ def attention(q, k_cache, v_cache, block_tables, seq_lens, query_start_loc, scal
     if seq_lens.shape[0] != B or query_start_loc.shape[0] != B + 1:
         raise ValueError("seq_lens must be [B], query_start_loc [B+1]")
     desc = _desc(k_cache, k_scale, v_scale)
-    opts = _AttnOpts(int(window))
+    opts = _AttnOpts(int(window), int(max_q_len))
     need = int(lib.pa_attention_workspace_size(B, T, MB, Hq, ctypes.byref(desc)))
     if need == 0:
         _err(lib, lib.pa_attention_ex(None, T, Hq, None, None, ctypes.byref(desc), None, B, MB, None, None,

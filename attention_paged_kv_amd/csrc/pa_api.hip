@@ -160,7 +160,9 @@ int validate_desc(const pa_cache_desc* c) {
 }
 
 // window: keys a row sees (pa::kNoWindow for all); it only bounds how many splits a row needs.
-int make_plan(int32_t B, int32_t T, int32_t MB, int32_t Hq, const pa_cache_desc* c, int window, Plan& p) {
+// max_q_len: the caller's bound on every q_len (0: none given).
+int make_plan(int32_t B, int32_t T, int32_t MB, int32_t Hq, const pa_cache_desc* c, int window, int max_q_len,
+              Plan& p) {
   int rc = validate_desc(c);
   if (rc) return rc;
   if (B < 1) return fail(PA_ERR_INVALID_ARG, "num_seqs must be >= 1 (got %d)", B);
@@ -177,7 +179,7 @@ int make_plan(int32_t B, int32_t T, int32_t MB, int32_t Hq, const pa_cache_desc*
   // min(kVerifyMax, the longest q_len the sizes allow); fp32 rows carry one.  The matrix-core
   // decode kernels hold up to 16 (position, query head) columns of a KV head per wave (the MFMA
   // column count); the fp32 vector-ALU decode holds a divisor of the group size up to 8.
-  const int longest = T - B + 1;
+  const int longest = (max_q_len > 0 && max_q_len < T - B + 1) ? max_q_len : T - B + 1;
   p.qmax = p.bf16 ? (longest < pa::kVerifyMax ? longest : pa::kVerifyMax) : 1;
   if (p.bf16) p.heads_per_wg = p.qmax * p.group < 16 ? p.qmax * p.group : 16;
   else p.heads_per_wg = (p.group % 8 == 0) ? 8 : (p.group % 4 == 0) ? 4 : (p.group % 2 == 0) ? 2 : 1;
@@ -303,8 +305,9 @@ int run_check(const pa::CheckArgs& base, hipStream_t s) {
   if (!host[0]) return PA_OK;
   static const char* what[] = {"", "slot outside the pool", "slot written twice", "query_start_loc[0] != 0",
                                "query_start_loc[num_seqs] != num_q_tokens", "q_len < 1", "seq_len < q_len",
-                               "seq_len > max_blocks_per_seq*16", "block id outside [0, num_blocks)"};
-  const int code = host[1] >= 1 && host[1] <= 8 ? host[1] : 0;
+                               "seq_len > max_blocks_per_seq*16", "block id outside [0, num_blocks)",
+                               "q_len > max_q_len"};
+  const int code = host[1] >= 1 && host[1] <= 9 ? host[1] : 0;
   return fail(PA_ERR_CHECK_FAILED, "check mode: %s (index %d, value %d)", what[code], host[2], host[3]);
 }
 
@@ -365,7 +368,7 @@ size_t pa_attention_workspace_size(int32_t num_seqs, int32_t num_q_tokens, int32
                                    int32_t num_q_heads, const pa_cache_desc* cache) {
   Plan p;
   std::string keep = g_err;
-  if (make_plan(num_seqs, num_q_tokens, max_blocks_per_seq, num_q_heads, cache, pa::kNoWindow, p) != PA_OK) {
+  if (make_plan(num_seqs, num_q_tokens, max_blocks_per_seq, num_q_heads, cache, pa::kNoWindow, 0, p) != PA_OK) {
     g_err = keep;
     return 0;
   }
@@ -378,14 +381,16 @@ int pa_attention_ex(const void* q, int32_t num_q_tokens, int32_t num_q_heads, co
                     void* out, void* workspace, size_t workspace_bytes, const pa_attention_opts* opts,
                     void* stream) {
   g_err.clear();
-  int window = pa::kNoWindow;
+  int window = pa::kNoWindow, max_q_len = 0;
   if (opts) {
     if (opts->sliding_window < 0)
       return fail(PA_ERR_INVALID_ARG, "sliding_window must be >= 0 (got %d)", opts->sliding_window);
     if (opts->sliding_window > 0 && opts->sliding_window < pa::kNoWindow) window = opts->sliding_window;
+    if (opts->max_q_len < 0) return fail(PA_ERR_INVALID_ARG, "max_q_len must be >= 0 (got %d)", opts->max_q_len);
+    max_q_len = opts->max_q_len;
   }
   Plan p;
-  int rc = make_plan(num_seqs, num_q_tokens, max_blocks_per_seq, num_q_heads, cache, window, p);
+  int rc = make_plan(num_seqs, num_q_tokens, max_blocks_per_seq, num_q_heads, cache, window, max_q_len, p);
   if (rc) return rc;
   if (!q || !k_cache || !v_cache || !block_tables || !seq_lens || !query_start_loc || !out)
     return fail(PA_ERR_INVALID_ARG, "null pointer argument");
@@ -435,6 +440,7 @@ int pa_attention_ex(const void* q, int32_t num_q_tokens, int32_t num_q_heads, co
     c.num_blocks = cache->num_blocks;
     c.num_q_tokens = num_q_tokens;
     c.window = window;
+    c.max_q_len = max_q_len;
     rc = run_check(c, s);
     if (rc) return rc;
   }

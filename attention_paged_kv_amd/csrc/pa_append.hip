@@ -118,6 +118,7 @@ __global__ __launch_bounds__(256) void check_kernel(CheckArgs a, unsigned* bitma
       const int ql = a.qsl[b + 1] - a.qsl[b];
       const int sl = a.seq_lens[b];
       if (ql < 1) { report(a.result, 5, b, ql); continue; }
+      if (a.max_q_len > 0 && ql > a.max_q_len) { report(a.result, 9, b, ql); continue; }
       if (sl < ql) { report(a.result, 6, b, sl); continue; }
       if (sl > a.max_blocks * kBlock) { report(a.result, 7, b, sl); continue; }
       const int nb = (sl + kBlock - 1) / kBlock;

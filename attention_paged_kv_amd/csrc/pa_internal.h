@@ -90,6 +90,7 @@ struct CheckArgs {
   int num_blocks;
   int num_q_tokens;
   int window;                    // table entries before the first row's window are not checked
+  int max_q_len;                 // > 0: every q_len must be at most this
   int* result;                   // [4]: flag, code, index, value (device, zeroed by caller)
 };
 

@@ -204,7 +204,8 @@ def main():
         dsteps.append(dict(q=to_dev(st.q), k=to_dev(st.k_new), v=to_dev(st.v_new),
                            slots=to_dev(st.slot_mapping.astype(np.int32)), bt=to_dev(st.block_tables),
                            sl=to_dev(st.seq_lens), qsl=to_dev(st.query_start_loc),
-                           out=torch.empty(st.q.shape, dtype=tdt, device=dev)))
+                           out=torch.empty(st.q.shape, dtype=tdt, device=dev),
+                           max_q=int(st.q_lens.max())))     # a scheduler knows its step's longest q_len
     ws_need = max(pa.workspace_size(st.num_seqs, st.num_tokens, st.block_tables.shape[1], w.num_q_heads, kc, ks, vs)
                   for st in steps)
     ws = torch.zeros(max(ws_need, 256), dtype=torch.uint8, device=dev)
@@ -213,7 +214,7 @@ def main():
         for d in dsteps:
             pa.append_kv(d["k"], d["v"], d["slots"], kc, vc, ks, vs)
             pa.attention(d["q"], kc, vc, d["bt"], d["sl"], d["qsl"], w.scale, d["out"], workspace=ws, window=win,
-                         k_scale=ks, v_scale=vs)
+                         k_scale=ks, v_scale=vs, max_q_len=d["max_q"])
 
     # algorithmic work of one step
     kv_bytes = sum(A.kv_read_bytes(st.seq_lens, w.num_kv_heads, w.head_dim, w.esz, st.q_lens, win) for st in steps)

@@ -35,7 +35,7 @@
 extern "C" {
 #endif
 
-#define PA_ABI_VERSION 3
+#define PA_ABI_VERSION 4
 #define PA_BLOCK_SIZE 16
 
 typedef enum {
@@ -158,6 +158,12 @@ typedef struct {
    * read (any value: a cache may drop such blocks), nor are the cache slots they would name.
    * Negative values are rejected with PA_ERR_INVALID_ARG. */
   int32_t sliding_window;
+  /* Largest q_len of any request in the batch, when the caller knows it (a scheduler does).  0:
+   * not given, the library assumes num_q_tokens - num_seqs + 1.  With a bound <= 8 (decode and
+   * verification steps) the prefill-tile pass is not launched at all.  A request whose q_len
+   * exceeds the bound gets an undefined output row; check mode reports it (PA_ERR_CHECK_FAILED).
+   * Negative values are rejected with PA_ERR_INVALID_ARG. */
+  int32_t max_q_len;
 } pa_attention_opts;
 
 /*

@@ -56,13 +56,13 @@ class GpuState:
                     v=dev_tensor(st.v_new, self.w.dtype), slots=int_tensor(st.slot_mapping),
                     bt=int_tensor(st.block_tables), sl=int_tensor(st.seq_lens), qsl=int_tensor(st.query_start_loc))
 
-    def step(self, st, append=True, window=0):
+    def step(self, st, append=True, window=0, max_q_len=0):
         x = self.inputs(st)
         if append:
             pa.append_kv(x["k"], x["v"], x["slots"], self.kc, self.vc, self.ks, self.vs)
         out = torch.empty_like(x["q"])
         pa.attention(x["q"], self.kc, self.vc, x["bt"], x["sl"], x["qsl"], self.w.scale, out, window=window,
-                     k_scale=self.ks, v_scale=self.vs)
+                     k_scale=self.ks, v_scale=self.vs, max_q_len=max_q_len)
         torch.cuda.synchronize()
         return host_array(out, self.w.dtype)
 

@@ -125,6 +125,10 @@ def test_window_option_rejected_when_negative_before_launch(lib):
     rc = lib.pa_attention_ex(p, 4, 8, p, p, ctypes.byref(d), p, 4, 16, p, p, ctypes.c_float(1), o, None, 0,
                              ctypes.byref(neg), None)
     assert rc == 1 and b"sliding_window" in lib.pa_last_error()
+    negq = pa._AttnOpts(0, -1)
+    rc = lib.pa_attention_ex(p, 4, 8, p, p, ctypes.byref(d), p, 4, 16, p, p, ctypes.c_float(1), o, None, 0,
+                             ctypes.byref(negq), None)
+    assert rc == 1 and b"max_q_len" in lib.pa_last_error()
     # a window does not lift the other checks: the 8-byte workspace is still refused before launch
     win = pa._AttnOpts(1000)     # rows may span 1015 keys: 4 splits, partials in the workspace
     small = ctypes.c_void_p(256)

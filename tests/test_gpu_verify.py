@@ -81,3 +81,29 @@ def test_verify_rows_equal_one_token_steps():
 def test_verify_batches_at_decode_workload_sizes(cfg, k):
     w = W.verify_variant(W.CONFIGS[cfg](), k)
     run(w, what=f"{cfg} verify {k}")
+
+
+def test_max_q_len_hint_skips_tiles_and_matches():
+    """With the caller's bound on q_len (<= 8) the tile pass is not launched; results are those of
+    the call without the bound.  A bound below some q_len is reported in check mode."""
+    seq, ql, Hq, Hkv, d, win = CASES[3]
+    w = W.make_batch(431, seq, ql, Hq, Hkv, d, "bf16", num_blocks=sum((s + 15) // 16 for s in seq) + 3)
+    g0, g1 = GpuState(w), GpuState(w)
+    pa.timing_reset()
+    pa.timing_enable(True)
+    try:
+        ref = g0.step(w.steps[0])
+        plain = pa.timing_read("prefill_tile")[1]
+        out = g1.step(w.steps[0], max_q_len=max(ql))
+        hinted = pa.timing_read("prefill_tile")[1] - plain
+    finally:
+        pa.timing_enable(False)
+    assert plain == 1 and hinted == 0, (plain, hinted)
+    assert np.array_equal(out, ref)
+    pa.set_check(True)
+    try:
+        with pytest.raises(pa.PAError) as ei:
+            GpuState(w).step(w.steps[0], max_q_len=max(ql) - 1)
+        assert ei.value.code == 5 and "max_q_len" in str(ei.value)
+    finally:
+        pa.set_check(False)
