@@ -683,6 +683,90 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a) {
   }
 }
 
+// Merge for stream mode, where a row has few pieces: one wave per (row, position, query head), four
+// per workgroup, no LDS.  The wave's lanes are 4 piece groups x 16 channel chunks; each piece's
+// weight 2^(m_s - m) is recomputed where it is used, so one pass over the partials suffices after
+// the max.  (With fixed splits a long row has dozens of partials; there a workgroup per item reads
+// them in parallel, above, and measured faster.)
+template <int D, bool BF16>
+__global__ __launch_bounds__(256) void merge_wave_kernel(DecodeArgs a) {
+  constexpr int CL = D / 16;                 // channels per lane
+  const int lane = threadIdx.x & (kWave - 1);
+  const int64_t item = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int h = (int)(item % a.num_q_heads);
+  const int r = (int)((item / a.num_q_heads) % a.qmax);
+  const int64_t row64 = item / ((int64_t)a.num_q_heads * a.qmax);
+  if (row64 >= a.num_rows) return;
+  const int row = (int)row64;
+  int b, t0, n_keys, ql;
+  if (!resolve_row(a, row, b, t0, n_keys, ql) || r >= ql) return;
+  int n;
+  if (a.stream_wgs > 0) {
+    int pre, nb;
+    const int tot = stream_scan(a, row, pre, nb);
+    n = stream_pieces(pre, nb, stream_run(a, tot));
+  } else {
+    n = (n_keys - split_origin(a, n_keys, ql) + a.split - 1) / a.split;
+  }
+  if (n <= 1) return;                                       // written directly by the split kernel
+  const int64_t pbase = partial_index(a, row, r, 0, h);    // split s adds s * num_q_heads
+  const int64_t st = a.num_q_heads;
+  const float* ml = a.part_ml;
+
+  float mx = -INFINITY, ls = 0.f;
+  for (int s = lane; s < n; s += kWave) mx = fmaxf(mx, ml[(pbase + s * st) * 2]);
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+  for (int s = lane; s < n; s += kWave) {
+    const float* p = ml + (pbase + s * st) * 2;
+    ls = fmaf(fast_exp2(p[0] - mx), p[1], ls);
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) ls += __shfl_xor(ls, o);
+
+  const int sg = lane >> 4, ch = lane & 15;                 // split group, channel chunk
+  float acc[CL];
+#pragma unroll
+  for (int e = 0; e < CL; ++e) acc[e] = 0.f;
+#pragma unroll 4
+  for (int s0 = 0; s0 < n; s0 += 4) {
+    const int s = s0 + sg;
+    if (s < n) {
+      const int64_t p = pbase + s * st;
+      const float wgt = fast_exp2(ml[p * 2] - mx);
+      const float4* o = reinterpret_cast<const float4*>(a.part_o + p * D + CL * ch);
+#pragma unroll
+      for (int e4 = 0; e4 < CL / 4; ++e4) {
+        const float4 v = o[e4];
+        acc[4 * e4] = fmaf(wgt, v.x, acc[4 * e4]);
+        acc[4 * e4 + 1] = fmaf(wgt, v.y, acc[4 * e4 + 1]);
+        acc[4 * e4 + 2] = fmaf(wgt, v.z, acc[4 * e4 + 2]);
+        acc[4 * e4 + 3] = fmaf(wgt, v.w, acc[4 * e4 + 3]);
+      }
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < CL; ++e) {
+    acc[e] += __shfl_xor(acc[e], 16);
+    acc[e] += __shfl_xor(acc[e], 32);
+  }
+  if (sg == 0) {
+    const float inv = 1.f / ls;
+    const int64_t o = ((int64_t)(t0 + r) * a.num_q_heads + h) * D + CL * ch;
+    if constexpr (BF16) {
+#pragma unroll
+      for (int e2 = 0; e2 < CL / 2; ++e2)
+        reinterpret_cast<uint32_t*>(reinterpret_cast<uint16_t*>(a.out) + o)[e2] =
+            pack_bf16x2(acc[2 * e2] * inv, acc[2 * e2 + 1] * inv);
+    } else {
+#pragma unroll
+      for (int e4 = 0; e4 < CL / 4; ++e4)
+        reinterpret_cast<float4*>(reinterpret_cast<float*>(a.out) + o)[e4] =
+            make_float4(acc[4 * e4] * inv, acc[4 * e4 + 1] * inv, acc[4 * e4 + 2] * inv, acc[4 * e4 + 3] * inv);
+    }
+  }
+}
+
 // ------------------------------------------------------------------------------------------
 namespace {
 template <int D>
@@ -726,15 +810,17 @@ hipError_t launch_decode_split(const DecodeArgs& a, int head_dim, bool bf16, hip
 }
 
 hipError_t launch_decode_merge(const DecodeArgs& a, int head_dim, bool bf16, hipStream_t s) {
-  const int64_t grid = (int64_t)a.num_rows * a.qmax * a.num_q_heads;
+  const int64_t items = (int64_t)a.num_rows * a.qmax * a.num_q_heads;
+  const bool wave = a.stream_wgs > 0;                      // few pieces per row: a wave per item
+  const int64_t grid = wave ? (items + 3) / 4 : items;
   if (grid <= 0 || grid > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
   const dim3 g((unsigned)grid), blk(256);
   if (head_dim == 128) {
-    if (bf16) decode_merge_kernel<128, true><<<g, blk, 0, s>>>(a);
-    else decode_merge_kernel<128, false><<<g, blk, 0, s>>>(a);
+    if (wave) bf16 ? merge_wave_kernel<128, true><<<g, blk, 0, s>>>(a) : merge_wave_kernel<128, false><<<g, blk, 0, s>>>(a);
+    else bf16 ? decode_merge_kernel<128, true><<<g, blk, 0, s>>>(a) : decode_merge_kernel<128, false><<<g, blk, 0, s>>>(a);
   } else if (head_dim == 64) {
-    if (bf16) decode_merge_kernel<64, true><<<g, blk, 0, s>>>(a);
-    else decode_merge_kernel<64, false><<<g, blk, 0, s>>>(a);
+    if (wave) bf16 ? merge_wave_kernel<64, true><<<g, blk, 0, s>>>(a) : merge_wave_kernel<64, false><<<g, blk, 0, s>>>(a);
+    else bf16 ? decode_merge_kernel<64, true><<<g, blk, 0, s>>>(a) : decode_merge_kernel<64, false><<<g, blk, 0, s>>>(a);
   } else {
     return hipErrorInvalidValue;
   }
