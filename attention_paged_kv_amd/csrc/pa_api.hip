@@ -59,14 +59,18 @@ bool check_on() {
   return v == 1;
 }
 
-int split_tokens() {
-  static int v = [] {
+// Keys per decode split: PA_SPLIT_TOKENS if set (a multiple of 16 up to 1024), else 256, or 384
+// when a row may span more than 8192 keys (measured: c5's rows of up to 32768 keys 175 against
+// 179 us; c2's rows of up to 4096 keys 207 against 211).  `bound`: sizing a workspace that must
+// serve every window, so the smaller split (more partials) is assumed.
+int split_tokens(int64_t span, bool bound) {
+  static const int over = [] {
     const char* e = std::getenv("PA_SPLIT_TOKENS");
-    int s = e ? std::atoi(e) : pa::kDefaultSplitTokens;
-    if (s < 16 || s > 1024 || s % 16 != 0) s = pa::kDefaultSplitTokens;  // <= 64 blocks per split
-    return s;
+    const int s = e ? std::atoi(e) : 0;
+    return (s >= 16 && s <= 1024 && s % 16 == 0) ? s : 0;   // <= 64 blocks per split
   }();
-  return v;
+  if (over) return over;
+  return (span > 8192 && !bound) ? pa::kLongSplitTokens : pa::kDefaultSplitTokens;
 }
 
 // ---- per-device state: library-owned workspace and the check-mode result slot ----
@@ -160,9 +164,10 @@ int validate_desc(const pa_cache_desc* c) {
 }
 
 // window: keys a row sees (pa::kNoWindow for all); it only bounds how many splits a row needs.
-// max_q_len: the caller's bound on every q_len (0: none given).
+// max_q_len: the caller's bound on every q_len (0: none given).  bound: the plan only sizes a
+// workspace for every option value.
 int make_plan(int32_t B, int32_t T, int32_t MB, int32_t Hq, const pa_cache_desc* c, int window, int max_q_len,
-              Plan& p) {
+              Plan& p, bool bound = false) {
   int rc = validate_desc(c);
   if (rc) return rc;
   if (B < 1) return fail(PA_ERR_INVALID_ARG, "num_seqs must be >= 1 (got %d)", B);
@@ -185,7 +190,6 @@ int make_plan(int32_t B, int32_t T, int32_t MB, int32_t Hq, const pa_cache_desc*
   else p.heads_per_wg = (p.group % 8 == 0) ? 8 : (p.group % 4 == 0) ? 4 : (p.group % 2 == 0) ? 2 : 1;
   if (p.bf16 && p.group > pa::kMaxTileGroup)
     return fail(PA_ERR_UNSUPPORTED, "query heads per KV head (%d) above %d", p.group, pa::kMaxTileGroup);
-  p.split = split_tokens();
   // A row's pass covers keys from the block holding the oldest key its first position sees (that
   // position's window reaches qmax - 1 keys further back than the last one's) to its last key:
   // at most min(MB * 16, window + qmax - 1 + 15) keys, and min(MB, ceil((window + qmax - 1) / 16) + 1)
@@ -196,6 +200,7 @@ int make_plan(int32_t B, int32_t T, int32_t MB, int32_t Hq, const pa_cache_desc*
   // Rows of several positions (verification) make uneven work per split (more columns on some
   // rows, longer merges); they are dealt out in balanced runs.  Plain decode rows measure best on
   // fixed splits, which the hardware schedules dynamically.
+  p.split = split_tokens(span, bound);
   p.stream = c->dtype == PA_DTYPE_BF16 && p.qmax > 1;
   if (p.stream) {
     // a row meets at most ceil(blocks / run) + 1 runs, and runs hold at least `split` keys
@@ -368,7 +373,7 @@ size_t pa_attention_workspace_size(int32_t num_seqs, int32_t num_q_tokens, int32
                                    int32_t num_q_heads, const pa_cache_desc* cache) {
   Plan p;
   std::string keep = g_err;
-  if (make_plan(num_seqs, num_q_tokens, max_blocks_per_seq, num_q_heads, cache, pa::kNoWindow, 0, p) != PA_OK) {
+  if (make_plan(num_seqs, num_q_tokens, max_blocks_per_seq, num_q_heads, cache, pa::kNoWindow, 0, p, true) != PA_OK) {
     g_err = keep;
     return 0;
   }

@@ -163,3 +163,20 @@ def test_binding_fails_loudly_without_library(tmp_path):
             pa.load_library(str(tmp_path / "missing.so"))
         finally:
             pa._lib = saved
+
+
+@pytest.mark.parametrize("window,max_q", [(0, 0), (8000, 0), (4096, 0), (100, 0), (8000, 8), (0, 2)])
+def test_workspace_size_serves_every_option(lib, window, max_q):
+    """pa_attention_workspace_size() for the sizes bounds what any window and q_len bound needs: a
+    call given exactly that many bytes is never refused for its workspace (code 4).  Rows of up to
+    8208 keys sit where the split length changes with the window (256 vs 384 keys)."""
+    d = _desc()
+    p = ctypes.c_void_p(16)
+    o = ctypes.c_void_p(48)
+    for B, T in ((4, 4), (4, 20), (32, 32)):
+        need = lib.pa_attention_workspace_size(B, T, 513, 8, ctypes.byref(d))
+        assert need > 0
+        opts = pa._AttnOpts(window, max_q)
+        rc = lib.pa_attention_ex(p, T, 8, p, p, ctypes.byref(d), p, B, 513, p, p, ctypes.c_float(1), o,
+                                 ctypes.c_void_p(256), need, ctypes.byref(opts), None)
+        assert rc != 4, (B, T, window, max_q, lib.pa_last_error())
