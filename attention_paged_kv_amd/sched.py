@@ -91,6 +91,11 @@ class Batch:
         return int(self.request_ids.shape[0])
 
     @property
+    def max_q_len(self) -> int:
+        """Longest q_len of the step: the bound to pass as attention(..., max_q_len=)."""
+        return int(np.diff(self.query_start_loc).max()) if self.num_seqs else 0
+
+    @property
     def num_tokens(self) -> int:
         return int(self.slot_mapping.shape[0])
 

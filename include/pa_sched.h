@@ -59,7 +59,8 @@ typedef struct {
 /* One planned step, in caller-owned host arrays.  In: the capacities.  Out: the sizes and the
  * arrays, in step order (decodes first).  block_tables rows are padded with -1.  samples[i] = 1
  * when request i's scheduled tokens end at its last known token, so the step yields its next
- * token (passed back through pa_sched_commit). */
+ * token (passed back through pa_sched_commit).  The step's longest q_len (the largest difference of
+ * consecutive query_start_loc entries) is the bound to pass as pa_attention_opts.max_q_len. */
 typedef struct {
   int32_t cap_seqs;            /* in: >= max_seqs, or >= live requests when max_seqs == 0         */
   int32_t cap_tokens;          /* in: >= token_budget                                            */

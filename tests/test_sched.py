@@ -21,6 +21,7 @@ def compare_step(cpp, orc, rng, stop_p):
     assert b.token_ids.tolist() == toks
     assert b.positions.tolist() == pos
     assert b.samples.tolist() == samples
+    assert b.max_q_len == (max(q1 - q0 for q0, q1 in zip(qsl, qsl[1:])) if len(qsl) > 1 else 0)
     assert cpp.preempted() == orc.preempted
     nxt = [int(x) for x in rng.integers(0, 40, len(plan))]
     stop = [int(x) for x in (rng.random(len(plan)) < stop_p)]
