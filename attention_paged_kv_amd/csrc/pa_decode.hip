@@ -228,6 +228,7 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(DecodeArgs a) {
     };
 
     for (int zh = 0; zh * a.heads_per_wg < ncol_all; zh += NG) {
+      issue(0, 0);                              // the first block's copies overlap the Q loads
       // this pass's columns: group gi holds columns (zh + gi) * heads_per_wg + col
       bool on[NG];
       int cr[NG], h[NG], nvis[NG], lo_c[NG];
@@ -248,8 +249,8 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(DecodeArgs a) {
           qb[gi][kk] = __builtin_bit_cast(bf16x8, v);
         }
       }
-      // wait for Q here, where nothing else is in flight: left to itself the compiler may put this
-      // wait (a full vmcnt(0)) inside the block loop, where it would also wait for the next block
+      // wait for Q (and the first block) here: left to itself the compiler may put this wait (a
+      // full vmcnt(0)) inside the block loop, where it would also wait for the next block
       __builtin_amdgcn_s_waitcnt(0x0F70);       // vmcnt(0) only
 
       float m[NG], lsum[NG];
@@ -332,7 +333,6 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(DecodeArgs a) {
 
       // one block in flight while the previous one is computed; the wait leaves exactly the next
       // block's NCP copies outstanding (vector memory operations complete in issue order)
-      issue(0, 0);
       for (int i = 0; i < nb; ++i) {
         if (i + 1 < nb) {
           issue(i + 1, (i + 1) & 1);

@@ -146,9 +146,10 @@ __global__ __launch_bounds__(64 * NW, 2) void decode_i8_kernel(DecodeArgs a) {
   // q' = q * k_scale * 2^-e as the B operand.  Step kk covers channels 64(kk/2) + 16grp + 8(kk%2)
   // + [0, 8) (any order of the channels works as long as K uses the same one).  The four lanes
   // of a column (grp = 0..3) share e, the scaled softmax factor c and the score bias.
+  // (Loaded by load_q after the first unit's copies are issued, so the two latencies overlap.)
   f16x8 qb[NKK];
   float c, bias;
-  {
+  auto load_q = [&]() {
     const uint16_t* qp = reinterpret_cast<const uint16_t*>(a.q) + ((int64_t)(t + cr) * a.num_q_heads + h) * D;
     const float* ksp = a.k_scale + (int64_t)g * D;
     float qf[NKK][8];
@@ -187,7 +188,7 @@ __global__ __launch_bounds__(64 * NW, 2) void decode_i8_kernel(DecodeArgs a) {
     qs = xor32_sum(qs);
     bias = kCodeBias * qs;                                  // score offset from the biased K codes
     c = ldexpf(a.scale_log2, e);                            // log2-unit factor of this column's scores
-  }
+  };
 
   const int64_t rs = (int64_t)a.num_kv_heads * D;          // bytes per cache token row
   const int64_t blkbytes = kBlock * rs;
@@ -330,6 +331,7 @@ __global__ __launch_bounds__(64 * NW, 2) void decode_i8_kernel(DecodeArgs a) {
   // one unit in flight while the previous one is computed; the wait leaves exactly the next unit's
   // NCP copies outstanding (vector memory operations complete in issue order)
   issue(0, 0);
+  load_q();
   for (int u = 0; u < nu; ++u) {
     if (u + 1 < nu) {
       issue(u + 1, (u + 1) & 1);
