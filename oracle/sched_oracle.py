@@ -14,7 +14,7 @@ Sources (cited by page and section):
   P1  "Prefill 和 Decode 不是两个步骤..." (lshu.cn/news/11576), §2.2-2.3: fixed 16-token blocks
       taken from a free pool, addressed through a block table.
 
-Policy (the readings this build takes where the pages stop; the C++ planner follows the same):
+Policy (the readings taken where the pages stop; the C++ planner follows the same):
   * A request holds its token ids (prompt, then every sampled token), the count already computed,
     and its block list.  It is decoding when all its prompt tokens are computed and exactly one
     token is pending (the last sampled one); otherwise it is prefilling (a recomputed request
