@@ -20,10 +20,10 @@ def check_mode():
     pa.set_check(False)
 
 
-def run_i8(w, window=0, rows=None, what=""):
+def run_i8(w, window=0, rows=None, what="", max_q_len=0):
     st = w.steps[0]
     g = GpuState(w)
-    out_g = g.step(st, window=window)
+    out_g = g.step(st, window=window, max_q_len=max_q_len)
     kc, vc = w.k_cache0.copy(), w.v_cache0.copy()
     out_r, _ = oracle.run_step(w, st, kc, vc, rows=rows, window=window)
     assert np.array_equal(host_array(g.kc, "i8"), kc), f"{what}: K codes differ after append"
@@ -191,7 +191,8 @@ def test_int8_verify_rows(case):
 
 
 @pytest.mark.timeout(600)
-def test_int8_verify_at_decode_workload_size():
+@pytest.mark.parametrize("hint", [0, 4])
+def test_int8_verify_at_decode_workload_size(hint):
     w = W.verify_variant(W.CONFIGS["c5"](cache="i8"), 4)
-    say("int8 verify: c5 requests, 4 tokens each")
-    run_i8(w, what="c5 int8 verify 4")
+    say(f"int8 verify: c5 requests, 4 tokens each, q_len bound {hint}")
+    run_i8(w, what=f"c5 int8 verify 4 bound {hint}", max_q_len=hint)

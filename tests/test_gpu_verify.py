@@ -21,10 +21,10 @@ def check_mode():
     pa.set_check(False)
 
 
-def run(w, window=0, rows=None, what=""):
+def run(w, window=0, rows=None, what="", max_q_len=0):
     st = w.steps[0]
     g = GpuState(w)
-    out_g = g.step(st, window=window)
+    out_g = g.step(st, window=window, max_q_len=max_q_len)
     kc, vc = w.k_cache0.copy(), w.v_cache0.copy()
     out_r, _ = oracle.run_step(w, st, kc, vc, rows=rows, window=window)
     assert np.array_equal(host_array(g.kc, w.dtype), kc), f"{what}: K cache differs after append"
@@ -77,10 +77,12 @@ def test_verify_rows_equal_one_token_steps():
 
 
 @pytest.mark.timeout(600)
-@pytest.mark.parametrize("cfg,k", [("c2", 4), ("c5", 8)])
-def test_verify_batches_at_decode_workload_sizes(cfg, k):
+@pytest.mark.parametrize("cfg,k,hint", [("c2", 4, 0), ("c5", 8, 0), ("c2", 4, 4), ("c5", 4, 4)])
+def test_verify_batches_at_decode_workload_sizes(cfg, k, hint):
+    """Full-size verification steps, without and with the q_len bound the benchmark passes (the
+    bound changes how many positions a row's columns are planned for)."""
     w = W.verify_variant(W.CONFIGS[cfg](), k)
-    run(w, what=f"{cfg} verify {k}")
+    run(w, what=f"{cfg} verify {k} bound {hint}", max_q_len=hint)
 
 
 def test_max_q_len_hint_skips_tiles_and_matches():
