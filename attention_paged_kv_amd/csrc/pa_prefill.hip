@@ -309,8 +309,10 @@ __global__ __launch_bounds__(512, 1) void prefill_tile_kernel(TileArgs a) {
     constexpr int RPI8 = 1024 / D;                // int8 rows per wave-wide 1 KiB load
     constexpr int IPB8 = kBlock / RPI8;
     constexpr int TILE8 = kTileKeys * D;          // bytes per staged int8 tile
-    __shared__ __align__(16) char sK[TILEB];       // bf16 tiles the math reads
-    __shared__ __align__(16) char sV[TILEB];
+    __shared__ __align__(16) char sK0[TILEB];      // bf16 tiles the math reads, double buffered
+    __shared__ __align__(16) char sV0[TILEB];
+    __shared__ __align__(16) char sK1[TILEB];
+    __shared__ __align__(16) char sV1[TILEB];
     __shared__ __align__(16) char sK8a[TILE8];     // int8 staging, double buffered
     __shared__ __align__(16) char sV8a[TILE8];
     __shared__ __align__(16) char sK8b[TILE8];
@@ -345,9 +347,9 @@ __global__ __launch_bounds__(512, 1) void prefill_tile_kernel(TileArgs a) {
     // conversion: threads 0-255 widen K, 256-511 V (whole waves each); thread -> (row t / 4,
     // quarter t % 4 of its channels); 16 codes -> two bf16 chunks
     const int ct = tid & 255, crow = ct >> 2, cq = ct & 3;
-    char* const cdst = is_v ? sV : sK;
-    auto convert = [&](const char* k8, const char* v8) {
+    auto convert = [&](const char* k8, const char* v8, char* kd, char* vd) {
       const char* src = is_v ? v8 : k8;
+      char* const cdst = is_v ? vd : kd;
 #pragma unroll
       for (int u = 0; u < D / 64; ++u) {
         const int c16 = (D / 64) * cq + u;                    // 16-code piece of the row
@@ -363,21 +365,27 @@ __global__ __launch_bounds__(512, 1) void prefill_tile_kernel(TileArgs a) {
       }
     };
 
+    // Tile kt+1 is widened in the same phase as tile kt's math (other buffers), so one barrier
+    // per tile separates the phases: before it, tile kt+1's codes have landed (staged a phase
+    // earlier) and tile kt+2's copies are in flight.
     stage8(kt_lo, sK8a, sV8a);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
+    convert(sK8a, sV8a, sK0, sV0);
+    if (kt_lo + 1 < n_kt) stage8(kt_lo + 1, sK8b, sV8b);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
     for (int kt = kt_lo; kt < n_kt; kt += 2) {
-      convert(sK8a, sV8a);
-      __syncthreads();
-      if (kt + 1 < n_kt) stage8(kt + 1, sK8b, sV8b);
-      tile_math(kt, sK, sV);
+      // tile kt widened in (sK0, sV0); tile kt + 1's codes in b
+      if (kt + 1 < n_kt) convert(sK8b, sV8b, sK1, sV1);
+      if (kt + 2 < n_kt) stage8(kt + 2, sK8a, sV8a);       // a was widened a phase ago
+      tile_math(kt, sK0, sV0);
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       __syncthreads();
       if (kt + 1 >= n_kt) break;
-      convert(sK8b, sV8b);
-      __syncthreads();
-      if (kt + 2 < n_kt) stage8(kt + 2, sK8a, sV8a);
-      tile_math(kt + 1, sK, sV);
+      if (kt + 2 < n_kt) convert(sK8a, sV8a, sK0, sV0);     // tile kt's math is done
+      if (kt + 3 < n_kt) stage8(kt + 3, sK8b, sV8b);
+      tile_math(kt + 1, sK1, sV1);
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       __syncthreads();
     }
