@@ -47,19 +47,6 @@ template <bool BF16>
 struct Io;
 
 template <>
-struct Io<true> {
-  static constexpr int kEsz = 2;
-  static constexpr int kEpl = 8;   // elements per 16-byte load
-  __device__ static void widen(const uint4& u, float* f) {
-    f[0] = bf16_lo(u.x); f[1] = bf16_hi(u.x); f[2] = bf16_lo(u.y); f[3] = bf16_hi(u.y);
-    f[4] = bf16_lo(u.z); f[5] = bf16_hi(u.z); f[6] = bf16_lo(u.w); f[7] = bf16_hi(u.w);
-  }
-  __device__ static void store(void* base, int64_t idx, float v) {
-    reinterpret_cast<uint16_t*>(base)[idx] = f32_to_bf16(v);
-  }
-};
-
-template <>
 struct Io<false> {
   static constexpr int kEsz = 4;
   static constexpr int kEpl = 4;
