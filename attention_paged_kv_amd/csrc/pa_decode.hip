@@ -1,11 +1,11 @@
-// pa_decode.hip -- split-KV attention for single query rows, and the cross-split merge.
+// pa_decode.hip -- split-KV attention for decode rows (and rows of a few tokens to verify), and the
+// cross-split merge.
 //
 // A decode step reads every cached key and value of its request once (P3 §3.1-3.2, §6.3): the
-// pass is bound by HBM bandwidth, not arithmetic.  Work unit = (query row, KV head and a group of
-// its query heads, split of `split` keys).  A workgroup loads each K/V row of its KV head once and
-// uses it for all the query heads it owns (grouped-query sharing, P3 §2.3).  Each wave of the
-// workgroup streams every 4th 16-key block of the split with an online softmax; the four waves are
-// merged at the end, and the splits of one row are merged by a second kernel with
+// pass is bound by HBM bandwidth, not arithmetic.  Work unit = (query row, KV heads and their
+// query heads, split of `split` keys).  Each K/V row of a KV head is loaded once and used for all
+// the query heads it serves (grouped-query sharing, P3 §2.3), with an online softmax over the
+// split's 16-key blocks; the splits of one row are merged by a second kernel with
 //   m = max_s m_s,  l = sum_s 2^(m_s - m) l_s,  o = sum_s 2^(m_s - m) o_s / l
 // (scores are kept in log2 units: x * scale * log2 e).  The pages do not describe how partial
 // softmaxes combine; this is the exact decomposition of the row softmax of P3 §3.1.
@@ -14,15 +14,17 @@
 // exactly like a split.
 //
 // bf16 caches: matrix cores do the arithmetic so that the vector ALUs stay idle however many
-// query heads share a KV head.  Per 16-key block and wave:
-//   S^T (16 keys x 16 query heads) = K (16 x d) . Q^T   -- v_mfma_f32_16x16x32_bf16, K loaded
-//                                                          from HBM straight into A-operand lanes
-//   O^T (d x 16 heads) += V^T (d x 16 keys) . P^T       -- v_mfma_f32_16x16x16_bf16; V is staged
-//       row-major in a per-wave LDS block and read back transposed with ds_read_b64_tr_b16
+// query heads share a KV head.  A workgroup's four waves own four adjacent KV heads; per 16-key
+// block and wave (K and V copied into a per-wave LDS slot by direct global->LDS loads):
+//   S^T (16 keys x 16 columns) = K (16 x d) . Q^T       -- v_mfma_f32_16x16x32_bf16, K read back
+//                                                          from LDS as A operands
+//   O^T (d x 16 columns) += V^T (d x 16 keys) . P^T     -- v_mfma_f32_16x16x16_bf16, V read back
+//       transposed with ds_read_b64_tr_b16
 // P^T stays in registers: the S^T accumulator layout (lane = head, 4 keys) is exactly the B
 // operand layout of the second product.  Unused head columns are zero.
-// fp32 caches: vector-ALU kernel (dot products reduced across 16-lane rows with DPP), serving every
-// query row of an fp32 batch.
+// fp32 caches: vector-ALU kernel (dot products reduced across 16-lane rows with DPP; the four
+// waves of a workgroup take every 4th block of the split and are merged at the end), serving
+// every query row of an fp32 batch.
 #include <cstdlib>
 #include <type_traits>
 

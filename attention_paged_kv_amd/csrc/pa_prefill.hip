@@ -34,8 +34,8 @@
 // 8-bit caches (P2 §4.3, §5.4: int8 codes with a scale per KV head and channel): the cache blocks
 // are copied to int8 staging buffers the same way, then the workgroup converts each tile once into
 // the bf16 tile layout above (exact: |code| <= 127), so the tile math is unchanged; the K scale is
-// folded into the query (q * k_scale rounded to bf16) and the V scale multiplies O at the end.  One
-// more barrier per tile separates the conversion from the math.
+// folded into the query (q * k_scale rounded to bf16) and the V scale multiplies O at the end.  The
+// bf16 tiles are double buffered: tile kt + 1 is converted in the same phase as tile kt's math.
 #include "pa_common.h"
 #include "pa_internal.h"
 
