@@ -42,6 +42,8 @@
 namespace pa {
 
 namespace {
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
 // Physical 16-byte chunk of logical chunk q in tile row r (bijective per row).
 template <int D>
 __device__ __forceinline__ int swz(int r) {
@@ -205,7 +207,7 @@ __global__ __launch_bounds__(512, 1) void prefill_tile_kernel(TileArgs a) {
     // ---- online softmax (scores in log2 units via c = scale * log2 e), lazy rescale ----
     float tm = fmaxf(S0[0], S1[0]);
 #pragma unroll
-    for (int v = 1; v < 16; ++v) tm = fmaxf(tm, fmaxf(S0[v], S1[v]));
+    for (int v = 1; v < 16; ++v) tm = fmaxf(fmaxf(tm, S0[v]), S1[v]);   // one v_max3 per v
     tm = xor32_max(tm);
     const float mn = fmaxf(m_run, tm);
     if (__any((mn - m_run) * c > 8.f)) {
@@ -219,16 +221,22 @@ __global__ __launch_bounds__(512, 1) void prefill_tile_kernel(TileArgs a) {
     }
     const float mc = (m_run == -INFINITY) ? 0.f : m_run * c;   // a row that has seen no key yet
     bf16x8 P[4];
-    float ps = 0.f;
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
-      const float p0 = fast_exp2(fmaf(S0[v], c, -mc));
-      const float p1 = fast_exp2(fmaf(S1[v], c, -mc));
-      ps += p0 + p1;
-      P[v >> 3][v & 7] = (__bf16)p0;
-      P[2 + (v >> 3)][v & 7] = (__bf16)p1;
+      P[v >> 3][v & 7] = (__bf16)fast_exp2(fmaf(S0[v], c, -mc));
+      P[2 + (v >> 3)][v & 7] = (__bf16)fast_exp2(fmaf(S1[v], c, -mc));
     }
-    l_run += ps;
+    // row sum of the bf16 probabilities the products use, two per v_dot2c_f32_bf16 against (1, 1)
+    const bf16x2 one2 = {(__bf16)1.f, (__bf16)1.f};
+    float ps0 = 0.f, ps1 = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      ps0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(P[i], P[i], 0, 1), one2, ps0, false);
+      ps1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(P[i], P[i], 2, 3), one2, ps1, false);
+      ps0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(P[i], P[i], 4, 5), one2, ps0, false);
+      ps1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(P[i], P[i], 6, 7), one2, ps1, false);
+    }
+    l_run += ps0 + ps1;
 
     // ---- O^T += V^T P^T : A operand = two 4-key transpose reads per 16-key step ----
 #pragma unroll
