@@ -352,24 +352,33 @@ __global__ __launch_bounds__(512, 1) void prefill_tile_kernel(TileArgs a) {
         }
       }
     };
-    // conversion: threads 0-255 widen K, 256-511 V (whole waves each); thread -> (row t / 4,
-    // quarter t % 4 of its channels); 16 codes -> two bf16 chunks
-    const int ct = tid & 255, crow = ct >> 2, cq = ct & 3;
+    // conversion: threads 0-255 widen K, 256-511 V (whole waves each); thread -> (row, 16-code
+    // piece cj of it), the PPR threads of a row adjacent, so 16 lanes read 256 contiguous bytes.
+    // Each piece becomes two bf16 chunks, stored in the order set by the row's parity: the 16
+    // stores of a lane group then land on 16 different physical chunks (rows r and r + 1 write
+    // chunks of opposite parity under the swizzle), which keeps the stores free of bank conflicts.
+    constexpr int PPR = D / 16;                   // 16-code pieces per row
+    constexpr int RPP = 256 / PPR;                // rows per pass
+    const int ct = tid & 255, cj = ct % PPR, crow0 = ct / PPR;
+    const int h0 = crow0 & 1;                     // RPP is even: every pass keeps the parity
+    auto widen8 = [](uint32_t w0, uint32_t w1) {
+      bf16x8 o;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[e] = (__bf16)(float)(signed char)((e < 4 ? w0 : w1) >> (8 * (e & 3)));
+      return o;
+    };
     auto convert = [&](const char* k8, const char* v8, char* kd, char* vd) {
       const char* src = is_v ? v8 : k8;
       char* const cdst = is_v ? vd : kd;
 #pragma unroll
-      for (int u = 0; u < D / 64; ++u) {
-        const int c16 = (D / 64) * cq + u;                    // 16-code piece of the row
-        const uint4 x = *reinterpret_cast<const uint4*>(src + crow * D + 16 * c16);
-        const uint32_t wx[4] = {x.x, x.y, x.z, x.w};
-#pragma unroll
-        for (int hq = 0; hq < 2; ++hq) {                      // logical bf16 chunk 2 * c16 + hq
-          bf16x8 o;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) o[e] = (__bf16)(float)(signed char)(wx[2 * hq + e / 4] >> (8 * (e & 3)));
-          *reinterpret_cast<bf16x8*>(cdst + crow * ROWB + (((2 * c16 + hq) ^ swz<D>(crow)) * 16)) = o;
-        }
+      for (int u = 0; u < 64 / RPP; ++u) {
+        const int crow = crow0 + RPP * u;
+        const uint4 x = *reinterpret_cast<const uint4*>(src + crow * D + 16 * cj);
+        const bf16x8 first = widen8(h0 ? x.z : x.x, h0 ? x.w : x.y);     // logical chunk 2cj + h0
+        const bf16x8 second = widen8(h0 ? x.x : x.z, h0 ? x.y : x.w);    // logical chunk 2cj + 1 - h0
+        char* const rowp = cdst + crow * ROWB;
+        *reinterpret_cast<bf16x8*>(rowp + (((2 * cj + h0) ^ swz<D>(crow)) * 16)) = first;
+        *reinterpret_cast<bf16x8*>(rowp + (((2 * cj + (h0 ^ 1)) ^ swz<D>(crow)) * 16)) = second;
       }
     };
 
