@@ -168,10 +168,14 @@ def workspace_size(num_seqs, num_q_tokens, max_blocks_per_seq, num_q_heads, k_ca
 
 
 def _workspace(dev, nbytes):
+    """The binding's cached workspace for (device, current stream): calls queued on one stream run
+    in order, so they may share one buffer; calls on different streams get different buffers."""
     import torch
-    key = (dev.type, dev.index)
+    stream = torch.cuda.current_stream(dev)
+    key = (dev.index, stream.cuda_stream)
     ws = _workspaces.get(key)
     if ws is None or ws.numel() < nbytes:
+        # allocated while `stream` is current, so the caching allocator ties the block to it
         ws = torch.empty(max(nbytes, 1 << 20), dtype=torch.uint8, device=dev)
         _workspaces[key] = ws
     return ws

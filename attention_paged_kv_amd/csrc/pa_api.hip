@@ -11,7 +11,9 @@
 #include <cstdlib>
 #include <mutex>
 #include <string>
+#include <map>
 #include <unordered_map>
+#include <utility>
 #include <vector>
 
 #include "pa.h"
@@ -73,15 +75,25 @@ int split_tokens(int64_t span, bool bound) {
   return (span > 8192 && !bound) ? pa::kLongSplitTokens : pa::kDefaultSplitTokens;
 }
 
-// ---- per-device state: library-owned workspace and the check-mode result slot ----
+// ---- per-device state: the check-mode result slot and the compute-unit count ----
 struct DevState {
-  void* ws = nullptr;
-  size_t ws_bytes = 0;
   int* check = nullptr;
   int cus = 0;            // compute units
 };
 std::mutex g_dev_mu;
 std::unordered_map<int, DevState> g_dev;
+
+// ---- library-owned workspaces (calls given a NULL workspace): one per (device, stream) ----
+// Calls on one stream run in stream order, so a buffer used by one stream only is never in use
+// by two kernels at once.  g_ws_mu is held from the lookup until every kernel of the call is
+// queued: a buffer is only grown (old one freed after its stream has drained) while no other
+// call on that stream can be between its lookup and its launches.
+struct StreamWs {
+  void* ptr = nullptr;
+  size_t bytes = 0;
+};
+std::mutex g_ws_mu;
+std::map<std::pair<int, uintptr_t>, StreamWs> g_ws;
 
 // ---- kernel timing ----
 struct TimedLaunch {
@@ -290,13 +302,17 @@ int ensure_check_slot(int dev, int*& slot) {
   return PA_OK;
 }
 
-int run_check(const pa::CheckArgs& base, hipStream_t s) {
-  int dev = 0;
-  int rc = get_device(dev);
-  if (rc) return rc;
-  int* slot = nullptr;
-  rc = ensure_check_slot(dev, slot);
-  if (rc) return rc;
+// Validator kernel over the index arguments; `slot` (4 ints of device memory) receives its
+// result, or the device's own slot is used when it is null.
+int run_check(const pa::CheckArgs& base, hipStream_t s, int* slot = nullptr) {
+  int rc;
+  if (!slot) {
+    int dev = 0;
+    rc = get_device(dev);
+    if (rc) return rc;
+    rc = ensure_check_slot(dev, slot);
+    if (rc) return rc;
+  }
   pa::CheckArgs a = base;
   a.result = slot;
   hipError_t e = hipMemsetAsync(slot, 0, 4 * sizeof(int), s);
@@ -316,6 +332,142 @@ int run_check(const pa::CheckArgs& base, hipStream_t s) {
   return fail(PA_ERR_CHECK_FAILED, "check mode: %s (index %d, value %d)", what[code], host[2], host[3]);
 }
 
+// The arguments of one attention call.
+struct Call {
+  const void* q;
+  int32_t T, Hq;
+  const void* k_cache;
+  const void* v_cache;
+  const pa_cache_desc* cache;
+  const int32_t* block_tables;
+  int32_t B, MB;
+  const int32_t* seq_lens;
+  const int32_t* qsl;
+  float scale;
+  void* out;
+  int window, max_q_len;
+};
+
+// Host checks shared by every attention entry point, and the plan of the call.
+int prepare(const Call& c, const pa_attention_opts* opts, Call& full, Plan& p) {
+  full = c;
+  full.window = pa::kNoWindow;
+  full.max_q_len = 0;
+  if (opts) {
+    if (opts->sliding_window < 0)
+      return fail(PA_ERR_INVALID_ARG, "sliding_window must be >= 0 (got %d)", opts->sliding_window);
+    if (opts->sliding_window > 0 && opts->sliding_window < pa::kNoWindow) full.window = opts->sliding_window;
+    if (opts->max_q_len < 0) return fail(PA_ERR_INVALID_ARG, "max_q_len must be >= 0 (got %d)", opts->max_q_len);
+    full.max_q_len = opts->max_q_len;
+  }
+  int rc = make_plan(c.B, c.T, c.MB, c.Hq, c.cache, full.window, full.max_q_len, p);
+  if (rc) return rc;
+  if (!c.q || !c.k_cache || !c.v_cache || !c.block_tables || !c.seq_lens || !c.qsl || !c.out)
+    return fail(PA_ERR_INVALID_ARG, "null pointer argument");
+  if (c.out == c.q || c.out == c.k_cache || c.out == c.v_cache) return fail(PA_ERR_INVALID_ARG, "out must not alias inputs");
+  if (misaligned(c.q) || misaligned(c.k_cache) || misaligned(c.v_cache) || misaligned(c.out))
+    return fail(PA_ERR_INVALID_ARG, "q, the caches, out and the workspace must be 16-byte aligned");
+  // the kernels track the running max of raw scores and apply the scale afterwards, which needs
+  // scale > 0
+  if (!std::isfinite(c.scale) || !(c.scale > 0.f))
+    return fail(PA_ERR_INVALID_ARG, "scale must be finite and > 0 (got %g)", (double)c.scale);
+  return PA_OK;
+}
+
+// Queues the call's kernels on `s`, with `ws` holding at least p.total bytes (null when p.total
+// is 0).  Allocates nothing when `check_slot` is given (check mode then reports through it).
+int launch_call(const Call& c, const Plan& p, char* ws, hipStream_t s, int* check_slot) {
+  int rc;
+  const pa_cache_desc* cache = c.cache;
+  if (check_on()) {
+    pa::CheckArgs ck{};
+    ck.block_tables = c.block_tables;
+    ck.seq_lens = c.seq_lens;
+    ck.qsl = c.qsl;
+    ck.num_seqs = c.B;
+    ck.max_blocks = c.MB;
+    ck.num_blocks = cache->num_blocks;
+    ck.num_q_tokens = c.T;
+    ck.window = c.window;
+    ck.max_q_len = c.max_q_len;
+    rc = run_check(ck, s, check_slot);
+    if (rc) return rc;
+  }
+
+  const float scale_log2 = c.scale * 1.4426950408889634f;
+  if (p.run_decode) {
+    pa::DecodeArgs d{};
+    d.q = c.q;
+    d.k_cache = c.k_cache;
+    d.v_cache = c.v_cache;
+    d.block_tables = c.block_tables;
+    d.seq_lens = c.seq_lens;
+    d.qsl = c.qsl;
+    d.out = c.out;
+    d.part_o = p.max_splits > 1 ? reinterpret_cast<float*>(ws + p.off_o) : nullptr;
+    d.part_ml = p.max_splits > 1 ? reinterpret_cast<float*>(ws + p.off_ml) : nullptr;
+    d.num_seqs = c.B;
+    d.num_rows = p.rows;
+    d.per_token = p.per_token;
+    d.qmax = p.qmax;
+    d.num_q_heads = c.Hq;
+    d.num_kv_heads = cache->num_kv_heads;
+    d.group = p.group;
+    d.heads_per_wg = p.heads_per_wg;
+    d.max_blocks = c.MB;
+    d.split = p.split;
+    d.max_splits = p.max_splits;
+    d.stream_wgs = 0;
+    if (p.stream) {
+      rc = stream_wgs(p, cache->num_kv_heads, d.stream_wgs);
+      if (rc) return rc;
+    }
+    d.window = c.window;
+    d.scale_log2 = scale_log2;
+    d.k_scale = cache->k_scale;
+    d.v_scale = cache->v_scale;
+    hipError_t e = timed("decode_split", s, [&] {
+      return p.i8 ? pa::launch_decode_split_i8(d, p.head_dim, s) : pa::launch_decode_split(d, p.head_dim, p.bf16, s);
+    });
+    if (e != hipSuccess) return device_fail(e, "decode split launch");
+    if (p.max_splits > 1) {
+      e = timed("decode_merge", s, [&] { return pa::launch_decode_merge(d, p.head_dim, p.bf16, s); });
+      if (e != hipSuccess) return device_fail(e, "decode merge launch");
+    }
+  }
+  if (p.run_tiles) {
+    int4* tiles = reinterpret_cast<int4*>(ws + p.off_tiles);
+    int* ntiles = reinterpret_cast<int*>(ws + p.off_ntiles);
+    hipError_t e = timed("plan", s, [&] {
+      return pa::launch_plan_tiles(c.qsl, c.B, p.pos_per_tile, p.qmax + 1, tiles, ntiles, s);
+    });
+    if (e != hipSuccess) return device_fail(e, "plan launch");
+    pa::TileArgs t{};
+    t.q = c.q;
+    t.k_cache = c.k_cache;
+    t.v_cache = c.v_cache;
+    t.block_tables = c.block_tables;
+    t.seq_lens = c.seq_lens;
+    t.qsl = c.qsl;
+    t.out = c.out;
+    t.tiles = tiles;
+    t.num_tiles = ntiles;
+    t.num_slots = p.num_slots;
+    t.num_q_heads = c.Hq;
+    t.num_kv_heads = cache->num_kv_heads;
+    t.group = p.group;
+    t.pos_per_tile = p.pos_per_tile;
+    t.max_blocks = c.MB;
+    t.window = c.window;
+    t.scale_log2 = scale_log2;
+    t.k_scale = cache->k_scale;
+    t.v_scale = cache->v_scale;
+    e = timed("prefill_tile", s, [&] { return pa::launch_prefill_tile(t, p.head_dim, p.i8, s); });
+    if (e != hipSuccess) return device_fail(e, "prefill tile launch");
+  }
+  return PA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -327,17 +479,27 @@ const char* pa_last_error(void) { return g_err.c_str(); }
 void pa_set_check(int on) { g_check.store(on ? 1 : 0); }
 
 void pa_release(void) {   // best effort: errors here have nowhere to go
-  std::lock_guard<std::mutex> lk(g_dev_mu);
   int cur = 0;
   (void)hipGetDevice(&cur);
-  for (auto& kv : g_dev) {
-    (void)hipSetDevice(kv.first);
-    (void)hipDeviceSynchronize();
-    if (kv.second.ws) (void)hipFree(kv.second.ws);
-    if (kv.second.check) (void)hipFree(kv.second.check);
-    kv.second = DevState{};
+  {
+    std::lock_guard<std::mutex> lk(g_ws_mu);
+    for (auto& kv : g_ws) {
+      (void)hipSetDevice(kv.first.first);
+      (void)hipDeviceSynchronize();
+      if (kv.second.ptr) (void)hipFree(kv.second.ptr);
+    }
+    g_ws.clear();
   }
-  g_dev.clear();
+  {
+    std::lock_guard<std::mutex> lk(g_dev_mu);
+    for (auto& kv : g_dev) {
+      (void)hipSetDevice(kv.first);
+      (void)hipDeviceSynchronize();
+      if (kv.second.check) (void)hipFree(kv.second.check);
+      kv.second = DevState{};
+    }
+    g_dev.clear();
+  }
   (void)hipSetDevice(cur);
 }
 
@@ -386,142 +548,41 @@ int pa_attention_ex(const void* q, int32_t num_q_tokens, int32_t num_q_heads, co
                     void* out, void* workspace, size_t workspace_bytes, const pa_attention_opts* opts,
                     void* stream) {
   g_err.clear();
-  int window = pa::kNoWindow, max_q_len = 0;
-  if (opts) {
-    if (opts->sliding_window < 0)
-      return fail(PA_ERR_INVALID_ARG, "sliding_window must be >= 0 (got %d)", opts->sliding_window);
-    if (opts->sliding_window > 0 && opts->sliding_window < pa::kNoWindow) window = opts->sliding_window;
-    if (opts->max_q_len < 0) return fail(PA_ERR_INVALID_ARG, "max_q_len must be >= 0 (got %d)", opts->max_q_len);
-    max_q_len = opts->max_q_len;
-  }
+  const Call given{q, num_q_tokens, num_q_heads, k_cache, v_cache, cache, block_tables, num_seqs,
+                   max_blocks_per_seq, seq_lens, query_start_loc, scale, out, 0, 0};
+  Call c;
   Plan p;
-  int rc = make_plan(num_seqs, num_q_tokens, max_blocks_per_seq, num_q_heads, cache, window, max_q_len, p);
+  int rc = prepare(given, opts, c, p);
   if (rc) return rc;
-  if (!q || !k_cache || !v_cache || !block_tables || !seq_lens || !query_start_loc || !out)
-    return fail(PA_ERR_INVALID_ARG, "null pointer argument");
-  if (out == q || out == k_cache || out == v_cache) return fail(PA_ERR_INVALID_ARG, "out must not alias inputs");
-  if (misaligned(q) || misaligned(k_cache) || misaligned(v_cache) || misaligned(out) || misaligned(workspace))
-    return fail(PA_ERR_INVALID_ARG, "q, the caches, out and the workspace must be 16-byte aligned");
-  // the kernels track the running max of raw scores and apply the scale afterwards, which needs
-  // scale > 0
-  if (!std::isfinite(scale) || !(scale > 0.f))
-    return fail(PA_ERR_INVALID_ARG, "scale must be finite and > 0 (got %g)", (double)scale);
+  if (misaligned(workspace)) return fail(PA_ERR_INVALID_ARG, "q, the caches, out and the workspace must be 16-byte aligned");
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-
-  char* ws = static_cast<char*>(workspace);
-  if (p.total > 0) {
-    if (ws) {
-      if (workspace_bytes < p.total)
-        return fail(PA_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu needed", workspace_bytes, p.total);
-    } else {
-      int dev = 0;
-      rc = get_device(dev);
-      if (rc) return rc;
-      std::lock_guard<std::mutex> lk(g_dev_mu);
-      DevState& st = g_dev[dev];
-      if (st.ws_bytes < p.total) {
-        if (st.ws) {
-          hipError_t e = hipDeviceSynchronize();             // earlier calls may still use it
-          if (e == hipSuccess) e = hipFree(st.ws);
-          st.ws = nullptr;
-          st.ws_bytes = 0;
-          if (e != hipSuccess) return device_fail(e, "releasing the old workspace");
-        }
-        hipError_t e = hipMalloc(&st.ws, p.total);
-        if (e != hipSuccess) return device_fail(e, "hipMalloc(workspace)");
-        st.ws_bytes = p.total;
-      }
-      ws = static_cast<char*>(st.ws);
+  if (p.total == 0) return launch_call(c, p, nullptr, s, nullptr);
+  if (workspace) {
+    if (workspace_bytes < p.total)
+      return fail(PA_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu needed", workspace_bytes, p.total);
+    return launch_call(c, p, static_cast<char*>(workspace), s, nullptr);
+  }
+  // library-owned buffer of this (device, stream), held locked until the kernels are queued
+  int dev = 0;
+  rc = get_device(dev);
+  if (rc) return rc;
+  std::lock_guard<std::mutex> lk(g_ws_mu);
+  StreamWs& ws = g_ws[{dev, reinterpret_cast<uintptr_t>(s)}];
+  if (ws.bytes < p.total) {
+    if (ws.ptr) {
+      hipError_t e = hipStreamSynchronize(s);               // the stream's earlier calls may still read it
+      if (e == hipSuccess) e = hipFree(ws.ptr);
+      ws = StreamWs{};
+      if (e != hipSuccess) return device_fail(e, "releasing the old workspace");
     }
-  }
-
-  if (check_on()) {
-    pa::CheckArgs c{};
-    c.block_tables = block_tables;
-    c.seq_lens = seq_lens;
-    c.qsl = query_start_loc;
-    c.num_seqs = num_seqs;
-    c.max_blocks = max_blocks_per_seq;
-    c.num_blocks = cache->num_blocks;
-    c.num_q_tokens = num_q_tokens;
-    c.window = window;
-    c.max_q_len = max_q_len;
-    rc = run_check(c, s);
-    if (rc) return rc;
-  }
-
-  const float scale_log2 = scale * 1.4426950408889634f;
-  if (p.run_decode) {
-    pa::DecodeArgs d{};
-    d.q = q;
-    d.k_cache = k_cache;
-    d.v_cache = v_cache;
-    d.block_tables = block_tables;
-    d.seq_lens = seq_lens;
-    d.qsl = query_start_loc;
-    d.out = out;
-    d.part_o = p.max_splits > 1 ? reinterpret_cast<float*>(ws + p.off_o) : nullptr;
-    d.part_ml = p.max_splits > 1 ? reinterpret_cast<float*>(ws + p.off_ml) : nullptr;
-    d.num_seqs = num_seqs;
-    d.num_rows = p.rows;
-    d.per_token = p.per_token;
-    d.qmax = p.qmax;
-    d.num_q_heads = num_q_heads;
-    d.num_kv_heads = cache->num_kv_heads;
-    d.group = p.group;
-    d.heads_per_wg = p.heads_per_wg;
-    d.max_blocks = max_blocks_per_seq;
-    d.split = p.split;
-    d.max_splits = p.max_splits;
-    d.stream_wgs = 0;
-    if (p.stream) {
-      rc = stream_wgs(p, cache->num_kv_heads, d.stream_wgs);
-      if (rc) return rc;
+    hipError_t e = hipMalloc(&ws.ptr, p.total);
+    if (e != hipSuccess) {
+      ws = StreamWs{};
+      return device_fail(e, "hipMalloc(workspace)");
     }
-    d.window = window;
-    d.scale_log2 = scale_log2;
-    d.k_scale = cache->k_scale;
-    d.v_scale = cache->v_scale;
-    hipError_t e = timed("decode_split", s, [&] {
-      return p.i8 ? pa::launch_decode_split_i8(d, p.head_dim, s) : pa::launch_decode_split(d, p.head_dim, p.bf16, s);
-    });
-    if (e != hipSuccess) return device_fail(e, "decode split launch");
-    if (p.max_splits > 1) {
-      e = timed("decode_merge", s, [&] { return pa::launch_decode_merge(d, p.head_dim, p.bf16, s); });
-      if (e != hipSuccess) return device_fail(e, "decode merge launch");
-    }
+    ws.bytes = p.total;
   }
-  if (p.run_tiles) {
-    int4* tiles = reinterpret_cast<int4*>(ws + p.off_tiles);
-    int* ntiles = reinterpret_cast<int*>(ws + p.off_ntiles);
-    hipError_t e = timed("plan", s, [&] {
-      return pa::launch_plan_tiles(query_start_loc, num_seqs, p.pos_per_tile, p.qmax + 1, tiles, ntiles, s);
-    });
-    if (e != hipSuccess) return device_fail(e, "plan launch");
-    pa::TileArgs t{};
-    t.q = q;
-    t.k_cache = k_cache;
-    t.v_cache = v_cache;
-    t.block_tables = block_tables;
-    t.seq_lens = seq_lens;
-    t.qsl = query_start_loc;
-    t.out = out;
-    t.tiles = tiles;
-    t.num_tiles = ntiles;
-    t.num_slots = p.num_slots;
-    t.num_q_heads = num_q_heads;
-    t.num_kv_heads = cache->num_kv_heads;
-    t.group = p.group;
-    t.pos_per_tile = p.pos_per_tile;
-    t.max_blocks = max_blocks_per_seq;
-    t.window = window;
-    t.scale_log2 = scale_log2;
-    t.k_scale = cache->k_scale;
-    t.v_scale = cache->v_scale;
-    e = timed("prefill_tile", s, [&] { return pa::launch_prefill_tile(t, p.head_dim, p.i8, s); });
-    if (e != hipSuccess) return device_fail(e, "prefill tile launch");
-  }
-  return PA_OK;
+  return launch_call(c, p, static_cast<char*>(ws.ptr), s, nullptr);
 }
 
 int pa_attention(const void* q, int32_t num_q_tokens, int32_t num_q_heads, const void* k_cache, const void* v_cache,

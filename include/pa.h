@@ -123,8 +123,10 @@ size_t pa_attention_workspace_size(int32_t num_seqs, int32_t num_q_tokens, int32
  * at absolute position ctx + r and attends to keys 0 .. ctx + r, read through block_tables[b].
  * Query head h uses KV head h / (Hq/Hkv).
  *   out[t][h][:] = sum_j softmax_j(scale * <q[t][h], K[j][g]>) * V[j][g]
- * where for I8 caches K[j][g][c] = code * k_scale[g][c] and V likewise (q and out are bf16; the
- * product q[c] * k_scale[g][c] is rounded to bf16 before it meets the codes).
+ * where for I8 caches K[j][g][c] = code * k_scale[g][c] and V likewise (q and out are bf16).  The
+ * product q[c] * k_scale[g][c] is rounded once before it meets the codes: to fp16 after scaling
+ * each query head by a power of two on the split-KV pass (rows of q_len <= 8), to bf16 on the
+ * prefill tiles (longer rows); both are rounding choices inside the bf16 tolerance.
  *
  *   q                device [num_q_tokens][num_q_heads][d], cache->dtype.
  *   k_cache, v_cache device, layout above (already holding this step's appended K/V).
@@ -139,7 +141,9 @@ size_t pa_attention_workspace_size(int32_t num_seqs, int32_t num_q_tokens, int32
  *                    Accumulation is fp32 for both dtypes; bf16 output is rounded to nearest even.
  *   workspace        device scratch of at least pa_attention_workspace_size() bytes, owned by
  *                    the caller and not used concurrently by another call; NULL = use a
- *                    library-owned per-device buffer (grown with hipMalloc, which synchronises).
+ *                    library-owned buffer of this (device, stream) pair.  Calls on one stream
+ *                    share it safely (stream order); growing it synchronises that stream, then
+ *                    frees and reallocates it (hipMalloc).  Such buffers live until pa_release().
  * Device-side index errors (bad q_len/seq_len, block id outside [0, NB)) are undefined unless
  * check mode is on.  num_q_heads must be a multiple of Hkv; for bf16, Hq/Hkv <= 128.
  */

@@ -82,3 +82,21 @@ def compare(out_gpu, out_ref, dtype, rows=None, what=""):
     assert maxabs <= TOL[dtype], f"{what}: max-abs {maxabs} > {TOL[dtype]}"
     assert rel <= ROW_REL_L2[dtype], f"{what}: row rel-L2 {rel} > {ROW_REL_L2[dtype]}"
     return maxabs, rel
+
+
+def tile_rows(q0, q_len, pos_per_tile, rng, n_random=16, waves=8):
+    """Query rows that touch every prefill tile of one request: each tile's first and last row,
+    one row in each wave's slice of the tile (a wave holds pos_per_tile / waves consecutive
+    positions), plus random rows.  Rows are token indices (q0 + local row)."""
+    rows = set()
+    per_wave = max(1, pos_per_tile // waves)
+    n_tiles = (q_len + pos_per_tile - 1) // pos_per_tile
+    for i in range(n_tiles):
+        lo, hi = i * pos_per_tile, min(q_len, (i + 1) * pos_per_tile)
+        rows.update((lo, hi - 1))
+        for wv in range(waves):
+            r = lo + wv * per_wave + (3 * i + 5 * wv) % per_wave
+            if r < hi:
+                rows.add(r)
+    rows.update(int(x) for x in rng.integers(0, q_len, n_random))
+    return q0 + np.array(sorted(rows), dtype=np.int64)

@@ -8,7 +8,7 @@ import pytest
 import attention_paged_kv_amd as pa
 from attention_paged_kv_amd import workloads as W
 import oracle
-from tests.gpu_helpers import GpuState, compare, host_array, say
+from tests.gpu_helpers import GpuState, compare, host_array, say, tile_rows
 
 pytestmark = pytest.mark.gpu
 
@@ -139,18 +139,17 @@ def test_int8_chunk_rows_with_window(window):
 
 
 @pytest.mark.timeout(600)
-def test_int8_c3_prefill_8k_sampled_rows():
-    rows = np.unique(np.concatenate([[0, 1, 2, 15, 16, 127, 128, 129, 4095, 4096, 8190, 8191],
-                                     np.random.default_rng(9).integers(0, 8192, 16)]))
-    run_i8(W.config3(cache="i8"), rows=rows, what="c3 int8 sampled rows")
+def test_int8_c3_prefill_8k_every_tile():
+    """Every 256-row tile of the 8k prefill over an int8 cache (all KV heads): first and last rows,
+    a row per wave, random rows."""
+    rows = tile_rows(0, 8192, 256, np.random.default_rng(3), n_random=24)
+    run_i8(W.config3(cache="i8"), rows=rows, what="c3 int8 rows of every tile")
 
 
 @pytest.mark.timeout(600)
-def test_int8_c4_mixed_chunk():
-    rng = np.random.default_rng(10)
-    chunk_rows = 30 + np.unique(np.concatenate([[0, 1, 31, 32, 2047], rng.integers(0, 2048, 12)]))
-    rows = np.concatenate([np.arange(30), chunk_rows])
-    run_i8(W.config4(cache="i8"), rows=rows, what="c4 int8 decodes + sampled chunk rows")
+def test_int8_c4_mixed_chunk_every_tile():
+    rows = np.concatenate([np.arange(30), tile_rows(30, 2048, 64, np.random.default_rng(4))])
+    run_i8(W.config4(cache="i8"), rows=rows, what="c4 int8 decodes + rows of every chunk tile")
 
 
 @pytest.mark.timeout(600)

@@ -10,7 +10,7 @@ import torch
 import attention_paged_kv_amd as pa
 from attention_paged_kv_amd import workloads as W
 import oracle
-from tests.gpu_helpers import DEV, GpuState, compare, dev_tensor, host_array, int_tensor, say
+from tests.gpu_helpers import DEV, GpuState, compare, dev_tensor, host_array, int_tensor, say, tile_rows
 
 pytestmark = pytest.mark.gpu
 
@@ -130,27 +130,143 @@ def test_c2_decode_batch():
 
 
 @pytest.mark.timeout(600)
-def test_c3_prefill_8k_sampled_rows():
+def test_c3_prefill_8k_every_tile():
+    """Every 256-row tile (all 32 KV heads, so every workgroup of the launch): its first and last
+    rows, one row in each wave's slice, plus random rows."""
     w = W.config3()
-    rows = np.unique(np.concatenate([[0, 1, 2, 15, 16, 127, 128, 129, 255, 4095, 4096, 8190, 8191],
-                                     np.random.default_rng(0).integers(0, 8192, 24)]))
-    run_and_compare(w, rows=rows, what="c3 sampled rows")
+    rows = tile_rows(0, 8192, 256 // (w.num_q_heads // w.num_kv_heads), np.random.default_rng(0), n_random=24)
+    say(f"c3: {len(rows)} rows")
+    run_and_compare(w, rows=rows, what="c3 rows of every tile")
 
 
 @pytest.mark.timeout(600)
-def test_c4_mixed_chunk():
+def test_c4_mixed_chunk_every_tile():
+    """Every decode row and, for the chunk, every 64-position tile (first and last rows, a row per
+    wave) plus random rows."""
+    w = W.config4()
+    rows = np.concatenate([np.arange(30), tile_rows(30, 2048, 256 // 4, np.random.default_rng(1))])
+    say(f"c4: {len(rows)} rows")
+    run_and_compare(w, rows=rows, what="c4 decodes + rows of every chunk tile")
+
+
+def one_shot_of_last_request(w, rng):
+    """The last request of a one-step workload as a one-shot prefill of its whole sequence: the
+    cached context's K/V read back through its table, the step's own tokens appended after it; the
+    query rows before the step's are fresh N(0,1) draws (their outputs are not compared)."""
+    st = w.steps[0]
+    b = st.num_seqs - 1
+    s, ql = int(st.seq_lens[b]), int(st.q_lens[b])
+    ctx, q0 = s - ql, int(st.query_start_loc[b])
+    slots = W.slots_for(st.block_tables, b, np.arange(s))
+    Hkv, d = w.num_kv_heads, w.head_dim
+    k_all = np.concatenate([w.k_cache0.reshape(-1, Hkv, d)[slots[:ctx]], st.k_new[q0:q0 + ql]])
+    v_all = np.concatenate([w.v_cache0.reshape(-1, Hkv, d)[slots[:ctx]], st.v_new[q0:q0 + ql]])
+    q_all = np.concatenate([W.normal_storage(rng, (ctx, w.num_q_heads, d), w.dtype), st.q[q0:q0 + ql]])
+    return W.Step(q=q_all, k_new=k_all, v_new=v_all, slot_mapping=slots.astype(np.int32),
+                  seq_lens=np.array([s], np.int32), query_start_loc=np.array([0, s], np.int32),
+                  block_tables=np.ascontiguousarray(st.block_tables[b:b + 1]))
+
+
+@pytest.mark.timeout(600)
+def test_c4_chunk_equals_one_shot_30720_prefill():
+    """P4 '把长输入切成块': chunk 15 of the 30720-token prompt (2048 rows over 28672 cached keys, in
+    the mixed step) gives the rows of a one-shot 30720-token prefill, both on the GPU.  The tiles of
+    the two calls cover the same absolute positions and keys in the same order, so the rows agree
+    bit for bit."""
     w = W.config4()
     st = w.steps[0]
-    rng = np.random.default_rng(1)
-    chunk_rows = 30 + np.unique(np.concatenate([[0, 1, 31, 32, 33, 1023, 2046, 2047], rng.integers(0, 2048, 16)]))
-    rows = np.concatenate([np.arange(30), chunk_rows])
-    out_g, _, _ = run_and_compare(w, rows=rows, what="c4 decodes + sampled chunk rows")
-
-
+    mixed = GpuState(w).step(st)
+    one = one_shot_of_last_request(w, np.random.default_rng(44))
+    full = GpuState(w).step(one)
+    say("c4 chunk vs one-shot 30720: last 2048 rows")
+    compare(mixed[30:], full[28672:], "bf16", what="c4 chunk vs one-shot")
+    assert np.array_equal(mixed[30:], full[28672:])
 @pytest.mark.timeout(600)
 def test_c5_skewed_long_decode():
     w = W.config5()
     run_and_compare(w, what="c5")
+
+
+# ------------------------------------------------------------------------------------------
+# padding slots and the last blocks of the pool (64-bit offsets)
+# ------------------------------------------------------------------------------------------
+def relabel_blocks(w, top):
+    """The same workload with physical blocks renamed so that its `top` highest-numbered used blocks
+    become the last blocks of the pool (NB-1, NB-2, ...): a permutation of block ids applied to the
+    caches, tables and slots alike (pure data movement)."""
+    st = w.steps[0]
+    NB = w.num_blocks
+    used = np.unique(st.block_tables[st.block_tables >= 0])
+    src = [int(x) for x in used[::-1][:top]]            # highest used ids
+    dst = list(range(NB - 1, NB - 1 - len(src), -1))    # last ids of the pool
+    perm = np.arange(NB, dtype=np.int64)                 # old id -> new id: disjoint swaps
+    for a, b in zip([x for x in src if x not in dst], [x for x in dst if x not in src]):
+        perm[a], perm[b] = b, a
+    kc = np.empty_like(w.k_cache0)
+    vc = np.empty_like(w.v_cache0)
+    kc[perm] = w.k_cache0
+    vc[perm] = w.v_cache0
+    bt = np.where(st.block_tables >= 0, perm[np.maximum(st.block_tables, 0)], -1).astype(np.int32)
+    sm = (perm[st.slot_mapping // 16] * 16 + st.slot_mapping % 16).astype(np.int32)
+    st2 = W.Step(q=st.q, k_new=st.k_new, v_new=st.v_new, slot_mapping=sm, seq_lens=st.seq_lens,
+                 query_start_loc=st.query_start_loc, block_tables=bt)
+    return W.Workload(name=w.name + "_relabelled", dtype=w.dtype, num_q_heads=w.num_q_heads,
+                      num_kv_heads=w.num_kv_heads, head_dim=w.head_dim, num_blocks=NB, scale=w.scale,
+                      k_cache0=kc, v_cache0=vc, steps=[st2], seed=w.seed, kv_dtype=w.kv_dtype,
+                      k_scale=w.k_scale, v_scale=w.v_scale)
+
+
+def with_padding_tokens(w, every, rng):
+    """The step's append gets a padding token (slot -1, random K/V) after every `every`-th token;
+    the attention call is unchanged (P1 §2.2: rows are written at their page index, padding has
+    none)."""
+    st = w.steps[0]
+    T = st.num_tokens
+    pos = np.arange(0, T, every)
+    n = len(pos)
+    kpad = W.normal_storage(rng, (n,) + st.k_new.shape[1:], w.dtype)
+    vpad = W.normal_storage(rng, (n,) + st.v_new.shape[1:], w.dtype)
+    k = np.insert(st.k_new, pos + 1, kpad, axis=0)
+    v = np.insert(st.v_new, pos + 1, vpad, axis=0)
+    sm = np.insert(st.slot_mapping, pos + 1, -1).astype(np.int32)
+    return k, v, sm
+
+
+@pytest.mark.parametrize("kind", ["bf16_c2_pool", "f32_over_2GiB", "i8_over_2GiB"])
+@pytest.mark.timeout(900)
+def test_append_padding_and_last_pool_blocks(kind):
+    """Padding tokens (slot < 0) are skipped and the pool's last blocks are written and read: caches
+    compared byte for byte over the whole pool, attention against the oracle on every row.  The c2
+    pool is exactly 2^31 bytes per cache; the other two pools exceed 2^31 bytes, so the last blocks'
+    byte offsets need 64 bits."""
+    rng = np.random.default_rng(71)
+    if kind == "bf16_c2_pool":
+        w = W.make_batch(71, [3000, 17, 1000, 256, 33], [1, 17, 1, 3, 1], 32, 32, 128, "bf16", num_blocks=16384,
+                         max_blocks=256)
+    elif kind == "f32_over_2GiB":
+        w = W.make_batch(72, [700, 40, 129], [1, 40, 2], 16, 8, 64, "f32", num_blocks=66000)
+    else:
+        w = W.make_batch(73, [2000, 70, 513], [1, 70, 1], 64, 32, 128, "bf16", num_blocks=33000, cache="i8")
+    cache_bytes = w.k_cache0.nbytes
+    say(f"{kind}: cache {cache_bytes / 2**30:.3f} GiB, pool {w.num_blocks} blocks")
+    w = relabel_blocks(w, top=4)
+    st = w.steps[0]
+    assert int(st.block_tables.max()) == w.num_blocks - 1
+    k, v, sm = with_padding_tokens(w, 3, rng)
+    g = GpuState(w)
+    dt = w.dtype
+    pa.append_kv(dev_tensor(k, dt), dev_tensor(v, dt), int_tensor(sm), g.kc, g.vc, g.ks, g.vs)
+    x = g.inputs(st)
+    out = torch.empty_like(x["q"])
+    pa.attention(x["q"], g.kc, g.vc, x["bt"], x["sl"], x["qsl"], w.scale, out, k_scale=g.ks, v_scale=g.vs)
+    torch.cuda.synchronize()
+    kc, vc = w.k_cache0.copy(), w.v_cache0.copy()
+    oracle.append(k, v, sm, kc, vc, w.k_scale, w.v_scale)
+    ref, _ = oracle.attention(st.q, kc, vc, st.block_tables, st.seq_lens, st.query_start_loc, w.scale,
+                              k_scale=w.k_scale, v_scale=w.v_scale)
+    assert np.array_equal(bits(host_array(g.kc, w.cache_dtype)), bits(kc)), f"{kind}: K cache differs"
+    assert np.array_equal(bits(host_array(g.vc, w.cache_dtype)), bits(vc)), f"{kind}: V cache differs"
+    compare(host_array(out, dt), ref, dt, what=kind)
 
 
 # ------------------------------------------------------------------------------------------

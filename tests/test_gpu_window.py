@@ -7,7 +7,7 @@ import pytest
 import attention_paged_kv_amd as pa
 from attention_paged_kv_amd import workloads as W
 import oracle
-from tests.gpu_helpers import GpuState, compare, host_array, say
+from tests.gpu_helpers import GpuState, compare, host_array, say, tile_rows
 
 pytestmark = pytest.mark.gpu
 
@@ -117,18 +117,16 @@ def test_window_c2_decode_batch():
 
 
 @pytest.mark.timeout(600)
-def test_window_c3_prefill_8k_sampled_rows():
-    rows = np.unique(np.concatenate([[0, 1, 15, 16, 4095, 4096, 4097, 8191],
-                                     np.random.default_rng(5).integers(0, 8192, 16)]))
-    run_window(W.config3(), 4096, rows=rows, what="c3 W=4096 sampled rows")
+def test_window_c3_prefill_8k_every_tile():
+    rows = tile_rows(0, 8192, 256, np.random.default_rng(5), n_random=24)
+    run_window(W.config3(), 4096, rows=rows, what="c3 W=4096 rows of every tile")
 
 
 @pytest.mark.timeout(600)
-def test_window_c4_mixed_chunk():
+def test_window_c4_mixed_chunk_every_tile():
     w = W.config4()
-    chunk_rows = 30 + np.unique(np.concatenate([[0, 1, 2047], np.random.default_rng(2).integers(0, 2048, 12)]))
-    rows = np.concatenate([np.arange(30), chunk_rows])
-    run_window(w, 4096, rows=rows, what="c4 W=4096")
+    rows = np.concatenate([np.arange(30), tile_rows(30, 2048, 64, np.random.default_rng(6))])
+    run_window(w, 4096, rows=rows, what="c4 W=4096 decodes + rows of every chunk tile")
 
 
 @pytest.mark.timeout(600)
