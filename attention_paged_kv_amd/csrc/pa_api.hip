@@ -152,7 +152,7 @@ struct Plan {
   bool stream = false;    // bf16 cache, rows of several positions: balanced runs instead of splits
   int span_blocks = 0;    // most 16-key blocks one row's decode pass covers
   int pos_per_tile = 0, num_slots = 0;
-  size_t off_o = 0, off_ml = 0, off_tiles = 0, off_ntiles = 0, total = 0;
+  size_t off_o = 0, off_ml = 0, total = 0;
 };
 
 // The kernels move data in 16-byte vectors.
@@ -241,12 +241,6 @@ int make_plan(int32_t B, int32_t T, int32_t MB, int32_t Hq, const pa_cache_desc*
     off = align256(off + units * p.head_dim * sizeof(float));
     p.off_ml = off;
     off = align256(off + units * 2 * sizeof(float));
-  }
-  if (p.run_tiles) {
-    p.off_tiles = off;
-    off = align256(off + (size_t)p.num_slots * sizeof(int4));
-    p.off_ntiles = off;
-    off = align256(off + sizeof(int));
   }
   p.total = off;
   const int64_t nzh = ((int64_t)p.qmax * p.group + p.heads_per_wg - 1) / p.heads_per_wg;
@@ -436,12 +430,6 @@ int launch_call(const Call& c, const Plan& p, char* ws, hipStream_t s, int* chec
     }
   }
   if (p.run_tiles) {
-    int4* tiles = reinterpret_cast<int4*>(ws + p.off_tiles);
-    int* ntiles = reinterpret_cast<int*>(ws + p.off_ntiles);
-    hipError_t e = timed("plan", s, [&] {
-      return pa::launch_plan_tiles(c.qsl, c.B, p.pos_per_tile, p.qmax + 1, tiles, ntiles, s);
-    });
-    if (e != hipSuccess) return device_fail(e, "plan launch");
     pa::TileArgs t{};
     t.q = c.q;
     t.k_cache = c.k_cache;
@@ -450,8 +438,8 @@ int launch_call(const Call& c, const Plan& p, char* ws, hipStream_t s, int* chec
     t.seq_lens = c.seq_lens;
     t.qsl = c.qsl;
     t.out = c.out;
-    t.tiles = tiles;
-    t.num_tiles = ntiles;
+    t.num_seqs = c.B;
+    t.min_q = p.qmax + 1;
     t.num_slots = p.num_slots;
     t.num_q_heads = c.Hq;
     t.num_kv_heads = cache->num_kv_heads;
@@ -462,7 +450,7 @@ int launch_call(const Call& c, const Plan& p, char* ws, hipStream_t s, int* chec
     t.scale_log2 = scale_log2;
     t.k_scale = cache->k_scale;
     t.v_scale = cache->v_scale;
-    e = timed("prefill_tile", s, [&] { return pa::launch_prefill_tile(t, p.head_dim, p.i8, s); });
+    const hipError_t e = timed("prefill_tile", s, [&] { return pa::launch_prefill_tile(t, p.head_dim, p.i8, s); });
     if (e != hipSuccess) return device_fail(e, "prefill tile launch");
   }
   return PA_OK;

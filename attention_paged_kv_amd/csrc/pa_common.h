@@ -65,6 +65,17 @@ __device__ __forceinline__ float xor16_sum(float v) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// Inclusive prefix sum across the wave.
+__device__ __forceinline__ int wave_incl_scan(int x) {
+  const int lane = threadIdx.x & (kWave - 1);
+#pragma unroll
+  for (int d = 1; d < kWave; d <<= 1) {
+    const int y = __shfl_up(x, d, kWave);
+    if (lane >= d) x += y;
+  }
+  return x;
+}
+
 // Block ids a wave will visit, 64 at a time: lane i holds the id of the wave's i-th block of the
 // current window, so the loop takes each id with one v_readlane instead of a memory round trip.
 struct BlockWindow {
@@ -106,6 +117,13 @@ __device__ __forceinline__ void dma16(const void* gbase, uint32_t voff, uint32_t
   uint32_t keep;
   asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %3\n\tglobal_load_lds_dwordx4 %1, %2\n\ts_mov_b32 m0, %0"
                : "=&s"(keep) : "v"(voff), "s"(gbase), "s"(lds) : "memory");
+}
+
+// As dma16, with a per-lane 64-bit global address.
+__device__ __forceinline__ void dma16_addr(const void* gaddr, uint32_t lds) {
+  uint32_t keep;
+  asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %1, off\n\ts_mov_b32 m0, %0"
+               : "=&s"(keep) : "v"(gaddr), "s"(lds) : "memory");
 }
 
 constexpr float kLog2e = 1.4426950408889634f;

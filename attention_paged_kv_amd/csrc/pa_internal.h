@@ -65,8 +65,8 @@ struct TileArgs {
   const int32_t* seq_lens;
   const int32_t* qsl;
   void* out;
-  const int4* tiles;      // (request, first local row, rows in tile, unused)
-  const int* num_tiles;
+  int num_seqs;
+  int min_q;              // requests with q_len >= min_q run here (shorter ones on the decode pass)
   int num_slots;          // upper bound on tiles launched per KV head
   int num_q_heads;
   int num_kv_heads;
@@ -99,8 +99,6 @@ hipError_t launch_append(const AppendArgs& a, hipStream_t s);
 hipError_t launch_decode_split(const DecodeArgs& a, int head_dim, bool bf16, hipStream_t s);
 hipError_t launch_decode_split_i8(const DecodeArgs& a, int head_dim, hipStream_t s);
 hipError_t launch_decode_merge(const DecodeArgs& a, int head_dim, bool bf16, hipStream_t s);
-hipError_t launch_plan_tiles(const int32_t* qsl, int num_seqs, int pos_per_tile, int min_q, int4* tiles,
-                             int* num_tiles, hipStream_t s);
 hipError_t launch_prefill_tile(const TileArgs& a, int head_dim, bool kv8, hipStream_t s);
 hipError_t launch_check(const CheckArgs& a, hipStream_t s);
 

@@ -1,5 +1,5 @@
 // pa_prefill.hip -- causal attention tiles for requests with q_len >= 2 (one-shot prefill and
-// chunked prefill), on bf16 MFMA, plus the device-side tile planner.
+// chunked prefill), on bf16 MFMA.  Each workgroup finds its own tile from its index.
 //
 // A prefill row block attends over every key up to its own position (P3 §2.1) and a chunk
 // additionally reads the keys of all earlier chunks from the cache (P4 "块大小怎样取舍": chunk 15
@@ -17,7 +17,9 @@
 //   O^T (d x 32 rows)     += V^T (d x 64) . P^T (64 x 32)   -- P^T stays in registers
 // K and V tiles are staged in LDS by direct global->LDS loads (no staging registers), double
 // buffered: the next tile's loads are in flight while the current one is consumed, with one
-// workgroup barrier per tile.  Each wave loads one 16-key cache block per tile, so its block-table
+// workgroup barrier per tile.  For bf16 caches the copies are issued as inline assembly and waited
+// for explicitly, so the compiler's own wait counting stays precise: K operands are then read two
+// k-steps ahead of their products instead of being waited for pair by pair.  Each wave loads one 16-key cache block per tile, so its block-table
 // lookup is a single uniform value.  LDS rows are unpadded and their 16-byte chunks XOR-swizzled by
 // row, which keeps the K operand reads and the V transpose reads free of bank conflicts.  V^T
 // operands come from the LDS transpose read: the S^T accumulator layout gives lane half a the keys
@@ -52,6 +54,31 @@ __device__ __forceinline__ int swz(int r) {
 }
 }  // namespace
 
+// One int32 per lane, loaded and waited for inside one asm block.  The key loop contains no load
+// the compiler can see: a visible load makes it place conservative vmcnt(0) waits in the loop, and
+// those would also wait for the next tile's copies (issued as inline assembly, which it does not
+// count), serialising the copies with the products.
+__device__ __forceinline__ int load_i32_sync(const int32_t* p) {
+  int v;
+  asm volatile("global_load_dword %0, %1, off\n\ts_waitcnt vmcnt(0)" : "=v"(v) : "v"(p) : "memory");
+  return v;
+}
+// Block ids of a wave's blocks, 64 at a time (lane i: the id of block first + stride * (base + i)),
+// taken with one v_readlane each; the ids are loaded with load_i32_sync (once per 64 tiles).
+// get() is only called for k < count, so count >= 1 and lanes past the end load the last entry.
+struct SyncWindow {
+  int ids = 0;
+  int base = -(1 << 30);
+  __device__ __forceinline__ int get(const int32_t* table, int first, int stride, int count, int k) {
+    if (k - base >= 64 || k < base) {
+      base = k;
+      const int i = k + (int)(threadIdx.x & 63);
+      ids = load_i32_sync(table + first + stride * min(i, count - 1));
+    }
+    return __builtin_amdgcn_readlane(ids, k - base);
+  }
+};
+
 template <int D, bool KV8>
 __global__ __launch_bounds__(512, 1) void prefill_tile_kernel(TileArgs a) {
   constexpr int ESZ = KV8 ? 1 : 2;          // bytes per cache element
@@ -85,9 +112,35 @@ __global__ __launch_bounds__(512, 1) void prefill_tile_kernel(TileArgs a) {
       slot = i / a.num_kv_heads;
     }
   }
-  if (slot >= *a.num_tiles) return;
-  const int4 tile = a.tiles[slot];
-  const int b = tile.x, q_off = tile.y, n_pos = tile.z;
+  // slot -> (request b, first local row q_off, rows n_pos): the tiles are the requests' row
+  // blocks of pos_per_tile positions, requests in order and each request's last (longest) row
+  // block first; requests with q_len < min_q have none.  Every wave finds its slot with a
+  // wave-wide prefix sum over the tile counts, 64 requests at a time.
+  int b = -1, q_off = 0, n_pos = 0;
+  {
+    int base = 0;
+    for (int c0 = 0; c0 < a.num_seqs; c0 += kWave) {
+      const int r = c0 + lane;
+      int qlr = 0, cnt = 0;
+      if (r < a.num_seqs) {
+        qlr = a.qsl[r + 1] - a.qsl[r];
+        cnt = qlr >= a.min_q ? (qlr + a.pos_per_tile - 1) / a.pos_per_tile : 0;
+      }
+      const int incl = wave_incl_scan(cnt);
+      const int total = __builtin_amdgcn_readlane(incl, kWave - 1);
+      if (slot < base + total) {
+        const int j = __popcll(__ballot(incl <= slot - base));   // requests wholly before the slot
+        b = c0 + j;
+        const int k = slot - base - __builtin_amdgcn_readlane(incl - cnt, j);   // its k-th tile
+        const int qi = __builtin_amdgcn_readlane(cnt, j) - 1 - k;                // last block first
+        q_off = qi * a.pos_per_tile;
+        n_pos = min(a.pos_per_tile, __builtin_amdgcn_readlane(qlr, j) - q_off);
+        break;
+      }
+      base += total;
+    }
+  }
+  if (b < 0) return;                             // past the last tile
   const int q0 = a.qsl[b];
   const int ql = a.qsl[b + 1] - q0;
   const int sl = a.seq_lens[b];
@@ -122,6 +175,10 @@ __global__ __launch_bounds__(512, 1) void prefill_tile_kernel(TileArgs a) {
     }
   }
 
+  // wait for Q here: left to itself the compiler puts this wait (vmcnt(0)) inside the key loop,
+  // where it would also wait for the next tile's copies
+  __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0) only
+
   const int kv_end = min(sl, ctx + q_off + n_pos);   // keys needed by the last row of the tile
   const int n_kt = (kv_end + kTileKeys - 1) / kTileKeys;
   const int first_pos = ctx + q_off;
@@ -141,7 +198,7 @@ __global__ __launch_bounds__(512, 1) void prefill_tile_kernel(TileArgs a) {
   const bool is_v = w >= 4;
   const char* tbase = is_v ? vbase : kbase;
   const int n_full = (sl / kBlock - bw + 3) / 4;  // count of kt with (4kt + bw + 1) * 16 <= sl
-  BlockWindow win;
+  SyncWindow win;
 
   float m_run = -INFINITY, l_run = 0.f;
   floatx16 O[NDT];
@@ -177,19 +234,25 @@ __global__ __launch_bounds__(512, 1) void prefill_tile_kernel(TileArgs a) {
     floatx16 S0, S1;
 #pragma unroll
     for (int v = 0; v < 16; ++v) { S0[v] = 0.f; S1[v] = 0.f; }
-    bf16x8 a0 = *reinterpret_cast<const bf16x8*>(kl + k_off[0]);
-    bf16x8 a1 = *reinterpret_cast<const bf16x8*>(kl + k_off[0] + 32 * ROWB);
+    // K operands are read PD k-steps ahead of their products; the scheduling barriers keep the
+    // compiler from sinking the reads next to their use (it otherwise waits on every pair)
+    constexpr int PD = 2;
+    bf16x8 ka[NKK], kb[NKK];
+#pragma unroll
+    for (int kk = 0; kk < PD; ++kk) {
+      ka[kk] = *reinterpret_cast<const bf16x8*>(kl + k_off[kk]);
+      kb[kk] = *reinterpret_cast<const bf16x8*>(kl + k_off[kk] + 32 * ROWB);
+    }
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk) {
-      bf16x8 n0 = a0, n1 = a1;
-      if (kk + 1 < NKK) {
-        n0 = *reinterpret_cast<const bf16x8*>(kl + k_off[kk + 1]);
-        n1 = *reinterpret_cast<const bf16x8*>(kl + k_off[kk + 1] + 32 * ROWB);
+      if (kk + PD < NKK) {
+        ka[kk + PD] = *reinterpret_cast<const bf16x8*>(kl + k_off[kk + PD]);
+        kb[kk + PD] = *reinterpret_cast<const bf16x8*>(kl + k_off[kk + PD] + 32 * ROWB);
       }
-      S0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qreg[kk], S0, 0, 0, 0);
-      S1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qreg[kk], S1, 0, 0, 0);
-      a0 = n0;
-      a1 = n1;
+      __builtin_amdgcn_sched_barrier(0);
+      S0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[kk], qreg[kk], S0, 0, 0, 0);
+      S1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kb[kk], qreg[kk], S1, 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
     }
 
     // ---- causal mask (only on tiles that cross the diagonal of the first row) and window mask
@@ -277,19 +340,18 @@ __global__ __launch_bounds__(512, 1) void prefill_tile_kernel(TileArgs a) {
       const int blk = 4 * kt + bw;
       if ((blk + 1) * kBlock <= sl && blk * kBlock >= lo_req) {   // whole block valid: one table entry
         const char* tb = tbase + (int64_t)win.get(table, bw, 4, n_full, kt) * (kBlock * rs * 2);
+        const uint32_t l = __builtin_amdgcn_readfirstlane(lds_u32(dl));
 #pragma unroll
-        for (int i = 0; i < IPB; ++i)
-          __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(tb + lane_off[i]),
-                                           (__attribute__((address_space(3))) void*)(dl + 1024 * i), 16, 0, 0);
+        for (int i = 0; i < IPB; ++i) dma16(tb, lane_off[i], l + 1024 * i);
       } else {                                      // edge block: clamp rows into [lo_req, sl)
+        const uint32_t l = __builtin_amdgcn_readfirstlane(lds_u32(dl));
 #pragma unroll
         for (int i = 0; i < IPB; ++i) {
           const int rr = RPI * i + lane / CPR;
           const int j = min(max(blk * kBlock + rr, lo_req), sl - 1);
           const int q = (lane % CPR) ^ swz<D>(16 * bw + rr);
-          const int64_t off = (((int64_t)table[j >> 4] * kBlock + (j & 15)) * rs) * 2 + q * 16;
-          __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(tbase + off),
-                                           (__attribute__((address_space(3))) void*)(dl + 1024 * i), 16, 0, 0);
+          const int64_t off = (((int64_t)load_i32_sync(table + (j >> 4)) * kBlock + (j & 15)) * rs) * 2 + q * 16;
+          dma16_addr(tbase + off, l + 1024 * i);
         }
       }
     };
@@ -429,49 +491,6 @@ __global__ __launch_bounds__(512, 1) void prefill_tile_kernel(TileArgs a) {
         *reinterpret_cast<uint2*>(op + dd * 2) = pk;
       }
   }
-}
-
-// One workgroup: per request, ceil(q_len / pos_per_tile) tiles for every request with
-// q_len >= min_q (shorter ones are rows of the split-KV decode pass), written with the last
-// (longest) row block of each request first.
-__global__ __launch_bounds__(256) void plan_tiles_kernel(const int32_t* qsl, int num_seqs, int pos_per_tile,
-                                                         int min_q, int4* tiles, int* num_tiles) {
-  __shared__ int scan[256];
-  __shared__ int base;
-  const int tid = threadIdx.x;
-  if (tid == 0) base = 0;
-  __syncthreads();
-  for (int c0 = 0; c0 < num_seqs; c0 += 256) {
-    const int b = c0 + tid;
-    int ql = 0, cnt = 0;
-    if (b < num_seqs) {
-      ql = qsl[b + 1] - qsl[b];
-      cnt = ql >= min_q ? (ql + pos_per_tile - 1) / pos_per_tile : 0;
-    }
-    scan[tid] = cnt;
-    __syncthreads();
-    for (int off = 1; off < 256; off <<= 1) {
-      const int v = tid >= off ? scan[tid - off] : 0;
-      __syncthreads();
-      scan[tid] += v;
-      __syncthreads();
-    }
-    const int excl = base + scan[tid] - cnt;
-    for (int i = 0; i < cnt; ++i) {
-      const int qi = cnt - 1 - i;
-      tiles[excl + i] = make_int4(b, qi * pos_per_tile, min(pos_per_tile, ql - qi * pos_per_tile), 0);
-    }
-    __syncthreads();
-    if (tid == 255) base += scan[255];
-    __syncthreads();
-  }
-  if (tid == 0) *num_tiles = base;
-}
-
-hipError_t launch_plan_tiles(const int32_t* qsl, int num_seqs, int pos_per_tile, int min_q, int4* tiles,
-                             int* num_tiles, hipStream_t s) {
-  plan_tiles_kernel<<<dim3(1), dim3(256), 0, s>>>(qsl, num_seqs, pos_per_tile, min_q, tiles, num_tiles);
-  return hipGetLastError();
 }
 
 hipError_t launch_prefill_tile(const TileArgs& a, int head_dim, bool kv8, hipStream_t s) {

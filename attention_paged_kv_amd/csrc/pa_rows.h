@@ -46,17 +46,6 @@ __device__ __forceinline__ int split_origin(const DecodeArgs& a, int n_keys, int
 // are merged as splits are.  Every workgroup reads the same number of blocks, so the launch has
 // no tail of workgroups still running while the rest of the chip idles.
 
-// Inclusive prefix sum across the wave.
-__device__ __forceinline__ int wave_incl_scan(int x) {
-  const int lane = threadIdx.x & (kWave - 1);
-#pragma unroll
-  for (int d = 1; d < kWave; d <<= 1) {
-    const int y = __shfl_up(x, d, kWave);
-    if (lane >= d) x += y;
-  }
-  return x;
-}
-
 // Blocks a row's pass covers: from the block holding the oldest key its first position sees to
 // the block holding its last key; 0 for rows that are not on this pass.
 __device__ __forceinline__ int row_blocks(const DecodeArgs& a, int row) {

@@ -6,10 +6,14 @@ then causal attention of every query row (decode splits + merge, and prefill/chu
 the batch has them).  Inputs are seeded synthetic tensors already resident in HBM.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--config c2|c3|c4|c5|c1] [--window N]
-                    [--kv bf16|i8] [--verify K] [--no-cpu-baseline]
+                    [--kv bf16|i8] [--verify K] [--no-cpu-baseline] [--only]
 
 Prints one JSON line.  The default workload is the 32-request bf16 decode batch (32/32 heads,
-d=128, contexts U[512, 4096], 16384-block pool); its metric is KV-read GB/s.  --window N runs the
+d=128, contexts U[512, 4096], 16384-block pool); its metric is KV-read GB/s.  The default run also
+times, in the same process, the 8k causal prefill (c3), the mixed chunked step (c4) and the
+length-skewed long decode (c5), each under "workloads" with its own roofline object; prefill
+workloads warm up for at least 60 steps (compute-bound launches speed up over a run's first few
+dozen).  --only times the named workload alone.  --window N runs the
 same workload with a sliding window of N keys per query row; work counts then cover only the keys
 and pairs inside the windows.  --kv i8 keeps the workload's shapes and lengths over an 8-bit cache
 (int8 codes, fp32 scale per KV head and channel; c2 .. c5): KV bytes count 1 byte per
@@ -115,68 +119,31 @@ def cpu_baseline(w, steps, is_decode, kv_bytes, window=0):
     return {"value": round(val, 6), "unit": unit, "cores": threads, "kind": "oracle", "sample": sample}
 
 
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=100)
-    ap.add_argument("--warmup", type=int, default=50)
-    ap.add_argument("--config", default="c2", choices=["c1", "c2", "c3", "c4", "c5"])
-    ap.add_argument("--window", type=int, default=0, help="sliding window in keys (0: none)")
-    ap.add_argument("--kv", default="bf16", choices=["bf16", "i8"], help="cache element type")
-    ap.add_argument("--verify", type=int, default=0, help="tokens per request to verify (decode workloads)")
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--copy-ref-mib", type=int, default=0,
-                    help="instead of the hot path, time a plain device copy of this many MiB "
-                         "(reference kernel for scaling the HBM byte counters)")
-    args = ap.parse_args()
+def host_cpu():
+    """(logical CPUs of the host, CPU model) for the baseline's context."""
+    model = ""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return os.cpu_count() or 0, model
 
-    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py runs on exactly one GPU: the hot path here is single-GPU (no collectives); "
-              "use --gpus 1.", file=sys.stderr)
-        sys.exit(2)
 
+def measure(cfg, kv, win, verify, steps_n, warmup, dev, want_cpu=False):
+    """Times one workload (append + attention per step) and returns its JSON record."""
     import torch
 
     import attention_paged_kv_amd as pa
     from attention_paged_kv_amd import accounting as A
     from attention_paged_kv_amd import workloads as W
 
-    if not torch.cuda.is_available():
-        print("bench.py needs a GPU", file=sys.stderr)
-        sys.exit(1)
-    pa.load_library()
-    dev = torch.device("cuda:0")
-
-    if args.copy_ref_mib:
-        n = args.copy_ref_mib << 20
-        src = torch.ones(n // 4, dtype=torch.float32, device=dev)
-        dst = torch.empty_like(src)
-        for _ in range(args.warmup):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        for _ in range(args.steps):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        dt = (time.perf_counter() - t0) / args.steps
-        print(json.dumps({"copy_ref_bytes_read": n, "copy_ref_bytes_written": n, "ms_per_copy": dt * 1e3,
-                          "GBps_read_plus_write": 2 * n / dt / 1e9}), flush=True)
-        return
-
-    if args.window < 0:
-        print("--window must be >= 0", file=sys.stderr)
-        sys.exit(2)
-    win = args.window
-    if args.kv == "i8" and args.config == "c1":
-        print("--kv i8 serves the bf16-activation workloads (c2 .. c5)", file=sys.stderr)
-        sys.exit(2)
     t0 = time.time()
-    w = W.CONFIGS[args.config](cache="i8") if args.kv == "i8" else W.CONFIGS[args.config]()
-    if args.verify > 1:
-        if args.config not in ("c2", "c5"):
-            print("--verify serves the decode workloads (c2, c5)", file=sys.stderr)
-            sys.exit(2)
-        w = W.verify_variant(w, args.verify)
+    w = W.CONFIGS[cfg](cache="i8") if kv == "i8" else W.CONFIGS[cfg]()
+    if verify > 1:
+        w = W.verify_variant(w, verify)
     log(f"generated {w.name} in {time.time() - t0:.1f}s")
     tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
 
@@ -184,8 +151,6 @@ def main():
         a = np.ascontiguousarray(a)
         if w.dtype == "bf16" and a.dtype == np.uint16:
             return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
-        if a.dtype == np.int32:
-            return torch.from_numpy(a).to(dev)
         return torch.from_numpy(a).to(dev)
 
     # c1 is a 17-step sequence; its "step" is the whole sequence.  Others are one step.
@@ -221,9 +186,11 @@ def main():
     flops = sum(A.attention_flops(st.q_lens, st.seq_lens, w.num_q_heads, w.head_dim, win) for st in steps)
     tile_flops = sum(A.attention_flops(st.q_lens[st.q_lens > 1], st.seq_lens[st.q_lens > 1], w.num_q_heads,
                                        w.head_dim, win) for st in steps)
+    dec_bytes = sum(A.kv_read_bytes(st.seq_lens[st.q_lens == 1], w.num_kv_heads, w.head_dim, w.esz,
+                                    st.q_lens[st.q_lens == 1], win) for st in steps)
     wname = w.name if win == 0 else f"{w.name}-w{win}"     # names the workload in the counter summary
 
-    for _ in range(args.warmup):
+    for _ in range(warmup):
         run_step()
     torch.cuda.synchronize()
 
@@ -232,29 +199,30 @@ def main():
     torch.cuda.synchronize()
     t_start = time.perf_counter()
     ev0.record(stream)
-    for _ in range(args.steps):
+    for _ in range(steps_n):
         run_step()
     ev1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_start
     gpu_ms = ev0.elapsed_time(ev1)
-    ms_per_step = 1e3 * wall / args.steps
+    ms_per_step = 1e3 * wall / steps_n
 
     # per-kernel durations from hipEvents the library records around its own launches (same stream)
     pa.timing_reset()
     pa.timing_enable(True)
-    for _ in range(args.steps):
+    for _ in range(steps_n):
         run_step()
     torch.cuda.synchronize()
     kern = {}
-    for name in ("append", "decode_split", "decode_merge", "plan", "prefill_tile"):
+    for name in ("append", "decode_split", "decode_merge", "prefill_tile"):
         ms, n = pa.timing_read(name)
         if n:
-            kern[name] = {"avg_us": 1e3 * ms / n, "launches_per_step": n / args.steps}
+            kern[name] = {"avg_us": 1e3 * ms / n, "launches_per_step": n / steps_n}
     pa.timing_enable(False)
     pa.timing_reset()
 
-    is_decode = args.config in ("c2", "c5")
+    is_decode = cfg in ("c2", "c5")
+    extra = {}
     if is_decode:
         unit = "GB/s"
         value = kv_bytes / (ms_per_step * 1e-3) / 1e9
@@ -284,27 +252,26 @@ def main():
                 "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / BF16_PEAK_TFLOPS, 4),
                 "traffic": measured_traffic("prefill_tile", wname),
                 "algorithmic_flops_per_launch": int(per_launch)}
+        if "decode_split" in kern and dec_bytes:
+            dk = kern["decode_split"]
+            ach = dec_bytes / dk["launches_per_step"] / (dk["avg_us"] * 1e-6) / 1e9
+            extra["decode_part"] = {"bound": "hbm", "kernel": "decode_split", "achieved": round(ach, 1),
+                                    "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4),
+                                    "traffic": measured_traffic("decode_split", wname),
+                                    "algorithmic_bytes_per_launch": int(dec_bytes / dk["launches_per_step"])}
+            # the whole step against its own roofline: the longer of its compute and memory times
+            t_roof = max(flops / (BF16_PEAK_TFLOPS * 1e12), kv_bytes / (HBM_PEAK_GBS * 1e9))
+            extra["step_roofline_frac"] = round(t_roof / (gpu_ms / steps_n * 1e-3), 4)
 
-    cpu = None
-    if not args.no_cpu_baseline:
-        cpu = cpu_baseline(w, steps, is_decode, kv_bytes, win)
-    from attention_paged_kv_amd.sched import bench_planner
-    planner = {k: (round(v, 2) if isinstance(v, float) else v) for k, v in bench_planner().items()}
-
-    res = {
-        "metric": METRIC,
+    cpu = cpu_baseline(w, steps, is_decode, kv_bytes, win) if want_cpu else None
+    rec = {
         "value": round(value, 2 if unit == "GB/s" else 3),
         "unit": unit,
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 5),
-        "gpu_ms_per_step": round(gpu_ms / args.steps, 5),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
+        "gpu_ms_per_step": round(gpu_ms / steps_n, 5),
+        "steps": steps_n,
+        "warmup": warmup,
         "dtype": w.dtype,
-        "data": "synthetic",
         "config": {"workload": wname, "description": w.description + (f", sliding window {win}" if win else ""),
                    "sliding_window": win, "kv_cache": w.cache_dtype, "num_seqs": int(steps[0].num_seqs),
                    "q_tokens": int(sum(st.num_tokens for st in steps)),
@@ -312,8 +279,122 @@ def main():
         "kernels": {k: {kk: round(vv, 3) for kk, vv in v.items()} for k, v in kern.items()},
         "roofline": roof,
         "cpu_baseline": cpu,
+    }
+    rec.update(extra)
+    del dsteps, kc, vc, ws
+    torch.cuda.empty_cache()
+    return rec
+
+
+# Compute-bound launches get faster over a run's first few dozen launches (the clock settles), so
+# prefill workloads warm up for at least this many steps whatever --warmup says.
+PREFILL_MIN_WARMUP = 60
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--config", default="c2", choices=["c1", "c2", "c3", "c4", "c5"])
+    ap.add_argument("--window", type=int, default=0, help="sliding window in keys (0: none)")
+    ap.add_argument("--kv", default="bf16", choices=["bf16", "i8"], help="cache element type")
+    ap.add_argument("--verify", type=int, default=0, help="tokens per request to verify (decode workloads)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--only", action="store_true",
+                    help="time the named workload only (the default run adds c3, c4 and c5 entries)")
+    ap.add_argument("--copy-ref-mib", type=int, default=0,
+                    help="instead of the hot path, time a plain device copy of this many MiB "
+                         "(reference kernel for scaling the HBM byte counters)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on exactly one GPU: the hot path here is single-GPU (no collectives); "
+              "use --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import attention_paged_kv_amd as pa
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    pa.load_library()
+    dev = torch.device("cuda:0")
+
+    if args.copy_ref_mib:
+        n = args.copy_ref_mib << 20
+        src = torch.ones(n // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(args.warmup):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        dt = (time.perf_counter() - t0) / args.steps
+        print(json.dumps({"copy_ref_bytes_read": n, "copy_ref_bytes_written": n, "ms_per_copy": dt * 1e3,
+                          "GBps_read_plus_write": 2 * n / dt / 1e9}), flush=True)
+        return
+
+    if args.window < 0:
+        print("--window must be >= 0", file=sys.stderr)
+        sys.exit(2)
+    if args.kv == "i8" and args.config == "c1":
+        print("--kv i8 serves the bf16-activation workloads (c2 .. c5)", file=sys.stderr)
+        sys.exit(2)
+    if args.verify > 1 and args.config not in ("c2", "c5"):
+        print("--verify serves the decode workloads (c2, c5)", file=sys.stderr)
+        sys.exit(2)
+
+    def warm(cfg):
+        return max(args.warmup, PREFILL_MIN_WARMUP) if cfg in ("c3", "c4") else args.warmup
+
+    head = measure(args.config, args.kv, args.window, args.verify, args.steps, warm(args.config), dev,
+                   want_cpu=not args.no_cpu_baseline)
+    if head["cpu_baseline"] is not None:
+        ncpu, model = host_cpu()
+        head["cpu_baseline"].update({"host_cpus": ncpu, "cpu_model": model})
+    others = {}
+    default_run = (args.config == "c2" and args.kv == "bf16" and args.window == 0 and args.verify <= 1
+                   and not args.only)
+    if default_run:
+        for cfg in ("c3", "c4", "c5"):
+            rec = measure(cfg, "bf16", 0, 0, args.steps, warm(cfg), dev)
+            rec.pop("cpu_baseline")
+            others[cfg] = rec
+    from attention_paged_kv_amd.sched import bench_planner
+    planner = {k: (round(v, 2) if isinstance(v, float) else v) for k, v in bench_planner().items()}
+
+    res = {
+        "metric": METRIC,
+        "value": head["value"],
+        "unit": head["unit"],
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": head["ms_per_step"],
+        "gpu_ms_per_step": head["gpu_ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": head["dtype"],
+        "data": "synthetic",
+        "config": head["config"],
+        "kernels": head["kernels"],
+        "roofline": head["roofline"],
+        "cpu_baseline": head["cpu_baseline"],
         "host_planner": planner,
     }
+    for k in ("decode_part", "step_roofline_frac"):
+        if k in head:
+            res[k] = head[k]
+    if head["warmup"] != args.warmup:
+        res["warmup_run"] = head["warmup"]
+    if others:
+        res["workloads"] = others
     print(json.dumps(res), flush=True)
 
 

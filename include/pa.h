@@ -185,7 +185,7 @@ int pa_attention_ex(const void* q, int32_t num_q_tokens, int32_t num_q_heads,
  * Measurement support (not part of the computation).  When timing is on, every kernel the
  * library launches is bracketed by a pair of hipEvents recorded on the same stream.
  * pa_timing_read() waits for the recorded events and returns, for the kernel family `name`
- * ("append", "decode_split", "decode_merge", "plan", "prefill_tile", "check"), the summed
+ * ("append", "decode_split", "decode_merge", "prefill_tile", "check"), the summed
  * duration in milliseconds and the number of launches since the last reset.
  */
 int pa_timing_enable(int on);

@@ -148,9 +148,9 @@ def test_int8_descriptor_rules_checked_before_launch(lib):
     assert lib.pa_attention(p, 4, 8, p, p, ctypes.byref(stray), p, 4, 16, p, p, ctypes.c_float(1), o, None, 0,
                             None) == 1
     i8 = pa._CacheDesc(8, 16, 2, 128, 2, sc, sc)
-    # a q_len above 8 is possible (13 tokens over 4 requests): the tile pass runs, which needs a tile
-    # list in the workspace, so an 8-byte one is refused before launch
-    assert lib.pa_attention(p, 13, 8, p, p, ctypes.byref(i8), p, 4, 16, p, p, ctypes.c_float(1), o,
+    # rows of up to 64 blocks take several decode splits, whose partials need workspace: an 8-byte
+    # one is refused before launch
+    assert lib.pa_attention(p, 13, 8, p, p, ctypes.byref(i8), p, 4, 64, p, p, ctypes.c_float(1), o,
                             ctypes.c_void_p(256), 8, None) == 4
     assert lib.pa_attention_workspace_size(4, 4, 64, 8, ctypes.byref(i8)) > 0
 
