@@ -16,7 +16,7 @@ from __future__ import annotations
 import ctypes
 import os
 
-ABI_VERSION = 4
+ABI_VERSION = 5
 BLOCK_SIZE = 16
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libpa.so")
@@ -65,6 +65,9 @@ def load_library(path: str = LIB_PATH):
     lib.pa_attention_ex.argtypes = [P, I, I, P, P, D, P, I, I, P, P, ctypes.c_float, P, P, Z,
                                     ctypes.POINTER(_AttnOpts), P]
     lib.pa_attention_ex.restype = ctypes.c_int
+    lib.pa_attention_noalloc.argtypes = [P, I, I, P, P, D, P, I, I, P, P, ctypes.c_float, P,
+                                         ctypes.POINTER(_AttnOpts), P]
+    lib.pa_attention_noalloc.restype = ctypes.c_int
     lib.pa_timing_enable.argtypes = [ctypes.c_int]
     lib.pa_timing_enable.restype = ctypes.c_int
     lib.pa_timing_read.argtypes = [ctypes.c_char_p, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64)]
@@ -221,6 +224,41 @@ def attention(q, k_cache, v_cache, block_tables, seq_lens, query_start_loc, scal
                              block_tables.data_ptr(), B, MB, seq_lens.data_ptr(), query_start_loc.data_ptr(),
                              ctypes.c_float(scale), out.data_ptr(), workspace.data_ptr(),
                              workspace.numel() * workspace.element_size(), ctypes.byref(opts), _stream(dev))
+    _err(lib, rc)
+    return out
+
+
+def attention_noalloc(q, k_cache, v_cache, block_tables, seq_lens, query_start_loc, scale, out, window=0,
+                      k_scale=None, v_scale=None, max_q_len=0):
+    """``attention`` through pa_attention_noalloc: the library's fixed per-device scratch array
+    instead of a workspace, so the call allocates no device memory.  Calls that may overlap on
+    one device race on that array (serialise them).  Raises PAError (code 4) for a batch whose
+    workspace would not fit the array."""
+    import torch
+    lib = load_library()
+    dev = q.device
+    _check_tensor("q", q, dev, ndim=3)
+    _check_tensor("k_cache", k_cache, dev, ndim=4)
+    _check_tensor("v_cache", v_cache, dev, dtype=k_cache.dtype, ndim=4)
+    if q.dtype != _act_dtype(k_cache):
+        raise TypeError(f"q must be {_act_dtype(k_cache)} for a {k_cache.dtype} cache, got {q.dtype}")
+    _check_tensor("out", out, dev, dtype=q.dtype, ndim=3)
+    _check_tensor("block_tables", block_tables, dev, dtype=torch.int32, ndim=2)
+    _check_tensor("seq_lens", seq_lens, dev, dtype=torch.int32, ndim=1)
+    _check_tensor("query_start_loc", query_start_loc, dev, dtype=torch.int32, ndim=1)
+    if v_cache.shape != k_cache.shape:
+        raise ValueError("k_cache and v_cache shapes differ")
+    T, Hq, d = q.shape
+    B, MB = block_tables.shape
+    if out.shape != q.shape or d != k_cache.shape[3]:
+        raise ValueError("out must match q, head_dim must match the cache")
+    if seq_lens.shape[0] != B or query_start_loc.shape[0] != B + 1:
+        raise ValueError("seq_lens must be [B], query_start_loc [B+1]")
+    desc = _desc(k_cache, k_scale, v_scale)
+    opts = _AttnOpts(int(window), int(max_q_len))
+    rc = lib.pa_attention_noalloc(q.data_ptr(), T, Hq, k_cache.data_ptr(), v_cache.data_ptr(), ctypes.byref(desc),
+                                  block_tables.data_ptr(), B, MB, seq_lens.data_ptr(), query_start_loc.data_ptr(),
+                                  ctypes.c_float(scale), out.data_ptr(), ctypes.byref(opts), _stream(dev))
     _err(lib, rc)
     return out
 

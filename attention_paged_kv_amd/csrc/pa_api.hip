@@ -458,6 +458,37 @@ int launch_call(const Call& c, const Plan& p, char* ws, hipStream_t s, int* chec
 
 }  // namespace
 
+// ---- the no-allocation entry point's scratch: a fixed array in each device's memory ----
+// In host code `scratch` is only a stand-in for the symbol: kernels and copies get the address
+// that hipGetSymbolAddress returns for the current device (each device holds its own copy).
+static __device__ __align__(256) char scratch[PA_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr size_t kScratchBytes = (size_t)PA_NOALLOC_SCRATCH_BYTES;
+constexpr size_t kScratchCheck = 256;              // first bytes: the check-mode result slot
+static_assert(kScratchBytes > kScratchCheck, "scratch holds the check slot and a workspace");
+
+std::mutex g_scratch_mu;
+std::unordered_map<int, char*> g_scratch;          // device -> address of its scratch array
+
+int scratch_address(char*& ptr) {
+  int dev = 0;
+  int rc = get_device(dev);
+  if (rc) return rc;
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  auto it = g_scratch.find(dev);
+  if (it == g_scratch.end()) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p) return device_fail(e != hipSuccess ? e : hipErrorInvalidSymbol, "hipGetSymbolAddress(scratch)");
+    it = g_scratch.emplace(dev, static_cast<char*>(p)).first;
+  }
+  ptr = it->second;
+  return PA_OK;
+}
+
+}  // namespace
+
 extern "C" {
 
 int pa_abi_version(void) { return PA_ABI_VERSION; }
@@ -580,6 +611,27 @@ int pa_attention(const void* q, int32_t num_q_tokens, int32_t num_q_heads, const
   return pa_attention_ex(q, num_q_tokens, num_q_heads, k_cache, v_cache, cache, block_tables, num_seqs,
                          max_blocks_per_seq, seq_lens, query_start_loc, scale, out, workspace, workspace_bytes,
                          nullptr, stream);
+}
+
+int pa_attention_noalloc(const void* q, int32_t num_q_tokens, int32_t num_q_heads, const void* k_cache,
+                         const void* v_cache, const pa_cache_desc* cache, const int32_t* block_tables,
+                         int32_t num_seqs, int32_t max_blocks_per_seq, const int32_t* seq_lens,
+                         const int32_t* query_start_loc, float scale, void* out, const pa_attention_opts* opts,
+                         void* stream) {
+  g_err.clear();
+  const Call given{q, num_q_tokens, num_q_heads, k_cache, v_cache, cache, block_tables, num_seqs,
+                   max_blocks_per_seq, seq_lens, query_start_loc, scale, out, 0, 0};
+  Call c;
+  Plan p;
+  int rc = prepare(given, opts, c, p);
+  if (rc) return rc;
+  if (p.total > kScratchBytes - kScratchCheck)
+    return fail(PA_ERR_WORKSPACE, "this batch needs %zu bytes of scratch; the no-allocation entry point holds %zu",
+                p.total, kScratchBytes - kScratchCheck);
+  char* base = nullptr;
+  rc = scratch_address(base);
+  if (rc) return rc;
+  return launch_call(c, p, base + kScratchCheck, reinterpret_cast<hipStream_t>(stream), reinterpret_cast<int*>(base));
 }
 
 int pa_timing_enable(int on) {

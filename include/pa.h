@@ -35,7 +35,7 @@
 extern "C" {
 #endif
 
-#define PA_ABI_VERSION 4
+#define PA_ABI_VERSION 5
 #define PA_BLOCK_SIZE 16
 
 typedef enum {
@@ -180,6 +180,28 @@ int pa_attention_ex(const void* q, int32_t num_q_tokens, int32_t num_q_heads,
                     const int32_t* block_tables, int32_t num_seqs, int32_t max_blocks_per_seq,
                     const int32_t* seq_lens, const int32_t* query_start_loc, float scale, void* out,
                     void* workspace, size_t workspace_bytes, const pa_attention_opts* opts, void* stream);
+
+/* Bytes of the per-device scratch array behind pa_attention_noalloc (64 MiB). */
+#define PA_NOALLOC_SCRATCH_BYTES (64u << 20)
+
+/*
+ * pa_attention_ex without a workspace, for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc).  Same arguments,
+ * layouts, ownership, results and errors as pa_attention_ex; the split partials and the tile list
+ * live in a fixed array of PA_NOALLOC_SCRATCH_BYTES in each device's memory, held by the library
+ * until the process ends.  The call allocates nothing (no hipMalloc, hipFree or allocating library
+ * routine; check mode also reports through that array).
+ *   - A batch whose workspace would exceed PA_NOALLOC_SCRATCH_BYTES - 256 bytes is refused with
+ *     PA_ERR_WORKSPACE before anything is launched (pa_attention_workspace_size() bounds the need).
+ *   - Every call on a device shares that device's array, and each call overwrites what it uses
+ *     (nothing in it needs to start at zero): calls that may overlap on one device -- on two
+ *     streams, or from two threads -- race and must be serialised by the caller.
+ */
+int pa_attention_noalloc(const void* q, int32_t num_q_tokens, int32_t num_q_heads,
+                         const void* k_cache, const void* v_cache, const pa_cache_desc* cache,
+                         const int32_t* block_tables, int32_t num_seqs, int32_t max_blocks_per_seq,
+                         const int32_t* seq_lens, const int32_t* query_start_loc, float scale, void* out,
+                         const pa_attention_opts* opts, void* stream);
 
 /*
  * Measurement support (not part of the computation).  When timing is on, every kernel the

@@ -180,3 +180,18 @@ def test_workspace_size_serves_every_option(lib, window, max_q):
         rc = lib.pa_attention_ex(p, T, 8, p, p, ctypes.byref(d), p, B, 513, p, p, ctypes.c_float(1), o,
                                  ctypes.c_void_p(256), need, ctypes.byref(opts), None)
         assert rc != 4, (B, T, window, max_q, lib.pa_last_error())
+
+
+def test_noalloc_refuses_batches_beyond_its_scratch_on_the_host(lib):
+    """pa_attention_noalloc sizes the call from the arguments alone and refuses a batch whose
+    workspace exceeds its fixed scratch before touching any device (the pointers are never read)."""
+    p = ctypes.c_void_p(16)
+    o = ctypes.c_void_p(48)
+    d = _desc(nb=4096, hkv=8, dtype=1)
+    # 31 requests over 2078 query tokens and 1920-block rows: split partials for up to 8 positions
+    # per row over 30720 keys, far more than 64 MiB
+    need = lib.pa_attention_workspace_size(31, 2078, 1920, 32, ctypes.byref(d))
+    assert need > (64 << 20)
+    rc = lib.pa_attention_noalloc(p, 2078, 32, p, p, ctypes.byref(d), p, 31, 1920, p, p, ctypes.c_float(0.1), o,
+                                  None, None)
+    assert rc == 4 and b"scratch" in lib.pa_last_error()
