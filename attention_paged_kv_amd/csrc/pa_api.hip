@@ -368,8 +368,34 @@ int prepare(const Call& c, const pa_attention_opts* opts, Call& full, Plan& p) {
   return PA_OK;
 }
 
-// Queues the call's kernels on `s`, with `ws` holding at least p.total bytes (null when p.total
-// is 0).  Allocates nothing when `check_slot` is given (check mode then reports through it).
+// ---- the side stream of a mixed step (decode rows beside prefill tiles), one per device ----
+// A batch with both decode rows and prefill tiles queues its tile pass on the caller's stream and
+// its decode pass (splits and merge) on this stream, forked from and joined back to the caller's
+// stream by events, so that decode workgroups take compute units as soon as tile workgroups leave
+// them instead of waiting for the whole tile pass (or holding it back).  The stream has the default
+// priority.  g_side_mu serialises the fork-join sequences of concurrent calls (the events are reused).
+std::mutex g_side_mu;
+struct Side { hipStream_t s = nullptr; hipEvent_t fork = nullptr, join = nullptr; };
+std::unordered_map<int, Side> g_side;
+int side_stream(hipStream_t& s, hipEvent_t& fork, hipEvent_t& join) {
+  int dev = 0;
+  int rc = get_device(dev);
+  if (rc) return rc;
+  std::lock_guard<std::mutex> lk(g_side_mu);
+  Side& sd = g_side[dev];
+  if (!sd.s) {
+    hipError_t e = hipStreamCreateWithFlags(&sd.s, hipStreamNonBlocking);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&sd.fork, hipEventDisableTiming);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&sd.join, hipEventDisableTiming);
+    if (e != hipSuccess) return device_fail(e, "side stream");
+  }
+  s = sd.s; fork = sd.fork; join = sd.join;
+  return PA_OK;
+}
+
+// Queues the call's kernels on `s` (a mixed batch forks its decode pass to the side stream), with
+// `ws` holding at least p.total bytes (null when p.total is 0).  Allocates nothing when
+// `check_slot` is given (check mode then reports through it, and nothing is forked).
 int launch_call(const Call& c, const Plan& p, char* ws, hipStream_t s, int* check_slot) {
   int rc;
   const pa_cache_desc* cache = c.cache;
@@ -389,70 +415,103 @@ int launch_call(const Call& c, const Plan& p, char* ws, hipStream_t s, int* chec
   }
 
   const float scale_log2 = c.scale * 1.4426950408889634f;
+  auto run_decode = [&](hipStream_t s) -> int {
+    int rc;
   if (p.run_decode) {
-    pa::DecodeArgs d{};
-    d.q = c.q;
-    d.k_cache = c.k_cache;
-    d.v_cache = c.v_cache;
-    d.block_tables = c.block_tables;
-    d.seq_lens = c.seq_lens;
-    d.qsl = c.qsl;
-    d.out = c.out;
-    d.part_o = p.max_splits > 1 ? reinterpret_cast<float*>(ws + p.off_o) : nullptr;
-    d.part_ml = p.max_splits > 1 ? reinterpret_cast<float*>(ws + p.off_ml) : nullptr;
-    d.num_seqs = c.B;
-    d.num_rows = p.rows;
-    d.per_token = p.per_token;
-    d.qmax = p.qmax;
-    d.num_q_heads = c.Hq;
-    d.num_kv_heads = cache->num_kv_heads;
-    d.group = p.group;
-    d.heads_per_wg = p.heads_per_wg;
-    d.max_blocks = c.MB;
-    d.split = p.split;
-    d.max_splits = p.max_splits;
-    d.stream_wgs = 0;
-    if (p.stream) {
-      rc = stream_wgs(p, cache->num_kv_heads, d.stream_wgs);
-      if (rc) return rc;
+      pa::DecodeArgs d{};
+      d.q = c.q;
+      d.k_cache = c.k_cache;
+      d.v_cache = c.v_cache;
+      d.block_tables = c.block_tables;
+      d.seq_lens = c.seq_lens;
+      d.qsl = c.qsl;
+      d.out = c.out;
+      d.part_o = p.max_splits > 1 ? reinterpret_cast<float*>(ws + p.off_o) : nullptr;
+      d.part_ml = p.max_splits > 1 ? reinterpret_cast<float*>(ws + p.off_ml) : nullptr;
+      d.num_seqs = c.B;
+      d.num_rows = p.rows;
+      d.per_token = p.per_token;
+      d.qmax = p.qmax;
+      d.num_q_heads = c.Hq;
+      d.num_kv_heads = cache->num_kv_heads;
+      d.group = p.group;
+      d.heads_per_wg = p.heads_per_wg;
+      d.max_blocks = c.MB;
+      d.split = p.split;
+      d.max_splits = p.max_splits;
+      d.stream_wgs = 0;
+      if (p.stream) {
+        rc = stream_wgs(p, cache->num_kv_heads, d.stream_wgs);
+        if (rc) return rc;
+      }
+      d.window = c.window;
+      d.scale_log2 = scale_log2;
+      d.k_scale = cache->k_scale;
+      d.v_scale = cache->v_scale;
+      hipError_t e = timed("decode_split", s, [&] {
+        return p.i8 ? pa::launch_decode_split_i8(d, p.head_dim, s) : pa::launch_decode_split(d, p.head_dim, p.bf16, s);
+      });
+      if (e != hipSuccess) return device_fail(e, "decode split launch");
+      if (p.max_splits > 1) {
+        e = timed("decode_merge", s, [&] { return pa::launch_decode_merge(d, p.head_dim, p.bf16, s); });
+        if (e != hipSuccess) return device_fail(e, "decode merge launch");
+      }
     }
-    d.window = c.window;
-    d.scale_log2 = scale_log2;
-    d.k_scale = cache->k_scale;
-    d.v_scale = cache->v_scale;
-    hipError_t e = timed("decode_split", s, [&] {
-      return p.i8 ? pa::launch_decode_split_i8(d, p.head_dim, s) : pa::launch_decode_split(d, p.head_dim, p.bf16, s);
-    });
-    if (e != hipSuccess) return device_fail(e, "decode split launch");
-    if (p.max_splits > 1) {
-      e = timed("decode_merge", s, [&] { return pa::launch_decode_merge(d, p.head_dim, p.bf16, s); });
-      if (e != hipSuccess) return device_fail(e, "decode merge launch");
-    }
-  }
+    return PA_OK;
+  };
+  auto run_tiles = [&](hipStream_t s) -> int {
   if (p.run_tiles) {
-    pa::TileArgs t{};
-    t.q = c.q;
-    t.k_cache = c.k_cache;
-    t.v_cache = c.v_cache;
-    t.block_tables = c.block_tables;
-    t.seq_lens = c.seq_lens;
-    t.qsl = c.qsl;
-    t.out = c.out;
-    t.num_seqs = c.B;
-    t.min_q = p.qmax + 1;
-    t.num_slots = p.num_slots;
-    t.num_q_heads = c.Hq;
-    t.num_kv_heads = cache->num_kv_heads;
-    t.group = p.group;
-    t.pos_per_tile = p.pos_per_tile;
-    t.max_blocks = c.MB;
-    t.window = c.window;
-    t.scale_log2 = scale_log2;
-    t.k_scale = cache->k_scale;
-    t.v_scale = cache->v_scale;
-    const hipError_t e = timed("prefill_tile", s, [&] { return pa::launch_prefill_tile(t, p.head_dim, p.i8, s); });
-    if (e != hipSuccess) return device_fail(e, "prefill tile launch");
+      pa::TileArgs t{};
+      t.q = c.q;
+      t.k_cache = c.k_cache;
+      t.v_cache = c.v_cache;
+      t.block_tables = c.block_tables;
+      t.seq_lens = c.seq_lens;
+      t.qsl = c.qsl;
+      t.out = c.out;
+      t.num_seqs = c.B;
+      t.min_q = p.qmax + 1;
+      t.num_slots = p.num_slots;
+      t.num_q_heads = c.Hq;
+      t.num_kv_heads = cache->num_kv_heads;
+      t.group = p.group;
+      t.pos_per_tile = p.pos_per_tile;
+      t.max_blocks = c.MB;
+      t.window = c.window;
+      t.scale_log2 = scale_log2;
+      t.k_scale = cache->k_scale;
+      t.v_scale = cache->v_scale;
+      const hipError_t e = timed("prefill_tile", s, [&] { return pa::launch_prefill_tile(t, p.head_dim, p.i8, s); });
+      if (e != hipSuccess) return device_fail(e, "prefill tile launch");
+    }
+    return PA_OK;
+  };
+  if (p.run_decode && p.run_tiles && !check_slot) {
+    // decode rows on the device's side stream, concurrently with the tiles on the caller's stream
+    // (the no-allocation entry point, which passes check_slot, creates no stream and runs both
+    // passes on the caller's stream)
+    hipStream_t side = nullptr;
+    hipEvent_t fork = nullptr, join = nullptr;
+    rc = side_stream(side, fork, join);
+    if (rc) return rc;
+    std::lock_guard<std::mutex> lk(g_side_mu);
+    hipError_t e = hipEventRecord(fork, s);
+    if (e == hipSuccess) e = hipStreamWaitEvent(side, fork, 0);
+    if (e != hipSuccess) return device_fail(e, "fork to the side stream");
+    rc = run_tiles(s);
+    if (rc) return rc;
+    rc = run_decode(side);
+    if (rc) return rc;
+    e = hipEventRecord(join, side);
+    if (e == hipSuccess) e = hipStreamWaitEvent(s, join, 0);
+    if (e != hipSuccess) return device_fail(e, "join from the side stream");
+    return PA_OK;
   }
+  if (p.run_decode) {
+    rc = run_decode(s);
+    if (rc) return rc;
+  }
+  if (p.run_tiles) return run_tiles(s);
   return PA_OK;
 }
 
@@ -518,6 +577,17 @@ void pa_release(void) {   // best effort: errors here have nowhere to go
       kv.second = DevState{};
     }
     g_dev.clear();
+  }
+  {
+    std::lock_guard<std::mutex> lk(g_side_mu);
+    for (auto& kv : g_side) {
+      (void)hipSetDevice(kv.first);
+      if (kv.second.s) (void)hipStreamSynchronize(kv.second.s);
+      if (kv.second.fork) (void)hipEventDestroy(kv.second.fork);
+      if (kv.second.join) (void)hipEventDestroy(kv.second.join);
+      if (kv.second.s) (void)hipStreamDestroy(kv.second.s);
+    }
+    g_side.clear();
   }
   (void)hipSetDevice(cur);
 }

@@ -29,9 +29,13 @@
 // instead (finite data under a zero probability).  With a sliding window (P2 §5.2, P3 §6.3: only
 // the most recent W keys count) the key loop starts at the tile holding the first row's oldest
 // visible key, and tiles crossing the window's lower edge are masked as well; keys older than the
-// request's first window are never read (their blocks may be gone), a valid row stands in.  The
-// running max is only moved (and O rescaled) when some row's max grows by more than 2^8; between
-// moves, probabilities may exceed 1 by at most 2^8.
+// request's first window are never read (their blocks may be gone), a valid row stands in.
+// Scores are in log2 units: Q is multiplied by scale * log2(e) once and rounded to bf16.  Each row
+// keeps a reference max m_ref, a bf16 value, and one more 16-wide k-step of the QK^T products (a
+// ones column of K against -m_ref in Q) makes the products s - m_ref directly, so the
+// probabilities are exp2 of the accumulators with no vector arithmetic before the exponential.
+// The reference is only moved (and O rescaled) when a row with none sees its first key or some
+// row's max exceeds it by more than 2^8; between moves, probabilities are at most about 2^8.
 //
 // 8-bit caches (P2 §4.3, §5.4: int8 codes with a scale per KV head and channel): the cache blocks
 // are copied to int8 staging buffers the same way, then the workgroup converts each tile once into
@@ -161,6 +165,9 @@ __global__ __launch_bounds__(512, 1) void prefill_tile_kernel(TileArgs a) {
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk) {
       const uint4 v = row_ok ? *reinterpret_cast<const uint4*>(qp + kk * 32) : make_uint4(0, 0, 0, 0);
+      // q * scale * log2(e) (and * k_scale for int8 caches), rounded once to bf16: the products are
+      // then scores in log2 units
+      const float cs = a.scale_log2;
       if constexpr (KV8) {                       // q * k_scale of channels 16kk + 8half .. +7
         const float* ks = a.k_scale + (int64_t)g * D + 16 * kk + 8 * half;
         const float4 s0 = *reinterpret_cast<const float4*>(ks);
@@ -168,9 +175,12 @@ __global__ __launch_bounds__(512, 1) void prefill_tile_kernel(TileArgs a) {
         const float f[8] = {bf16_lo(v.x) * s0.x, bf16_hi(v.x) * s0.y, bf16_lo(v.y) * s0.z, bf16_hi(v.y) * s0.w,
                             bf16_lo(v.z) * s1.x, bf16_hi(v.z) * s1.y, bf16_lo(v.w) * s1.z, bf16_hi(v.w) * s1.w};
 #pragma unroll
-        for (int e = 0; e < 8; ++e) qreg[kk][e] = (__bf16)f[e];
+        for (int e = 0; e < 8; ++e) qreg[kk][e] = (__bf16)(f[e] * cs);
       } else {
-        qreg[kk] = __builtin_bit_cast(bf16x8, v);
+        const float f[8] = {bf16_lo(v.x), bf16_hi(v.x), bf16_lo(v.y), bf16_hi(v.y),
+                            bf16_lo(v.z), bf16_hi(v.z), bf16_lo(v.w), bf16_hi(v.w)};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) qreg[kk][e] = (__bf16)(f[e] * cs);
       }
     }
   }
@@ -186,7 +196,6 @@ __global__ __launch_bounds__(512, 1) void prefill_tile_kernel(TileArgs a) {
   const int lo_req = max(0, ctx - a.window + 1);     // oldest key any row of the request sees
   const int kt_lo = max(0, first_pos - a.window + 1) / kTileKeys;   // first key tile of this tile
   const int low_edge = last_pos - a.window + 1;      // tiles starting below this need the window mask
-  const float c = a.scale_log2;
   const int64_t rs = (int64_t)a.num_kv_heads * D;    // elements per cache token row
   const char* kbase = reinterpret_cast<const char*>(a.k_cache) + (int64_t)g * D * ESZ;
   const char* vbase = reinterpret_cast<const char*>(a.v_cache) + (int64_t)g * D * ESZ;
@@ -200,7 +209,16 @@ __global__ __launch_bounds__(512, 1) void prefill_tile_kernel(TileArgs a) {
   const int n_full = (sl / kBlock - bw + 3) / 4;  // count of kt with (4kt + bw + 1) * 16 <= sl
   SyncWindow win;
 
-  float m_run = -INFINITY, l_run = 0.f;
+  // m_ref: the row's reference max (log2 units, a bf16 value so that -m_ref is exact in an MFMA
+  // operand); has_ref: whether the row has one yet (before its first visible key it does not, and
+  // m_ref is 0).  The products give s - m_ref directly: one more k-step multiplies the ones column
+  // (A, lane half 0, element 0) with -m_ref (B, lane half 0, element 0).
+  float m_ref = 0.f, l_run = 0.f;
+  bool has_ref = false;
+  bf16x8 ones_a, mref_b;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) { ones_a[e] = (__bf16)0.f; mref_b[e] = (__bf16)0.f; }
+  if (half == 0) ones_a[0] = (__bf16)1.f;
   floatx16 O[NDT];
 #pragma unroll
   for (int dt = 0; dt < NDT; ++dt)
@@ -234,6 +252,8 @@ __global__ __launch_bounds__(512, 1) void prefill_tile_kernel(TileArgs a) {
     floatx16 S0, S1;
 #pragma unroll
     for (int v = 0; v < 16; ++v) { S0[v] = 0.f; S1[v] = 0.f; }
+    S0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ones_a, mref_b, S0, 0, 0, 0);   // -m_ref
+    S1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ones_a, mref_b, S1, 0, 0, 0);
     // K operands are read PD k-steps ahead of their products; the scheduling barriers keep the
     // compiler from sinking the reads next to their use (it otherwise waits on every pair)
     constexpr int PD = 2;
@@ -267,27 +287,36 @@ __global__ __launch_bounds__(512, 1) void prefill_tile_kernel(TileArgs a) {
       }
     }
 
-    // ---- online softmax (scores in log2 units via c = scale * log2 e), lazy rescale ----
+    // ---- online softmax on s - m_ref; the reference moves (O and l rescaled) only when a row has
+    //      none yet and sees a key, or its max exceeds the reference by more than 2^8 ----
     float tm = fmaxf(S0[0], S1[0]);
 #pragma unroll
     for (int v = 1; v < 16; ++v) tm = fmaxf(fmaxf(tm, S0[v]), S1[v]);   // one v_max3 per v
     tm = xor32_max(tm);
-    const float mn = fmaxf(m_run, tm);
-    if (__any((mn - m_run) * c > 8.f)) {
-      const float alpha = (m_run == -INFINITY) ? 0.f : fast_exp2((m_run - mn) * c);
-      m_run = mn;
-      l_run *= alpha;
+    const bool need = has_ref ? (tm > 8.f) : (tm > -INFINITY);
+    if (__any(need)) {
+      float shift = 0.f;                               // new reference - old, this row
+      if (need) {
+        const float m_new = (float)(__bf16)(m_ref + tm);
+        shift = m_new - m_ref;
+        const float alpha = has_ref ? fast_exp2(-shift) : 0.f;
+        l_run *= alpha;
 #pragma unroll
-      for (int dt = 0; dt < NDT; ++dt)
+        for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
-        for (int v = 0; v < 16; ++v) O[dt][v] *= alpha;
+          for (int v = 0; v < 16; ++v) O[dt][v] *= alpha;
+        m_ref = m_new;
+        has_ref = true;
+        if (half == 0) mref_b[0] = (__bf16)(-m_new);
+      }
+#pragma unroll
+      for (int v = 0; v < 16; ++v) { S0[v] -= shift; S1[v] -= shift; }
     }
-    const float mc = (m_run == -INFINITY) ? 0.f : m_run * c;   // a row that has seen no key yet
     bf16x8 P[4];
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
-      P[v >> 3][v & 7] = (__bf16)fast_exp2(fmaf(S0[v], c, -mc));
-      P[2 + (v >> 3)][v & 7] = (__bf16)fast_exp2(fmaf(S1[v], c, -mc));
+      P[v >> 3][v & 7] = (__bf16)fast_exp2(S0[v]);
+      P[2 + (v >> 3)][v & 7] = (__bf16)fast_exp2(S1[v]);
     }
     // row sum of the bf16 probabilities the products use, two per v_dot2c_f32_bf16 against (1, 1)
     const bf16x2 one2 = {(__bf16)1.f, (__bf16)1.f};

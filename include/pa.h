@@ -76,7 +76,7 @@ int pa_abi_version(void);
 const char* pa_last_error(void);
 
 /* Frees the library-owned workspaces of every device (those used when pa_attention gets a
- * NULL workspace).  Synchronises the devices that own them. */
+ * NULL workspace) and the side streams of mixed batches.  Synchronises the devices that own them. */
 void pa_release(void);
 
 /* Check mode: when on (or when the environment variable PA_CHECK=1 is set at the first call),
@@ -146,6 +146,10 @@ size_t pa_attention_workspace_size(int32_t num_seqs, int32_t num_q_tokens, int32
  *                    frees and reallocates it (hipMalloc).  Such buffers live until pa_release().
  * Device-side index errors (bad q_len/seq_len, block id outside [0, NB)) are undefined unless
  * check mode is on.  num_q_heads must be a multiple of Hkv; for bf16, Hq/Hkv <= 128.
+ * A batch with both decode rows (q_len <= 8 for bf16 activations, q_len 1 for fp32) and longer
+ * rows (P4 "一步的 token 预算": all decodes plus a prefill chunk in one step) runs its decode pass on
+ * a library-owned side stream of the device, forked from `stream` and joined back to it with
+ * events: every kernel of the call still completes before later work on `stream` starts.
  */
 int pa_attention(const void* q, int32_t num_q_tokens, int32_t num_q_heads,
                  const void* k_cache, const void* v_cache, const pa_cache_desc* cache,
