@@ -301,7 +301,7 @@ __global__ __launch_bounds__(64 * NW, 2) void decode_i8_kernel(DecodeArgs a) {
 #pragma unroll
       for (int tt = 0; tt < NT; ++tt) O[tt] *= alpha;
     }
-    const float mc = m * c;
+    const float mc = (m == -INFINITY) ? 0.f : m * c;       // a column that has seen no key yet: p = 0
     f16x8 pb;
     float ps = 0.f;
 #pragma unroll

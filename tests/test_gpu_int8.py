@@ -176,6 +176,9 @@ I8_VERIFY_CASES = [
     ([3000, 777, 64], [4, 8, 2], 32, 8, 128, 100),              # windows start mid-block per column
     ([3000, 1243, 250, 5000], [8, 8, 7, 8], 32, 8, 128, 238),   # first position reaches past a split
     ([500, 500], [8, 8], 8, 2, 128, 1),
+    # rows whose last split holds only keys past the first positions (129 = 128 + 1, 257 = 256 + 1):
+    # those columns see no key of that split, whose partial must then carry no weight
+    ([129, 257, 513, 40], [2, 4, 8, 3], 32, 8, 128, 0),
     ([1030, 260, 90], [1, 3, 90], 24, 3, 128, 0),              # verify rows beside a prefill
 ]
 
