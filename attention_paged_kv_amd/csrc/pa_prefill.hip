@@ -246,8 +246,17 @@ __global__ __launch_bounds__(512, 1) void prefill_tile_kernel(TileArgs a) {
     v_off[1][dt] = r_hi * ROWB + ((lq ^ swz<D>(r_hi)) * 16) + sub;
   }
 
+  // The wave's rows are positions wp0 .. wp1 of the tile (none when wp1 < wp0).  A key tile wholly
+  // after the newest key they see, or (sliding window) wholly before the oldest, changes none of
+  // them: on tiles crossing the diagonal the waves whose rows all come before the tile skip it.
+  const int wp0 = (32 * w) / G;
+  const int wp1 = min((32 * w + 31) / G, n_pos - 1);
+  const int wave_newest = ctx + q_off + wp1;
+  const int wave_oldest = ctx + q_off + wp0 - a.window + 1;
+
   // one key tile: S^T, mask, online softmax, O^T += V^T P^T, reading (kl, vl)
   auto tile_math = [&](int kt, const char* kl, const char* vl) {
+    if (wp1 < wp0 || kt * kTileKeys > wave_newest || kt * kTileKeys + kTileKeys - 1 < wave_oldest) return;
     // ---- S^T = K Q^T : two 32-key sub-tiles, chains interleaved, operands read one step ahead ----
     floatx16 S0, S1;
 #pragma unroll
