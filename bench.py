@@ -6,7 +6,7 @@ then causal attention of every query row (decode splits + merge, and prefill/chu
 the batch has them).  Inputs are seeded synthetic tensors already resident in HBM.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--config c2|c3|c4|c5|c1] [--window N]
-                    [--kv bf16|i8] [--verify K] [--no-cpu-baseline] [--only]
+                    [--kv bf16|i8] [--verify K] [--chunks N] [--no-cpu-baseline] [--only]
 
 Prints one JSON line.  The default workload is the 32-request bf16 decode batch (32/32 heads,
 d=128, contexts U[512, 4096], 16384-block pool); its metric is KV-read GB/s.  The default run also
@@ -19,6 +19,9 @@ and pairs inside the windows.  --kv i8 keeps the workload's shapes and lengths o
 (int8 codes, fp32 scale per KV head and channel; c2 .. c5): KV bytes count 1 byte per
 element.  --verify K turns a decode workload into a verification step: each request appends and
 attends its last K tokens (same lengths and tables), still one read of every visible key.
+--chunks N (c3) appends and attends the prompt as N equal chunks, each over the keys cached before
+it; a step is then the whole prompt, and the default run reports four 2048-token chunks next to
+the one-shot prefill ("c3_chunks4", with chunked_over_one_shot = the ratio of their GPU times).
 """
 import argparse
 import json
@@ -132,8 +135,10 @@ def host_cpu():
     return os.cpu_count() or 0, model
 
 
-def measure(cfg, kv, win, verify, steps_n, warmup, dev, want_cpu=False):
-    """Times one workload (append + attention per step) and returns its JSON record."""
+def measure(cfg, kv, win, verify, steps_n, warmup, dev, want_cpu=False, chunks=1):
+    """Times one workload (append + attention per step) and returns its JSON record.  chunks > 1
+    (one-request prefill workloads): the prompt is appended and attended as that many equal chunks,
+    each over the keys cached before it, and a "step" is the whole sequence of chunks."""
     import torch
 
     import attention_paged_kv_amd as pa
@@ -144,6 +149,9 @@ def measure(cfg, kv, win, verify, steps_n, warmup, dev, want_cpu=False):
     w = W.CONFIGS[cfg](cache="i8") if kv == "i8" else W.CONFIGS[cfg]()
     if verify > 1:
         w = W.verify_variant(w, verify)
+    if chunks > 1:
+        S = int(w.steps[0].seq_lens[0])
+        w = W.chunked_steps(w, [S // chunks] * (chunks - 1) + [S - (S // chunks) * (chunks - 1)])
     log(f"generated {w.name} in {time.time() - t0:.1f}s")
     tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
 
@@ -277,6 +285,7 @@ def measure(cfg, kv, win, verify, steps_n, warmup, dev, want_cpu=False):
         "dtype": w.dtype,
         "config": {"workload": wname, "description": w.description + (f", sliding window {win}" if win else ""),
                    "sliding_window": win, "kv_cache": w.cache_dtype, "num_seqs": int(steps[0].num_seqs),
+                   "attention_calls_per_step": len(steps),
                    "q_tokens": int(sum(st.num_tokens for st in steps)),
                    "kv_read_bytes": int(kv_bytes), "flops": int(flops), "parallelism": "single-gpu"},
         "kernels": {k: {kk: round(vv, 3) for kk, vv in v.items()} for k, v in kern.items()},
@@ -336,6 +345,8 @@ def main():
     ap.add_argument("--window", type=int, default=0, help="sliding window in keys (0: none)")
     ap.add_argument("--kv", default="bf16", choices=["bf16", "i8"], help="cache element type")
     ap.add_argument("--verify", type=int, default=0, help="tokens per request to verify (decode workloads)")
+    ap.add_argument("--chunks", type=int, default=1,
+                    help="c3: append and attend the prompt as this many equal chunks (a step = all of them)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only", action="store_true",
                     help="time the named workload only (the default run adds c3, c4 and c5 entries)")
@@ -384,23 +395,32 @@ def main():
     if args.verify > 1 and args.config not in ("c2", "c5"):
         print("--verify serves the decode workloads (c2, c5)", file=sys.stderr)
         sys.exit(2)
+    if args.chunks < 1 or (args.chunks > 1 and args.config != "c3"):
+        print("--chunks serves the one-shot prefill workload (c3)", file=sys.stderr)
+        sys.exit(2)
 
     def warm(cfg):
         return max(args.warmup, PREFILL_MIN_WARMUP) if cfg in ("c3", "c4") else args.warmup
 
     head = measure(args.config, args.kv, args.window, args.verify, args.steps, warm(args.config), dev,
-                   want_cpu=not args.no_cpu_baseline)
+                   want_cpu=not args.no_cpu_baseline, chunks=args.chunks)
     if head["cpu_baseline"] is not None:
         ncpu, model = host_cpu()
         head["cpu_baseline"].update({"host_cpus": ncpu, "cpu_model": model})
     others = {}
     default_run = (args.config == "c2" and args.kv == "bf16" and args.window == 0 and args.verify <= 1
-                   and not args.only)
+                   and args.chunks == 1 and not args.only)
     if default_run:
         for cfg in ("c3", "c4", "c5"):
             rec = measure(cfg, "bf16", 0, 0, args.steps, warm(cfg), dev)
             rec.pop("cpu_baseline")
             others[cfg] = rec
+        # the same 8192-token prompt in four 2048-token chunks (each re-reading the cached keys of the
+        # ones before it), against the one-shot prefill: total GPU time per prompt
+        rec = measure("c3", "bf16", 0, 0, max(1, args.steps // 4), warm("c3") // 4 + 1, dev, chunks=4)
+        rec.pop("cpu_baseline")
+        rec["chunked_over_one_shot"] = round(rec["gpu_ms_per_step"] / others["c3"]["gpu_ms_per_step"], 4)
+        others["c3_chunks4"] = rec
     from attention_paged_kv_amd.sched import bench_planner
     planner = {k: (round(v, 2) if isinstance(v, float) else v) for k, v in bench_planner().items()}
 
