@@ -306,7 +306,10 @@ def decode_rows_alone(pa, w, steps, dsteps, kc, vc, ks, vs, win, steps_n, dev):
     rows = np.nonzero(st.q_lens == 1)[0]
     tok = st.query_start_loc[rows]
     q = d["q"][torch.from_numpy(tok.astype(np.int64)).to(dev)].contiguous()
-    bt = d["bt"][torch.from_numpy(rows.astype(np.int64)).to(dev)].contiguous()
+    # a batch of its own carries a table as wide as its longest row (the mixed step's table is as wide
+    # as its long prompt, which would size the decode splits for that prompt)
+    width = int((st.seq_lens[rows].max() + 15) // 16)
+    bt = d["bt"][torch.from_numpy(rows.astype(np.int64)).to(dev)][:, :width].contiguous()
     sl = d["sl"][torch.from_numpy(rows.astype(np.int64)).to(dev)].contiguous()
     qsl = torch.arange(len(rows) + 1, dtype=torch.int32, device=dev)
     out = torch.empty_like(q)
@@ -359,6 +362,18 @@ def main():
         print("bench.py runs on exactly one GPU: the hot path here is single-GPU (no collectives); "
               "use --gpus 1.", file=sys.stderr)
         sys.exit(2)
+    if args.window < 0:
+        print("--window must be >= 0", file=sys.stderr)
+        sys.exit(2)
+    if args.kv == "i8" and args.config == "c1":
+        print("--kv i8 serves the bf16-activation workloads (c2 .. c5)", file=sys.stderr)
+        sys.exit(2)
+    if args.verify > 1 and args.config not in ("c2", "c5"):
+        print("--verify serves the decode workloads (c2, c5)", file=sys.stderr)
+        sys.exit(2)
+    if args.chunks < 1 or (args.chunks > 1 and args.config != "c3"):
+        print("--chunks serves the one-shot prefill workload (c3)", file=sys.stderr)
+        sys.exit(2)
 
     import torch
 
@@ -386,18 +401,6 @@ def main():
                           "GBps_read_plus_write": 2 * n / dt / 1e9}), flush=True)
         return
 
-    if args.window < 0:
-        print("--window must be >= 0", file=sys.stderr)
-        sys.exit(2)
-    if args.kv == "i8" and args.config == "c1":
-        print("--kv i8 serves the bf16-activation workloads (c2 .. c5)", file=sys.stderr)
-        sys.exit(2)
-    if args.verify > 1 and args.config not in ("c2", "c5"):
-        print("--verify serves the decode workloads (c2, c5)", file=sys.stderr)
-        sys.exit(2)
-    if args.chunks < 1 or (args.chunks > 1 and args.config != "c3"):
-        print("--chunks serves the one-shot prefill workload (c3)", file=sys.stderr)
-        sys.exit(2)
 
     def warm(cfg):
         return max(args.warmup, PREFILL_MIN_WARMUP) if cfg in ("c3", "c4") else args.warmup

@@ -18,6 +18,19 @@ def test_more_than_one_gpu_is_refused_with_a_message():
     assert "one GPU" in r.stderr
 
 
+@pytest.mark.parametrize("args, words", [
+    (["--chunks", "4"], "--chunks"),                    # chunks serve the one-shot prefill (c3) only
+    (["--config", "c3", "--chunks", "0"], "--chunks"),
+    (["--config", "c3", "--verify", "4"], "--verify"),  # verification serves the decode workloads
+    (["--window", "-1"], "--window"),
+])
+def test_workload_options_are_checked_before_any_gpu_work(args, words):
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py")] + args,
+                       capture_output=True, text=True, timeout=300)
+    assert r.returncode == 2
+    assert words in r.stderr
+
+
 def _summary_lines():
     for line in open(os.path.join(ROOT, "profiles", "hbm_traffic.txt")):
         if not line.startswith("#") and line.strip():
