@@ -61,18 +61,21 @@ bool check_on() {
   return v == 1;
 }
 
-// Keys per decode split: PA_SPLIT_TOKENS if set (a multiple of 16 up to 1024), else 256, or 384
-// when a row may span more than 8192 keys (measured: c5's rows of up to 32768 keys 175 against
-// 179 us; c2's rows of up to 4096 keys 207 against 211).  `bound`: sizing a workspace that must
-// serve every window, so the smaller split (more partials) is assumed.
-int split_tokens(int64_t span, bool bound) {
+// Keys per decode split: PA_SPLIT_TOKENS if set (a multiple of 16 up to 1024), else 256 (320 over
+// an 8-bit cache, ten of its 32-key units), or 384 when a row may span more than 8192 keys
+// (measured: c5's rows of up to 32768 keys 175 against 179 us; c2's rows of up to 4096 keys 207
+// against 211, and over an 8-bit cache 111 against 114 at 256).  `bound`: sizing a workspace that
+// must serve every window and cache, so the smallest split (the most partials) is assumed.
+int split_tokens(int64_t span, bool bound, bool i8) {
   static const int over = [] {
     const char* e = std::getenv("PA_SPLIT_TOKENS");
     const int s = e ? std::atoi(e) : 0;
     return (s >= 16 && s <= 1024 && s % 16 == 0) ? s : 0;   // <= 64 blocks per split
   }();
   if (over) return over;
-  return (span > 8192 && !bound) ? pa::kLongSplitTokens : pa::kDefaultSplitTokens;
+  if (bound) return pa::kDefaultSplitTokens;
+  if (span > 8192) return pa::kLongSplitTokens;
+  return i8 ? pa::kI8SplitTokens : pa::kDefaultSplitTokens;
 }
 
 // ---- per-device state: the check-mode result slot and the compute-unit count ----
@@ -212,7 +215,7 @@ int make_plan(int32_t B, int32_t T, int32_t MB, int32_t Hq, const pa_cache_desc*
   // Rows of several positions (verification) make uneven work per split (more columns on some
   // rows, longer merges); they are dealt out in balanced runs.  Plain decode rows measure best on
   // fixed splits, which the hardware schedules dynamically.
-  p.split = split_tokens(span, bound);
+  p.split = split_tokens(span, bound, c->dtype == PA_DTYPE_I8);
   p.stream = c->dtype == PA_DTYPE_BF16 && p.qmax > 1;
   if (p.stream) {
     // a row meets at most ceil(blocks / run) + 1 runs, and runs hold at least `split` keys

@@ -6,11 +6,12 @@
 
 namespace pa {
 
-// bf16 requests with q_len <= kVerifyMax (decode, and a few tokens to verify), int8 requests with
-// q_len == 1, and every query row of an fp32 batch run on the split-KV decode kernels; longer bf16
-// requests run on the MFMA tile kernel.
+// Requests with q_len <= kVerifyMax over a bf16 or int8 cache (decode, and a few tokens to
+// verify) and every query row of an fp32 batch run on the split-KV decode kernels; longer requests
+// over a bf16 or int8 cache run on the MFMA tile kernel.
 constexpr int kDefaultSplitTokens = 256;   // keys per decode split (multiple of 16, at most 1024)
-constexpr int kLongSplitTokens = 384;      // the same when a row may span more than 8192 keys
+constexpr int kI8SplitTokens = 320;        // the same over an 8-bit cache
+constexpr int kLongSplitTokens = 384;      // either, when a row may span more than 8192 keys
 constexpr int kTileRows = 256;             // query rows (position x head-in-group) per prefill workgroup
 constexpr int kMaxTileGroup = 128;         // query heads per KV head the prefill tiles accept
 constexpr int kTileKeys = 64;              // keys per MFMA K/V tile

@@ -165,12 +165,17 @@ def test_binding_fails_loudly_without_library(tmp_path):
             pa._lib = saved
 
 
+@pytest.mark.parametrize("dtype", [1, 2])
 @pytest.mark.parametrize("window,max_q", [(0, 0), (8000, 0), (4096, 0), (100, 0), (8000, 8), (0, 2)])
-def test_workspace_size_serves_every_option(lib, window, max_q):
+def test_workspace_size_serves_every_option(lib, window, max_q, dtype):
     """pa_attention_workspace_size() for the sizes bounds what any window and q_len bound needs: a
     call given exactly that many bytes is never refused for its workspace (code 4).  Rows of up to
-    8208 keys sit where the split length changes with the window (256 vs 384 keys)."""
-    d = _desc()
+    8208 keys sit where the split length changes with the window (256 or, over an 8-bit cache, 320
+    keys vs 384)."""
+    d = _desc(dtype=dtype)
+    if dtype == 2:                      # an 8-bit cache needs scale pointers (never read on the host)
+        d.k_scale = ctypes.c_void_p(512)
+        d.v_scale = ctypes.c_void_p(768)
     p = ctypes.c_void_p(16)
     o = ctypes.c_void_p(48)
     for B, T in ((4, 4), (4, 20), (32, 32)):
