@@ -247,7 +247,8 @@ int make_plan(int32_t B, int32_t T, int32_t MB, int32_t Hq, const pa_cache_desc*
   }
   p.total = off;
   const int64_t nzh = ((int64_t)p.qmax * p.group + p.heads_per_wg - 1) / p.heads_per_wg;
-  const int64_t heads = p.bf16 ? (c->num_kv_heads + 3) / 4 : c->num_kv_heads;
+  // KV heads per decode workgroup: 4 (int8), 2 or 4 (bf16: the smaller bounds the grid), 1 (fp32)
+  const int64_t heads = p.i8 ? (c->num_kv_heads + 3) / 4 : p.bf16 ? (c->num_kv_heads + 1) / 2 : c->num_kv_heads;
   const int64_t dec_grid = heads * nzh * p.max_splits * p.rows;
   if (p.run_decode && !p.stream && dec_grid > 0x7FFFFFFF) return fail(PA_ERR_UNSUPPORTED, "batch too large for one launch");
   return PA_OK;
@@ -259,14 +260,11 @@ int get_device(int& dev) {
   return PA_OK;
 }
 
-// Stream-mode workgroups per four KV heads: the decode kernel keeps two workgroups resident per
-// compute unit, so two per CU over all head quads make one full wave of the chip; never more than
-// the rows' blocks fill with runs of `split` keys.  PA_DECODE_WGS overrides the chip-wide count.
-int stream_wgs(const Plan& p, int num_kv_heads, int& out) {
+// Compute units of the current device (looked up once per device).
+int chip_cus(int& cus) {
   int dev = 0;
   int rc = get_device(dev);
   if (rc) return rc;
-  int cus = 0;
   {
     std::lock_guard<std::mutex> lk(g_dev_mu);
     cus = g_dev[dev].cus;
@@ -277,6 +275,16 @@ int stream_wgs(const Plan& p, int num_kv_heads, int& out) {
     std::lock_guard<std::mutex> lk(g_dev_mu);
     g_dev[dev].cus = cus;
   }
+  return PA_OK;
+}
+
+// Stream-mode workgroups per four KV heads: the decode kernel keeps two workgroups resident per
+// compute unit, so two per CU over all head quads make one full wave of the chip; never more than
+// the rows' blocks fill with runs of `split` keys.  PA_DECODE_WGS overrides the chip-wide count.
+int stream_wgs(const Plan& p, int num_kv_heads, int& out) {
+  int cus = 0;
+  int rc = chip_cus(cus);
+  if (rc) return rc;
   static const int over = [] {
     const char* e = std::getenv("PA_DECODE_WGS");
     return e ? std::atoi(e) : 0;
@@ -446,6 +454,14 @@ int launch_call(const Call& c, const Plan& p, char* ws, hipStream_t s, int* chec
       if (p.stream) {
         rc = stream_wgs(p, cache->num_kv_heads, d.stream_wgs);
         if (rc) return rc;
+      } else if (cache->dtype == PA_DTYPE_BF16) {
+        // split-mode bf16 decode: two-KV-head workgroups (one wave per SIMD) when the grid of
+        // four-head ones (two resident per CU) makes at least two chip-wide rounds
+        int cus = 0;
+        rc = chip_cus(cus);
+        if (rc) return rc;
+        const int64_t units4 = (int64_t)((cache->num_kv_heads + 3) / 4) * p.max_splits * p.rows;
+        d.pair_wgs = units4 >= 4 * (int64_t)cus;
       }
       d.window = c.window;
       d.scale_log2 = scale_log2;

@@ -91,9 +91,14 @@ __device__ __forceinline__ bool get_unit(const DecodeArgs& a, int nzh, Unit& u) 
 }  // namespace
 
 // ------------------------------------------------------------------------------------------
-// bf16: matrix-core split kernel.  A workgroup covers four adjacent KV heads of the
-// same request and split (one wave each), so together its waves read contiguous 4 x 256-byte
-// spans of every token row.  Each wave streams all blocks of the split for its head: K and V of a
+// bf16: matrix-core split kernel.  A workgroup covers NW adjacent KV heads of the same request
+// and split (one wave each), so together its waves read contiguous NW x 256-byte spans of every
+// token row.  NW = 4 with two waves per SIMD (two workgroups, eight waves per CU), or, on grids of
+// at least two chip-wide rounds, NW = 2 with one wave per SIMD (two workgroups, four waves per CU,
+// each wave with the whole register file).  Measured on this chip: the two-wave form with half the
+// copies in flight per CU is faster on such grids (c2 200-201 against 205 us, c5 169 against 174),
+// and neither more waves per CU nor spill-free registers alone gave it; on grids of about one round
+// the four-wave form is faster (c5 under a 4096-key window 43 against 46 us).  Each wave streams all blocks of the split for its head: K and V of a
 // block are copied by direct global->LDS loads into one slot of a per-wave double buffer while the
 // wave computes on the other slot (rows' 16-byte chunks XOR-swizzled so the K operand reads and the
 // V transpose reads are free of bank conflicts).  The copies are issued as inline assembly and
@@ -138,8 +143,8 @@ __device__ __forceinline__ int load_ids_sync(const int32_t* p, int count) {
 // model, or more than 16 query heads per KV head) carries two column groups of 16 through each pass
 // over the split's keys, so K and V are read once for 32 columns; the choice is made per workgroup
 // from its own row, and both forms are compiled into the kernel.
-template <int D, bool STREAM>
-__global__ __launch_bounds__(256, 2) void decode_mfma_kernel(DecodeArgs a) {
+template <int D, bool STREAM, int NW>
+__global__ __launch_bounds__(64 * NW, NW == 2 ? 1 : 2) void decode_mfma_kernel(DecodeArgs a) {
   constexpr int NKK = D / 32;                 // 16x16x32 k-steps over d for S^T
   constexpr int NT = D / 16;                  // 16-row d tiles of O^T
   constexpr int ROWB = D * 2;                 // bytes of one head's K or V row
@@ -148,16 +153,16 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(DecodeArgs a) {
   constexpr int IPB = kBlock / RPI;           // copies per 16-row block
   constexpr int VB = kBlock * ROWB;           // bytes per staged K (or V) block
   constexpr int NCP = 2 * IPB;                // copies per block (K and V)
-  __shared__ __align__(16) char sKV[2 * 4 * 2 * VB];   // [slot][wave][K block, V block]
+  __shared__ __align__(16) char sKV[2 * NW * 2 * VB];  // [slot][wave][K block, V block]
 
   // unit: (row, split) -- or, in stream mode, run pw of the concatenated blocks of all rows, taken
-  // as one piece per row it meets -- for head quad `quad` (the quad fastest); the wave's KV head is
-  // 4 * quad + w.  A row with more (position, head) columns than NG MFMAs hold runs its column
+  // as one piece per row it meets -- for head group `quad` of NW KV heads (fastest); the wave's KV
+  // head is NW * quad + w.  A row with more (position, head) columns than NG MFMAs hold runs its column
   // groups NG at a time in the same workgroup (the K/V re-read comes straight after the first pass).
-  const int nq = (a.num_kv_heads + 3) / 4;
+  const int nq = (a.num_kv_heads + NW - 1) / NW;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int quad = blockIdx.x % nq;
-  const int g = 4 * quad + w;
+  const int g = NW * quad + w;
   if (g >= a.num_kv_heads) return;                         // waves are independent: no barriers
   int row, split, b, t0, n_keys, ql, ctx, lo_min, lo_max, k0, k1, n_splits, ncol_all;
 
@@ -200,7 +205,7 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(DecodeArgs a) {
       tr_off[tt] = r * ROWB + ((lq ^ dswz<D>(r)) * 16) + (col & 1) * 8;
     }
 
-    char* const mine = sKV + w * 2 * VB;                       // this wave's slot 0; slot 1 is 8 * VB on
+    char* const mine = sKV + w * 2 * VB;                       // this wave's slot 0; slot 1 is 2NW * VB on
     auto issue = [&](int i, int slot) {                        // block kb0 + i: K and V into the slot
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");      // the slot's earlier reads are done
       if (i - ids_base >= kWave) {                             // next 64 ids (once per 64 blocks)
@@ -209,7 +214,7 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(DecodeArgs a) {
       }
       const char* kb = kbase + (int64_t)__builtin_amdgcn_readlane(ids, i - ids_base) * blkbytes;
       const char* vb = vbase + (kb - kbase);
-      const uint32_t l = __builtin_amdgcn_readfirstlane(lds_u32(mine + slot * 8 * VB));
+      const uint32_t l = __builtin_amdgcn_readfirstlane(lds_u32(mine + slot * 2 * NW * VB));
 #pragma unroll
       for (int j = 0; j < IPB; ++j) dma16(kb, k_lane[j], l + 1024 * j);
 #pragma unroll
@@ -259,7 +264,7 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(DecodeArgs a) {
       auto consume_as = [&](auto edge_tag, int i, int slot) {
         constexpr bool EDGE = decltype(edge_tag)::value;
         const int s0 = (kb0 + i) * kBlock;
-        const char* kw = mine + slot * 8 * VB;
+        const char* kw = mine + slot * 2 * NW * VB;
         bf16x8 kop[NKK];
 #pragma unroll
         for (int kk = 0; kk < NKK; ++kk) kop[kk] = *reinterpret_cast<const bf16x8*>(kw + k_rd[kk]);
@@ -761,8 +766,9 @@ namespace {
 template <int D>
 hipError_t mfma_dispatch(const DecodeArgs& a, dim3 g, hipStream_t s) {
   if (a.heads_per_wg < 1 || a.heads_per_wg > 16) return hipErrorInvalidValue;   // 16 MFMA columns
-  if (a.stream_wgs > 0) decode_mfma_kernel<D, true><<<g, dim3(256), 0, s>>>(a);
-  else decode_mfma_kernel<D, false><<<g, dim3(256), 0, s>>>(a);
+  if (a.stream_wgs > 0) decode_mfma_kernel<D, true, 4><<<g, dim3(256), 0, s>>>(a);
+  else if (a.pair_wgs) decode_mfma_kernel<D, false, 2><<<g, dim3(128), 0, s>>>(a);
+  else decode_mfma_kernel<D, false, 4><<<g, dim3(256), 0, s>>>(a);
   return hipGetLastError();
 }
 template <int D, bool BF16>
@@ -781,8 +787,9 @@ hipError_t valu_dispatch(const DecodeArgs& a, dim3 g, hipStream_t s) {
 
 hipError_t launch_decode_split(const DecodeArgs& a, int head_dim, bool bf16, hipStream_t s) {
   const int64_t nzh = ((int64_t)a.qmax * a.group + a.heads_per_wg - 1) / a.heads_per_wg;
-  const int64_t heads = bf16 ? (a.num_kv_heads + 3) / 4 : a.num_kv_heads;   // MFMA: 4 KV heads per WG
-  // MFMA: one workgroup per (row, split) or stream_wgs runs, per head quad, column groups looping
+  const int nw = (a.stream_wgs == 0 && a.pair_wgs) ? 2 : 4;                   // MFMA: KV heads per WG
+  const int64_t heads = bf16 ? (a.num_kv_heads + nw - 1) / nw : a.num_kv_heads;
+  // MFMA: one workgroup per (row, split) or stream_wgs runs, per group of nw KV heads, column groups looping
   // inside the workgroup; fp32: one workgroup per (row, split, column group)
   const int64_t grid = bf16 ? heads * (a.stream_wgs > 0 ? a.stream_wgs : a.max_splits * a.num_rows)
                             : heads * nzh * a.max_splits * a.num_rows;

@@ -353,6 +353,30 @@ def test_argmax_probe_bit_exact(dtype, prefill):
                 assert np.array_equal(o[r], expect), (target, r)
 
 
+def test_two_and_four_head_decode_workgroups_agree_bitwise():
+    """bf16 decode rows are served by workgroups of four KV heads, or of two (one wave per SIMD) on
+    grids of at least two chip-wide rounds.  The same rows in a grid just under that size and, with
+    one more row, just over it give identical outputs bit for bit: every wave computes its KV head
+    the same way in both forms."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    Hkv, splits = 8, 16                       # rows of up to 4096 keys: 16 splits of 256 keys
+    over = -(-4 * cus // ((Hkv // 4) * splits))
+    rng = np.random.default_rng(21)
+    lens = rng.integers(3000, 4096, size=over, endpoint=True)
+    w = W.make_batch(21, lens, np.ones(over, np.int64), 32, Hkv, 128, "bf16", max_blocks=256)
+    st = w.steps[0]
+    n = over - 1
+    st_under = W.Step(q=st.q[:n], k_new=st.k_new[:n], v_new=st.v_new[:n], slot_mapping=st.slot_mapping[:n],
+                      seq_lens=st.seq_lens[:n], query_start_loc=st.query_start_loc[:n + 1],
+                      block_tables=st.block_tables[:n])
+    o_over = GpuState(w).step(st)
+    o_under = GpuState(w).step(st_under)
+    say(f"  {over} rows (two-head workgroups) against {n} (four-head workgroups)")
+    assert np.array_equal(o_over[:n], o_under)
+    compare(o_over, oracle_out(w, st, w.k_cache0.copy(), w.v_cache0.copy(), rows=[0, n // 2, n]), "bf16",
+            rows=[0, n // 2, n], what="two-head workgroups")
+
+
 def test_repeat_runs_are_bitwise_identical():
     w = W.make_batch(8, [900, 64, 3000], [1, 64, 1], 32, 8, 128, "bf16")
     g = GpuState(w)
