@@ -45,10 +45,14 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+# Sources a kernel's HBM traffic depends on: the kernel, its helpers and the host code that sets its
+# launch (split lengths, workgroup forms, tile sizes).
 KERNEL_SOURCES = {
     "decode_split": ["attention_paged_kv_amd/csrc/pa_decode.hip", "attention_paged_kv_amd/csrc/pa_decode_i8.hip",
-                     "attention_paged_kv_amd/csrc/pa_rows.h", "attention_paged_kv_amd/csrc/pa_common.h"],
-    "prefill_tile": ["attention_paged_kv_amd/csrc/pa_prefill.hip", "attention_paged_kv_amd/csrc/pa_common.h"],
+                     "attention_paged_kv_amd/csrc/pa_rows.h", "attention_paged_kv_amd/csrc/pa_common.h",
+                     "attention_paged_kv_amd/csrc/pa_internal.h", "attention_paged_kv_amd/csrc/pa_api.hip"],
+    "prefill_tile": ["attention_paged_kv_amd/csrc/pa_prefill.hip", "attention_paged_kv_amd/csrc/pa_common.h",
+                     "attention_paged_kv_amd/csrc/pa_internal.h", "attention_paged_kv_amd/csrc/pa_api.hip"],
 }
 
 
