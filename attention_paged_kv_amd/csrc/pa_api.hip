@@ -278,8 +278,8 @@ int chip_cus(int& cus) {
   return PA_OK;
 }
 
-// Stream-mode workgroups per four KV heads: the decode kernel keeps two workgroups resident per
-// compute unit, so two per CU over all head quads make one full wave of the chip; never more than
+// Stream-mode workgroups per two KV heads: the decode kernel keeps two workgroups resident per
+// compute unit, so two per CU over all head pairs make one full wave of the chip; never more than
 // the rows' blocks fill with runs of `split` keys.  PA_DECODE_WGS overrides the chip-wide count.
 int stream_wgs(const Plan& p, int num_kv_heads, int& out) {
   int cus = 0;
@@ -289,7 +289,7 @@ int stream_wgs(const Plan& p, int num_kv_heads, int& out) {
     const char* e = std::getenv("PA_DECODE_WGS");
     return e ? std::atoi(e) : 0;
   }();
-  const int64_t nq = (num_kv_heads + 3) / 4;
+  const int64_t nq = (num_kv_heads + 1) / 2;
   const int64_t chip = over > 0 ? over : 2 * (int64_t)cus;
   const int64_t fill = ((int64_t)p.rows * p.span_blocks * PA_BLOCK_SIZE + p.split - 1) / p.split;
   out = (int)std::max<int64_t>(1, std::min<int64_t>(std::max<int64_t>(1, chip / nq), fill));

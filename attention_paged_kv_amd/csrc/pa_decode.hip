@@ -94,11 +94,13 @@ __device__ __forceinline__ bool get_unit(const DecodeArgs& a, int nzh, Unit& u) 
 // bf16: matrix-core split kernel.  A workgroup covers NW adjacent KV heads of the same request
 // and split (one wave each), so together its waves read contiguous NW x 256-byte spans of every
 // token row.  NW = 4 with two waves per SIMD (two workgroups, eight waves per CU), or, on grids of
-// at least two chip-wide rounds, NW = 2 with one wave per SIMD (two workgroups, four waves per CU,
-// each wave with the whole register file).  Measured on this chip: the two-wave form with half the
+// at least two chip-wide rounds and always in stream mode, NW = 2 with one wave per SIMD (two
+// workgroups, four waves per CU, each wave with the whole register file).  Measured on this chip: the two-wave form with half the
 // copies in flight per CU is faster on such grids (c2 200-201 against 205 us, c5 169 against 174),
 // and neither more waves per CU nor spill-free registers alone gave it; on grids of about one round
-// the four-wave form is faster (c5 under a 4096-key window 43 against 46 us).  Each wave streams all blocks of the split for its head: K and V of a
+// the four-wave form is faster (c5 under a 4096-key window 43 against 46 us).  Stream mode (rows of
+// tokens to verify, balanced runs) gains on every grid: c5 verifying 4 tokens 167 against 183 us,
+// c2 209 against 217, the windowed c5 48 against 50.  Each wave streams all blocks of the split for its head: K and V of a
 // block are copied by direct global->LDS loads into one slot of a per-wave double buffer while the
 // wave computes on the other slot (rows' 16-byte chunks XOR-swizzled so the K operand reads and the
 // V transpose reads are free of bank conflicts).  The copies are issued as inline assembly and
@@ -766,7 +768,7 @@ namespace {
 template <int D>
 hipError_t mfma_dispatch(const DecodeArgs& a, dim3 g, hipStream_t s) {
   if (a.heads_per_wg < 1 || a.heads_per_wg > 16) return hipErrorInvalidValue;   // 16 MFMA columns
-  if (a.stream_wgs > 0) decode_mfma_kernel<D, true, 4><<<g, dim3(256), 0, s>>>(a);
+  if (a.stream_wgs > 0) decode_mfma_kernel<D, true, 2><<<g, dim3(128), 0, s>>>(a);
   else if (a.pair_wgs) decode_mfma_kernel<D, false, 2><<<g, dim3(128), 0, s>>>(a);
   else decode_mfma_kernel<D, false, 4><<<g, dim3(256), 0, s>>>(a);
   return hipGetLastError();
@@ -787,7 +789,7 @@ hipError_t valu_dispatch(const DecodeArgs& a, dim3 g, hipStream_t s) {
 
 hipError_t launch_decode_split(const DecodeArgs& a, int head_dim, bool bf16, hipStream_t s) {
   const int64_t nzh = ((int64_t)a.qmax * a.group + a.heads_per_wg - 1) / a.heads_per_wg;
-  const int nw = (a.stream_wgs == 0 && a.pair_wgs) ? 2 : 4;                   // MFMA: KV heads per WG
+  const int nw = (a.stream_wgs > 0 || a.pair_wgs) ? 2 : 4;                     // MFMA: KV heads per WG
   const int64_t heads = bf16 ? (a.num_kv_heads + nw - 1) / nw : a.num_kv_heads;
   // MFMA: one workgroup per (row, split) or stream_wgs runs, per group of nw KV heads, column groups looping
   // inside the workgroup; fp32: one workgroup per (row, split, column group)

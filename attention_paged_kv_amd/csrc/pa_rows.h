@@ -41,7 +41,7 @@ __device__ __forceinline__ int split_origin(const DecodeArgs& a, int n_keys, int
 
 // ---- stream mode (bf16 decode) ----
 // The 16-key blocks that the rows' passes cover, concatenated in row order, are dealt out in equal
-// runs of L blocks to stream_wgs workgroups per four KV heads.  A run may end one row and begin the
+// runs of L blocks to stream_wgs workgroups per two KV heads.  A run may end one row and begin the
 // next; each (row, run) piece is a partial softmax of the row, like a split, and a row's pieces
 // are merged as splits are.  Every workgroup reads the same number of blocks, so the launch has
 // no tail of workgroups still running while the rest of the chip idles.
