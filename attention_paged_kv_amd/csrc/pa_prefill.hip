@@ -31,8 +31,8 @@
 // visible key, and tiles crossing the window's lower edge are masked as well; keys older than the
 // request's first window are never read (their blocks may be gone), a valid row stands in.
 // Scores are in log2 units: Q is multiplied by scale * log2(e) once and rounded to bf16.  Each row
-// keeps a reference max m_ref, a bf16 value, and one more 16-wide k-step of the QK^T products (a
-// ones column of K against -m_ref in Q) makes the products s - m_ref directly, so the
+// keeps a reference max m_ref, a bf16 value, and its QK^T products start from -m_ref in the
+// accumulators instead of zero, so they give s - m_ref directly and the
 // probabilities are exp2 of the accumulators with no vector arithmetic before the exponential.
 // The reference is only moved (and O rescaled) when a row with none sees its first key or some
 // row's max exceeds it by more than 2^8; between moves, probabilities are at most about 2^8.
@@ -209,16 +209,15 @@ __global__ __launch_bounds__(512, 1) void prefill_tile_kernel(TileArgs a) {
   const int n_full = (sl / kBlock - bw + 3) / 4;  // count of kt with (4kt + bw + 1) * 16 <= sl
   SyncWindow win;
 
-  // m_ref: the row's reference max (log2 units, a bf16 value so that -m_ref is exact in an MFMA
-  // operand); has_ref: whether the row has one yet (before its first visible key it does not, and
-  // m_ref is 0).  The products give s - m_ref directly: one more k-step multiplies the ones column
-  // (A, lane half 0, element 0) with -m_ref (B, lane half 0, element 0).
+  // m_ref: the row's reference max (log2 units, rounded to a bf16 value); has_ref: whether the row
+  // has one yet (before its first visible key it does not, and m_ref is 0).  The products give
+  // s - m_ref directly: both QK^T chains start from mref16, the lane's -m_ref in every accumulator
+  // entry (a lane's 16 entries all belong to its own row), instead of from zero.
   float m_ref = 0.f, l_run = 0.f;
   bool has_ref = false;
-  bf16x8 ones_a, mref_b;
+  floatx16 mref16;
 #pragma unroll
-  for (int e = 0; e < 8; ++e) { ones_a[e] = (__bf16)0.f; mref_b[e] = (__bf16)0.f; }
-  if (half == 0) ones_a[0] = (__bf16)1.f;
+  for (int v = 0; v < 16; ++v) mref16[v] = 0.f;
   floatx16 O[NDT];
 #pragma unroll
   for (int dt = 0; dt < NDT; ++dt)
@@ -258,11 +257,7 @@ __global__ __launch_bounds__(512, 1) void prefill_tile_kernel(TileArgs a) {
   auto tile_math = [&](int kt, const char* kl, const char* vl) {
     if (wp1 < wp0 || kt * kTileKeys > wave_newest || kt * kTileKeys + kTileKeys - 1 < wave_oldest) return;
     // ---- S^T = K Q^T : two 32-key sub-tiles, chains interleaved, operands read one step ahead ----
-    floatx16 S0, S1;
-#pragma unroll
-    for (int v = 0; v < 16; ++v) { S0[v] = 0.f; S1[v] = 0.f; }
-    S0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ones_a, mref_b, S0, 0, 0, 0);   // -m_ref
-    S1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ones_a, mref_b, S1, 0, 0, 0);
+    floatx16 S0 = mref16, S1 = mref16;                 // -m_ref
     // K operands are read PD k-steps ahead of their products; the scheduling barriers keep the
     // compiler from sinking the reads next to their use (it otherwise waits on every pair)
     constexpr int PD = 2;
@@ -316,7 +311,8 @@ __global__ __launch_bounds__(512, 1) void prefill_tile_kernel(TileArgs a) {
           for (int v = 0; v < 16; ++v) O[dt][v] *= alpha;
         m_ref = m_new;
         has_ref = true;
-        if (half == 0) mref_b[0] = (__bf16)(-m_new);
+#pragma unroll
+        for (int v = 0; v < 16; ++v) mref16[v] = -m_new;
       }
 #pragma unroll
       for (int v = 0; v < 16; ++v) { S0[v] -= shift; S1[v] -= shift; }
