@@ -591,17 +591,16 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeArgs a) {
 }
 
 // ------------------------------------------------------------------------------------------
-// Cross-split merge: one workgroup per (row, position, query head); splits are read in parallel.
+// Cross-split merge: one workgroup per (row, position, query head).  Groups of its threads each fold
+// a share of the splits in one pass (a running max, their partials read together), and the groups
+// are then combined in LDS: one round of reads instead of a max pass, a sum pass and an output pass.
 // ------------------------------------------------------------------------------------------
 template <int D, bool BF16>
 __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a) {
   constexpr int CH = D / 4;                  // float4 chunks of a row
   constexpr int NG = 256 / CH;               // split groups
-  constexpr int WCAP = 1024;                 // splits whose weights are kept in LDS
-  __shared__ float sw[WCAP];
-  __shared__ float red[256 / kWave];
   __shared__ float4 racc[NG][CH];
-  __shared__ float s_m, s_l;
+  __shared__ float sm[NG], sl[NG];
 
   const int h = blockIdx.x % a.num_q_heads;
   const int r = (blockIdx.x / a.num_q_heads) % a.qmax;
@@ -619,62 +618,62 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a) {
   }
   if (n <= 1) return;                                       // written directly by the split kernel
   const int tid = threadIdx.x;
-  const int lane = tid & (kWave - 1), w = tid >> 6;
   const int64_t pbase = partial_index(a, row, r, 0, h);    // split s adds s * num_q_heads
   const float* ml = a.part_ml;
 
-  float mx = -INFINITY;
-  for (int s = tid; s < n; s += 256) mx = fmaxf(mx, ml[(pbase + (int64_t)s * a.num_q_heads) * 2]);
-  for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
-  if (lane == 0) red[w] = mx;
-  __syncthreads();
-  if (tid == 0) s_m = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-  __syncthreads();
-  const float M = s_m;
-  float ls = 0.f;
-  for (int s = tid; s < n; s += 256) {
-    const int64_t p = (pbase + (int64_t)s * a.num_q_heads) * 2;
-    const float wgt = fast_exp2(ml[p] - M);
-    if (s < WCAP) sw[s] = wgt;
-    ls = fmaf(wgt, ml[p + 1], ls);
-  }
-  for (int o = 32; o > 0; o >>= 1) ls += __shfl_xor(ls, o);
-  __syncthreads();
-  if (lane == 0) red[w] = ls;
-  __syncthreads();
-  if (tid == 0) s_l = (red[0] + red[1]) + (red[2] + red[3]);
-  __syncthreads();
-
+  // one pass: group g folds splits g, g + NG, ... into (m, l, o) with a running max (all threads
+  // of a group see the same splits, so the same m and l), then the groups are combined in LDS
   const int cidx = tid % CH, gidx = tid / CH;
+  float m = -INFINITY, l = 0.f;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll 4
   for (int s = gidx; s < n; s += NG) {
     const int64_t p = pbase + (int64_t)s * a.num_q_heads;
-    const float wgt = s < WCAP ? sw[s] : fast_exp2(ml[p * 2] - M);
+    const float ms = ml[p * 2], ls = ml[p * 2 + 1];
     const float4 o = reinterpret_cast<const float4*>(a.part_o + p * D)[cidx];
-    acc.x = fmaf(wgt, o.x, acc.x);
-    acc.y = fmaf(wgt, o.y, acc.y);
-    acc.z = fmaf(wgt, o.z, acc.z);
-    acc.w = fmaf(wgt, o.w, acc.w);
+    const float mn = fmaxf(m, ms);
+    const float wo = (m == -INFINITY) ? 0.f : fast_exp2(m - mn);   // weight of what is folded so far
+    const float ws = (ms == -INFINITY) ? 0.f : fast_exp2(ms - mn); // a split that saw no key: 0
+    l = fmaf(ls, ws, l * wo);
+    acc.x = fmaf(o.x, ws, acc.x * wo);
+    acc.y = fmaf(o.y, ws, acc.y * wo);
+    acc.z = fmaf(o.z, ws, acc.z * wo);
+    acc.w = fmaf(o.w, ws, acc.w * wo);
+    m = mn;
   }
   racc[gidx][cidx] = acc;
+  if (cidx == 0) {
+    sm[gidx] = m;
+    sl[gidx] = l;
+  }
   __syncthreads();
   if (tid < CH) {
-    float4 r = racc[0][tid];
-    for (int gq = 1; gq < NG; ++gq) {
-      const float4 x = racc[gq][tid];
-      r.x += x.x; r.y += x.y; r.z += x.z; r.w += x.w;
+    float M = sm[0];
+#pragma unroll
+    for (int g = 1; g < NG; ++g) M = fmaxf(M, sm[g]);
+    float4 rr = make_float4(0.f, 0.f, 0.f, 0.f);
+    float L = 0.f;
+#pragma unroll
+    for (int g = 0; g < NG; ++g) {
+      if (sm[g] == -INFINITY) continue;                     // a group with no split (n < NG)
+      const float wg = fast_exp2(sm[g] - M);
+      const float4 x = racc[g][tid];
+      L = fmaf(sl[g], wg, L);
+      rr.x = fmaf(x.x, wg, rr.x);
+      rr.y = fmaf(x.y, wg, rr.y);
+      rr.z = fmaf(x.z, wg, rr.z);
+      rr.w = fmaf(x.w, wg, rr.w);
     }
-    const float inv = 1.f / s_l;
+    const float inv = 1.f / L;
     const int64_t o = ((int64_t)t * a.num_q_heads + h) * D + 4 * tid;
     if (BF16) {
       uint2 pk;
-      pk.x = pack_bf16x2(r.x * inv, r.y * inv);
-      pk.y = pack_bf16x2(r.z * inv, r.w * inv);
+      pk.x = pack_bf16x2(rr.x * inv, rr.y * inv);
+      pk.y = pack_bf16x2(rr.z * inv, rr.w * inv);
       *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(a.out) + o) = pk;
     } else {
       *reinterpret_cast<float4*>(reinterpret_cast<float*>(a.out) + o) =
-          make_float4(r.x * inv, r.y * inv, r.z * inv, r.w * inv);
+          make_float4(rr.x * inv, rr.y * inv, rr.z * inv, rr.w * inv);
     }
   }
 }
