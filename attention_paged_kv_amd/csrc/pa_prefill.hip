@@ -394,17 +394,21 @@ __global__ __launch_bounds__(512, 1) void prefill_tile_kernel(TileArgs a) {
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
 
-    // two tiles per iteration so that each buffer is a fixed LDS variable
+    // two tiles per iteration so that each buffer is a fixed LDS variable (the second one
+    // conditional rather than a break out of the loop: a break leaves the loop-carried values
+    // undefined on its path, and the compiler then fills them from a register the last product
+    // writes, which makes the wave wait for that product before the barrier)
     for (int kt = kt_lo; kt < n_kt; kt += 2) {
       if (kt + 1 < n_kt) stage(kt + 1, sK1, sV1);     // in flight during this tile's math
       tile_math(kt, sK0, sV0);
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       __syncthreads();
-      if (kt + 1 >= n_kt) break;
-      if (kt + 2 < n_kt) stage(kt + 2, sK0, sV0);
-      tile_math(kt + 1, sK1, sV1);
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      __syncthreads();
+      if (kt + 1 < n_kt) {
+        if (kt + 2 < n_kt) stage(kt + 2, sK0, sV0);
+        tile_math(kt + 1, sK1, sV1);
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+      }
     }
 
 
@@ -495,12 +499,13 @@ __global__ __launch_bounds__(512, 1) void prefill_tile_kernel(TileArgs a) {
       tile_math(kt, sK0, sV0);
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       __syncthreads();
-      if (kt + 1 >= n_kt) break;
-      if (kt + 2 < n_kt) convert(sK8a, sV8a, sK0, sV0);     // tile kt's math is done
-      if (kt + 3 < n_kt) stage8(kt + 3, sK8b, sV8b);
-      tile_math(kt + 1, sK1, sV1);
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      __syncthreads();
+      if (kt + 1 < n_kt) {                                  // (conditional, not a break: see above)
+        if (kt + 2 < n_kt) convert(sK8a, sV8a, sK0, sV0);   // tile kt's math is done
+        if (kt + 3 < n_kt) stage8(kt + 3, sK8b, sV8b);
+        tile_math(kt + 1, sK1, sV1);
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+      }
     }
   }
 
