@@ -353,7 +353,8 @@ def test_argmax_probe_bit_exact(dtype, prefill):
                 assert np.array_equal(o[r], expect), (target, r)
 
 
-def test_two_and_four_head_decode_workgroups_agree_bitwise():
+@pytest.mark.parametrize("d", [64, 128])
+def test_two_and_four_head_decode_workgroups_agree_bitwise(d):
     """bf16 decode rows are served by workgroups of four KV heads, or of two (one wave per SIMD) on
     grids of at least two chip-wide rounds.  The same rows in a grid just under that size and, with
     one more row, just over it give identical outputs bit for bit: every wave computes its KV head
@@ -363,7 +364,7 @@ def test_two_and_four_head_decode_workgroups_agree_bitwise():
     over = -(-4 * cus // ((Hkv // 4) * splits))
     rng = np.random.default_rng(21)
     lens = rng.integers(3000, 4096, size=over, endpoint=True)
-    w = W.make_batch(21, lens, np.ones(over, np.int64), 32, Hkv, 128, "bf16", max_blocks=256)
+    w = W.make_batch(21, lens, np.ones(over, np.int64), 32, Hkv, d, "bf16", max_blocks=256)
     st = w.steps[0]
     n = over - 1
     st_under = W.Step(q=st.q[:n], k_new=st.k_new[:n], v_new=st.v_new[:n], slot_mapping=st.slot_mapping[:n],
@@ -371,7 +372,7 @@ def test_two_and_four_head_decode_workgroups_agree_bitwise():
                       block_tables=st.block_tables[:n])
     o_over = GpuState(w).step(st)
     o_under = GpuState(w).step(st_under)
-    say(f"  {over} rows (two-head workgroups) against {n} (four-head workgroups)")
+    say(f"  d = {d}: {over} rows (two-head workgroups) against {n} (four-head workgroups)")
     assert np.array_equal(o_over[:n], o_under)
     compare(o_over, oracle_out(w, st, w.k_cache0.copy(), w.v_cache0.copy(), rows=[0, n // 2, n]), "bf16",
             rows=[0, n // 2, n], what="two-head workgroups")
