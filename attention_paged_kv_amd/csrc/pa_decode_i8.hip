@@ -37,13 +37,26 @@ typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
 constexpr float kCodeBias = 1152.f;          // value of fp16 bits 0x6400 | (code ^ 0x80)
 
-// Physical 16-byte chunk of logical chunk q in row r of staged block blk is q ^ vswz(blk, r):
-// with it the transpose reads of a wave hit every LDS bank once.
+// Per-wave staging (a wave's own head, D bytes per staged row): the physical 16-byte chunk of
+// logical chunk q in row r of staged V block blk is q ^ vswz(blk, r), so that the transpose reads of
+// a wave hit every LDS bank once, and in staged K row r it is q ^ kswz(r), so that the 16 rows read
+// by one 16-lane group for the same logical chunk land on distinct bank groups.
 template <int D>
 __device__ __forceinline__ int vswz(int blk, int r) {
   if constexpr (D == 128) return ((r ^ (r >> 2)) & 3) | (blk << 2);
   else return (((r >> 1) ^ (r >> 2)) & 1) | (blk << 1);
 }
+template <int D>
+__device__ __forceinline__ int kswz(int r) {
+  if constexpr (D == 128) return (r >> 1) & 7;
+  else return (r >> 2) & 3;
+}
+
+// Whole-row staging (the workgroup's NW heads, NW * D bytes per staged row, a multiple of 256, so
+// every row starts on the same LDS bank): physical chunk p of staged row r holds logical chunk
+// p ^ row_swz(r) of the NW heads' bytes, for K and V alike; the 16 rows that a 16-lane group reads
+// for one logical chunk land on 16 different bank groups, and so do the rows of a transpose read.
+__device__ __forceinline__ int row_swz(int r) { return r & 15; }
 
 // Eight int8 codes (little-endian in lo, hi) as fp16 values 1152 + code, exactly.  v_perm_b32
 // picks bytes of {0x64646464 : x}: selector 0-3 = byte of x, 4 = 0x64.
@@ -70,14 +83,6 @@ __device__ __forceinline__ f16x8 codes_f16(uint32_t lo, uint32_t hi) {
   return r;
 }
 
-// Physical 16-byte chunk of logical chunk q in staged K row r (D / 16 chunks per row) is q ^ kswz(r):
-// the 16 rows read by one 16-lane group for the same logical chunk land on distinct bank groups.
-template <int D>
-__device__ __forceinline__ int kswz(int r) {
-  if constexpr (D == 128) return (r >> 1) & 7;
-  else return (r >> 2) & 3;
-}
-
 // 8-bit transpose read: in each 16-lane group, lane 2e + h gives the address of bytes 8h..8h+7 of
 // row e of an 8 x 16-byte tile; lane j receives column j of the tile (rows 0..7).
 typedef __attribute__((address_space(3))) i32x2 lds_i32x2_t;
@@ -87,22 +92,36 @@ __device__ __forceinline__ i32x2 lds_read_tr8(const char* p) {
 
 }  // namespace
 
-// NW waves per workgroup, one adjacent KV head each: together they read NW * d contiguous bytes of
-// every token row they visit.  K and V codes of a 32-key unit are copied by direct global->LDS loads
-// into one slot of a per-wave double buffer while the wave computes the other slot; the copies are
-// inline assembly waited for with explicit vmcnt counts (see dma16), so the next unit's copies stay
-// in flight during the arithmetic.
-template <int D, int NW>
+// NW = 4 waves per workgroup, one adjacent KV head each.  K and V codes of a 32-key unit are copied
+// by direct global->LDS loads (inline assembly waited for with explicit vmcnt counts, see dma16)
+// into one slot of a double buffer while the other slot is computed, in one of two forms:
+//   * per wave (ROWS = false): each wave copies its own head's D-byte pieces of the unit's 32 token
+//     rows into a buffer of its own; the waves run independently, with no barriers, and the wait
+//     leaves the next unit's copies in flight during the arithmetic;
+//   * whole rows (ROWS = true): the workgroup stages the NW heads' NW * D contiguous bytes of each
+//     token row, the 32 rows split among the waves, each 1 KiB copy covering 1024 / (NW * D) rows;
+//     a barrier per unit ends unit u's copies (and every wave's reads of unit u - 1), after which
+//     the copies of unit u + 1 go out and stay in flight while unit u is computed.
+// Whole rows turn each copy into runs of 256 or 512 contiguous bytes instead of one head's 64 or
+// 128; that pays where cache rows are 4 KiB or wider and costs where they are narrower (the launch
+// picks the form by the row width).
+template <int D, int NW, bool ROWS>
 __global__ __launch_bounds__(64 * NW, 2) void decode_i8_kernel(DecodeArgs a) {
+  static_assert(NW == 4, "whole-row staging splits the unit's 32 rows 8 per wave");
   constexpr int NKK = D / 32;                 // 16x16x32 k-steps over d for S^T (8 codes per lane)
   constexpr int NT = D / 16;                  // 16-row d tiles of O^T
   constexpr int KL = D / 64;                  // 16-byte K loads per lane and block
-  constexpr int CPR = D / 16;                 // 16-byte chunks per row
-  constexpr int RPI = 1024 / D;               // rows per wave-wide 1 KiB copy
-  constexpr int IPB = kBlock / RPI;           // copies per 16-row block
-  constexpr int UB = 2 * kBlock * D;          // bytes of one staged 32-key unit (two blocks)
-  constexpr int NCP = 4 * IPB;                // copies per unit (two blocks of K and of V)
-  __shared__ __align__(16) char sKV[2 * NW * 2 * UB];   // [slot][wave][K unit, V unit]
+  constexpr int CPH = D / 16;                 // 16-byte chunks per head in a row
+  constexpr int RB = ROWS ? NW * D : D;       // bytes of one staged token row
+  constexpr int CPS = RB / 16;                // 16-byte chunks per staged row
+  constexpr int RPC = 1024 / RB;              // rows per wave-wide 1 KiB copy
+  constexpr int RPW = ROWS ? 2 * kBlock / NW : 2 * kBlock;   // rows of a unit copied by each wave
+  constexpr int CPW = RPW / RPC;              // copies per wave, unit and tensor
+  constexpr int UB = 2 * kBlock * RB;         // bytes of one staged 32-key unit (two blocks)
+  constexpr int NCP = 2 * CPW;                // copies per wave and unit (K and V)
+  static_assert(!ROWS || (RB % 256 == 0 && CPS <= 64 && RPW % RPC == 0 && RPW <= kBlock), "staging shape");
+  // [slot][K unit, V unit], per wave in the per-wave form
+  __shared__ __align__(16) char sKV[2 * (ROWS ? 1 : NW) * 2 * UB];
 
   // unit: (row, split, head group, column group); the wave's KV head is NW * group + w.  Columns
   // are the row's (position, query head) pairs of that KV head, heads_per_wg of them per group: a
@@ -128,11 +147,13 @@ __global__ __launch_bounds__(64 * NW, 2) void decode_i8_kernel(DecodeArgs a) {
   const int k1 = min(k0 + a.split, n_keys);
   const int n_splits = (n_keys - kbeg + a.split - 1) / a.split;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int g = NW * (z / nzh) + w;
-  if (g >= a.num_kv_heads) return;                         // waves are independent: no barriers
+  const int g0 = NW * (z / nzh);                           // the workgroup's first KV head
+  const int g = g0 + w;
+  const bool live = g < a.num_kv_heads;
+  if (!ROWS && !live) return;                              // (whole rows: such a wave only copies)
   const int c0 = (z % nzh) * a.heads_per_wg;               // first column of this group
   const int ncol_all = ql * a.group;
-  if (c0 >= ncol_all) return;
+  if (c0 >= ncol_all) return;                              // (every other return is per workgroup)
 
   const int lane = threadIdx.x & (kWave - 1);
   const int col = lane & 15;                  // S^T / O^T column; also the K row loaded
@@ -192,41 +213,49 @@ __global__ __launch_bounds__(64 * NW, 2) void decode_i8_kernel(DecodeArgs a) {
 
   const int64_t rs = (int64_t)a.num_kv_heads * D;          // bytes per cache token row
   const int64_t blkbytes = kBlock * rs;
-  const char* kbase = reinterpret_cast<const char*>(a.k_cache) + (int64_t)g * D;
-  const char* vbase = reinterpret_cast<const char*>(a.v_cache) + (int64_t)g * D;
   const int32_t* table = a.block_tables + (int64_t)b * a.max_blocks;
   const int kb0 = k0 / kBlock;
   const int nb = (k1 + kBlock - 1) / kBlock - kb0;         // <= 64: splits are at most 1024 keys
   const int nu = (nb + 1) >> 1;                            // 32-key units
   const int ids = lane < nb ? table[kb0 + lane] : 0;       // lane i: id of the split's i-th block
 
-  // K operand j of a block: key row `col`, logical chunk grp + 4j (bytes 64j + 16grp .. +16)
+  // K operand j of a block: key row `col`, this head's logical chunk grp + 4j (channels 64j + 16grp
+  // .. +16); the second block's rows are kBlock rows on, with the same swizzle
   uint32_t k_rd[KL];
 #pragma unroll
-  for (int j = 0; j < KL; ++j) k_rd[j] = col * D + (((grp + 4 * j) ^ kswz<D>(col)) * 16);
-  // copy i of staged block sb: lane -> (row RPI*i + lane / CPR, physical chunk lane % CPR), holding
-  // logical chunk (lane % CPR) ^ swizzle of the cache row
-  uint32_t k_lane[IPB], v_lane[2][IPB];
+  for (int j = 0; j < KL; ++j)
+    k_rd[j] = ROWS ? col * RB + (((w * CPH + grp + 4 * j) ^ row_swz(col)) * 16)
+                   : col * RB + (((grp + 4 * j) ^ kswz<D>(col)) * 16);
+  // copy i of this wave: lane -> staged row ur = (ROWS ? RPW*w : 0) + RPC*i + lane / CPS of the unit
+  // (row ur % 16 of its block ur / 16), physical chunk lane % CPS, which holds the swizzled logical
+  // chunk of the staged bytes; offsets from the block's first byte.  Whole rows: a chunk of a head
+  // past the last one (the last group of a cache whose head count is no multiple of NW) loads the
+  // first head's chunk instead, which stays in bounds and is never read, and K and V share the layout.
+  const int nh = min(NW, a.num_kv_heads - g0);
+  uint32_t k_lane[CPW], v_lane[CPW];
 #pragma unroll
-  for (int i = 0; i < IPB; ++i) {
-    const int r = RPI * i + lane / CPR;
-    k_lane[i] = (uint32_t)(r * rs) + (((lane % CPR) ^ kswz<D>(r)) * 16);
-  }
-#pragma unroll
-  for (int sb = 0; sb < 2; ++sb)
-#pragma unroll
-    for (int i = 0; i < IPB; ++i) {
-      const int r = RPI * i + lane / CPR;
-      v_lane[sb][i] = (uint32_t)(r * rs) + (((lane % CPR) ^ vswz<D>(sb, r)) * 16);
+  for (int i = 0; i < CPW; ++i) {
+    const int ur = (ROWS ? RPW * w : 0) + RPC * i + lane / CPS;
+    const int sb = ur / kBlock, r = ur % kBlock;
+    if constexpr (ROWS) {
+      int q = (lane % CPS) ^ row_swz(ur);
+      if (q >= nh * CPH) q %= CPH;
+      k_lane[i] = v_lane[i] = (uint32_t)(r * rs) + (uint32_t)(g0 * D + q * 16);
+    } else {
+      k_lane[i] = (uint32_t)(r * rs) + (uint32_t)(g * D + (((lane % CPS) ^ kswz<D>(r)) * 16));
+      v_lane[i] = (uint32_t)(r * rs) + (uint32_t)(g * D + (((lane % CPS) ^ vswz<D>(sb, r)) * 16));
     }
+  }
   // transpose read of tile tt: lane 2e + hh of group grp -> key e of the group, i.e. staged block
-  // e / 4, row 4grp + e % 4, channels 16tt + 8hh .. +7
+  // e / 4, row 4grp + e % 4, this head's channels 16tt + 8hh .. +7
   uint32_t tr_off[NT];
   {
     const int e = col >> 1, hh = col & 1;
-    const int sb = e >> 2, r = 4 * grp + (e & 3);
+    const int sb = e >> 2, rr = 4 * grp + (e & 3), r = kBlock * sb + rr;
 #pragma unroll
-    for (int tt = 0; tt < NT; ++tt) tr_off[tt] = sb * (kBlock * D) + r * D + ((tt ^ vswz<D>(sb, r)) * 16) + 8 * hh;
+    for (int tt = 0; tt < NT; ++tt)
+      tr_off[tt] = ROWS ? r * RB + (((w * CPH + tt) ^ row_swz(r)) * 16) + 8 * hh
+                        : r * RB + ((tt ^ vswz<D>(sb, rr)) * 16) + 8 * hh;
   }
 
   float m = -INFINITY, lsum = 0.f;
@@ -235,36 +264,33 @@ __global__ __launch_bounds__(64 * NW, 2) void decode_i8_kernel(DecodeArgs a) {
   for (int tt = 0; tt < NT; ++tt) O[tt] = floatx4{0.f, 0.f, 0.f, 0.f};
 
   // unit u = blocks 2u and 2u + 1 of the split; a missing second block is replaced by the first
-  // (valid memory) and all its keys are masked
-  char* const mine = sKV + w * 2 * UB;                     // this wave's slot 0; slot 1 is NW * 2 * UB on
+  // (valid memory) and all its keys are masked.  The slot of unit u is wave_buf + (u & 1) * SLOT.
+  constexpr int SLOT = (ROWS ? 1 : NW) * 2 * UB;
+  char* const wave_buf = ROWS ? sKV : sKV + w * 2 * UB;
   auto issue = [&](int u, int slot) {
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");    // the slot's earlier reads are done
-    const int i1 = min(2 * u + 1, nb - 1);
-    const int64_t o0 = (int64_t)__builtin_amdgcn_readlane(ids, 2 * u) * blkbytes;
-    const int64_t o1 = (int64_t)__builtin_amdgcn_readlane(ids, i1) * blkbytes;
-    const uint32_t l = __builtin_amdgcn_readfirstlane(lds_u32(mine + slot * NW * 2 * UB));
+    if constexpr (!ROWS) asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // the slot's earlier reads are done
+    const int b0 = ROWS ? min(2 * u + (RPW * w) / kBlock, nb - 1) : 2 * u;
+    const int64_t o0 = (int64_t)__builtin_amdgcn_readlane(ids, b0) * blkbytes;
+    const int64_t o1 = ROWS ? o0 : (int64_t)__builtin_amdgcn_readlane(ids, min(2 * u + 1, nb - 1)) * blkbytes;
+    const uint32_t l = __builtin_amdgcn_readfirstlane(lds_u32(wave_buf + slot * SLOT + (ROWS ? RPW * w * RB : 0)));
+    const char* kc = reinterpret_cast<const char*>(a.k_cache);
+    const char* vc = reinterpret_cast<const char*>(a.v_cache);
 #pragma unroll
-    for (int i = 0; i < IPB; ++i) {
-      dma16(kbase + o0, k_lane[i], l + 1024 * i);
-      dma16(kbase + o1, k_lane[i], l + kBlock * D + 1024 * i);
-    }
+    for (int i = 0; i < CPW; ++i) dma16(kc + (RPC * i < kBlock ? o0 : o1), k_lane[i], l + 1024 * i);
 #pragma unroll
-    for (int i = 0; i < IPB; ++i) {
-      dma16(vbase + o0, v_lane[0][i], l + UB + 1024 * i);
-      dma16(vbase + o1, v_lane[1][i], l + UB + kBlock * D + 1024 * i);
-    }
+    for (int i = 0; i < CPW; ++i) dma16(vc + (RPC * i < kBlock ? o0 : o1), v_lane[i], l + UB + 1024 * i);
   };
 
   // one unit; EDGE: it holds keys some column must not see -- past k1 or past a column's position
   // (the split's last units), or before a column's window (the first unit of split 0)
   auto consume = [&](auto edge_tag, int u, int slot) {
     constexpr bool EDGE = decltype(edge_tag)::value;
-    const char* kw = mine + slot * NW * 2 * UB;
+    const char* kw = wave_buf + slot * SLOT;
     uint4 kr[2 * KL];
 #pragma unroll
     for (int j = 0; j < KL; ++j) {
       kr[j] = *reinterpret_cast<const uint4*>(kw + k_rd[j]);
-      kr[KL + j] = *reinterpret_cast<const uint4*>(kw + kBlock * D + k_rd[j]);
+      kr[KL + j] = *reinterpret_cast<const uint4*>(kw + kBlock * RB + k_rd[j]);
     }
     floatx4 sA = floatx4{0.f, 0.f, 0.f, 0.f}, sB = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -328,24 +354,32 @@ __global__ __launch_bounds__(64 * NW, 2) void decode_i8_kernel(DecodeArgs a) {
     return base + 2 * kBlock > edge_hi || base < lo_max;
   };
 
-  // one unit in flight while the previous one is computed; the wait leaves exactly the next unit's
-  // NCP copies outstanding (vector memory operations complete in issue order)
+  // one unit in flight while the previous one is computed.  Per wave: the wait leaves exactly the
+  // next unit's NCP copies outstanding (vector memory operations complete in issue order).  Whole
+  // rows: the wait covers this wave's copies of unit u (and its Q loads), the barrier every wave's,
+  // and after it no wave still reads unit u - 1, whose slot the next copies fill.
   issue(0, 0);
-  load_q();
+  if (live) load_q();
   for (int u = 0; u < nu; ++u) {
-    if (u + 1 < nu) {
+    if constexpr (ROWS) {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
+      if (u + 1 < nu) issue(u + 1, (u + 1) & 1);
+    } else if (u + 1 < nu) {
       issue(u + 1, (u + 1) & 1);
       asm volatile("s_waitcnt vmcnt(%0)" :: "n"(NCP) : "memory");
     } else {
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     }
-    if (edge(u)) consume(Edge{}, u, u & 1);
-    else consume(Full{}, u, u & 1);
+    if (live) {
+      if (edge(u)) consume(Edge{}, u, u & 1);
+      else consume(Full{}, u, u & 1);
+    }
   }
   lsum = xor16_sum(lsum);
   lsum = xor32_sum(lsum);
 
-  if (on) {
+  if (on && live) {
     // O^T rows held by this lane are channels 16tt + 4grp + v: apply their V scale
     const float* vsp = a.v_scale + (int64_t)g * D + 4 * grp;
 #pragma unroll
@@ -381,21 +415,25 @@ __global__ __launch_bounds__(64 * NW, 2) void decode_i8_kernel(DecodeArgs a) {
 }
 
 namespace {
-template <int D, int NW>
+constexpr int kI8WholeRowBytes = 4096;      // cache token rows this wide or wider: whole-row staging
+
+template <int D, int NW, bool ROWS>
 hipError_t i8_dispatch(const DecodeArgs& a, hipStream_t s) {
   if (a.heads_per_wg < 1 || a.heads_per_wg > 16) return hipErrorInvalidValue;   // 16 MFMA columns
   const int64_t nzh = ((int64_t)a.qmax * a.group + a.heads_per_wg - 1) / a.heads_per_wg;
   const int64_t grid = (int64_t)((a.num_kv_heads + NW - 1) / NW) * nzh * a.max_splits * a.num_rows;
   if (grid <= 0 || grid > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
-  decode_i8_kernel<D, NW><<<dim3((unsigned)grid), dim3(64 * NW), 0, s>>>(a);
+  decode_i8_kernel<D, NW, ROWS><<<dim3((unsigned)grid), dim3(64 * NW), 0, s>>>(a);
   return hipGetLastError();
 }
 }  // namespace
 
-// Four waves per workgroup: eight (one workgroup per CU at this register count) measured slower.
+// Four waves per workgroup: eight (one workgroup per CU at this register count) measured slower,
+// with either staging form.  Whole-row staging where a cache token row holds 4 KiB or more.
 hipError_t launch_decode_split_i8(const DecodeArgs& a, int head_dim, hipStream_t s) {
-  if (head_dim == 128) return i8_dispatch<128, 4>(a, s);
-  if (head_dim == 64) return i8_dispatch<64, 4>(a, s);
+  const bool rows = (int64_t)a.num_kv_heads * head_dim >= kI8WholeRowBytes;
+  if (head_dim == 128) return rows ? i8_dispatch<128, 4, true>(a, s) : i8_dispatch<128, 4, false>(a, s);
+  if (head_dim == 64) return rows ? i8_dispatch<64, 4, true>(a, s) : i8_dispatch<64, 4, false>(a, s);
   return hipErrorInvalidValue;
 }
 

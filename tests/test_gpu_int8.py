@@ -48,6 +48,10 @@ CASES = [
     ([1030, 300], 24, 3, 128),
     ([4097, 9000], 64, 4, 128),
     ([2000, 33, 700], 64, 2, 128),          # 32 query heads per KV head
+    # cache rows of 4 KiB or more (KV heads x d codes) are staged as whole rows of four heads:
+    ([1, 15, 16, 17, 33, 700, 2500], 34, 34, 128),   # last head group holds two heads
+    ([1, 17, 48, 321, 1500], 64, 64, 64),
+    ([5, 260, 1100], 132, 66, 64),                   # d = 64, last group of two heads, 2 q-heads each
 ]
 
 
@@ -64,10 +68,17 @@ def test_int8_decode_with_window(window):
     run_i8(w, window=window, what=f"int8 W={window}")
 
 
-def test_int8_argmax_probe_bit_exact():
+@pytest.mark.parametrize("window", [1, 17, 1000])
+def test_int8_decode_with_window_whole_rows(window):
+    w = i8_batch(680 + window, [15, 16, 17, 600, 2000, 3001], 64, 32, 128)
+    run_i8(w, window=window, what=f"int8 whole rows W={window}")
+
+
+@pytest.mark.parametrize("Hq,Hkv", [(8, 2), (64, 32)])
+def test_int8_argmax_probe_bit_exact(Hq, Hkv):
     """Power-of-two scales make code * scale exact; with one dominant key per row the output is its
-    dequantised V row, bit for bit, after the split merge too."""
-    d, Hq, Hkv = 128, 8, 2
+    dequantised V row, bit for bit, after the split merge too (per-wave and whole-row staging)."""
+    d = 128
     lens = [67, 300, 1500, 16, 17]
     w = i8_batch(700, lens, Hq, Hkv, d)
     rng = np.random.default_rng(7)
@@ -103,8 +114,9 @@ def test_int8_argmax_probe_bit_exact():
         assert np.array_equal(out[b], expect), b
 
 
-def test_int8_repeat_runs_bitwise_identical():
-    w = i8_batch(710, [3000, 47, 900], 32, 8, 128)
+@pytest.mark.parametrize("Hkv", [8, 32])
+def test_int8_repeat_runs_bitwise_identical(Hkv):
+    w = i8_batch(710, [3000, 47, 900], 32, Hkv, 128)
     a = GpuState(w).step(w.steps[0])
     b = GpuState(w).step(w.steps[0])
     assert np.array_equal(a, b)
@@ -180,6 +192,8 @@ I8_VERIFY_CASES = [
     # those columns see no key of that split, whose partial must then carry no weight
     ([129, 257, 513, 40], [2, 4, 8, 3], 32, 8, 128, 0),
     ([1030, 260, 90], [1, 3, 90], 24, 3, 128, 0),              # verify rows beside a prefill
+    ([17, 300, 1000, 2049], [2, 8, 5, 1], 64, 32, 128, 0),     # whole-row staging, 2 heads per KV head
+    ([3000, 777, 64], [4, 8, 2], 64, 32, 128, 100),
 ]
 
 
