@@ -152,7 +152,7 @@ struct Plan {
   int head_dim = 0, group = 0, heads_per_wg = 0;
   bool run_decode = false, run_tiles = false;
   int rows = 0, per_token = 0, qmax = 1, split = 0, max_splits = 0;
-  bool stream = false;    // bf16 cache, rows of several positions: balanced runs instead of splits
+  bool stream = false;    // bf16 or int8 cache, rows of several positions: balanced runs, not splits
   int span_blocks = 0;    // most 16-key blocks one row's decode pass covers
   int pos_per_tile = 0, num_slots = 0;
   size_t off_o = 0, off_ml = 0, total = 0;
@@ -216,7 +216,7 @@ int make_plan(int32_t B, int32_t T, int32_t MB, int32_t Hq, const pa_cache_desc*
   // rows, longer merges); they are dealt out in balanced runs.  Plain decode rows measure best on
   // fixed splits, which the hardware schedules dynamically.
   p.split = split_tokens(span, bound, c->dtype == PA_DTYPE_I8);
-  p.stream = c->dtype == PA_DTYPE_BF16 && p.qmax > 1;
+  p.stream = (c->dtype == PA_DTYPE_BF16 || c->dtype == PA_DTYPE_I8) && p.qmax > 1;
   if (p.stream) {
     // a row meets at most ceil(blocks / run) + 1 runs, and runs hold at least `split` keys
     p.max_splits = (int)(((int64_t)p.span_blocks * PA_BLOCK_SIZE + p.split - 1) / p.split) + 1;
@@ -278,9 +278,11 @@ int chip_cus(int& cus) {
   return PA_OK;
 }
 
-// Stream-mode workgroups per two KV heads: the decode kernel keeps two workgroups resident per
-// compute unit, so two per CU over all head pairs make one full wave of the chip; never more than
-// the rows' blocks fill with runs of `split` keys.  PA_DECODE_WGS overrides the chip-wide count.
+// Stream-mode workgroups per head group (bf16: two KV heads, their column groups carried inside
+// the workgroup; int8: four KV heads and one column group): both decode kernels keep two workgroups
+// resident per compute unit, so two per CU over all head groups make one full wave of the chip;
+// never more than the rows' blocks fill with runs of `split` keys.  PA_DECODE_WGS overrides the
+// chip-wide count.
 int stream_wgs(const Plan& p, int num_kv_heads, int& out) {
   int cus = 0;
   int rc = chip_cus(cus);
@@ -289,7 +291,8 @@ int stream_wgs(const Plan& p, int num_kv_heads, int& out) {
     const char* e = std::getenv("PA_DECODE_WGS");
     return e ? std::atoi(e) : 0;
   }();
-  const int64_t nq = (num_kv_heads + 1) / 2;
+  const int64_t nzh = ((int64_t)p.qmax * p.group + p.heads_per_wg - 1) / p.heads_per_wg;
+  const int64_t nq = p.i8 ? (int64_t)((num_kv_heads + 3) / 4) * nzh : (num_kv_heads + 1) / 2;
   const int64_t chip = over > 0 ? over : 2 * (int64_t)cus;
   const int64_t fill = ((int64_t)p.rows * p.span_blocks * PA_BLOCK_SIZE + p.split - 1) / p.split;
   out = (int)std::max<int64_t>(1, std::min<int64_t>(std::max<int64_t>(1, chip / nq), fill));

@@ -129,18 +129,6 @@ __device__ __forceinline__ int kswz(int r) {
 }
 }
 
-namespace {
-// Lane i (active lanes only) loads p[i] and waits for it, in inline assembly: a load the compiler
-// sees inside the block loop makes it wait for every outstanding copy on every block thereafter.
-__device__ __forceinline__ int load_ids_sync(const int32_t* p, int count) {
-  int v = 0;
-  const int lane = threadIdx.x & (kWave - 1);
-  const int32_t* q = p + lane;
-  if (lane < count) asm volatile("global_load_dword %0, %1, off\n\ts_waitcnt vmcnt(0)" : "=v"(v) : "v"(q) : "memory");
-  return v;
-}
-}  // namespace
-
 // A row with more than 16 (position, head) columns (several tokens to verify on a grouped-query
 // model, or more than 16 query heads per KV head) carries two column groups of 16 through each pass
 // over the split's keys, so K and V are read once for 32 columns; the choice is made per workgroup

@@ -51,7 +51,7 @@ struct DecodeArgs {
   int max_blocks;
   int split;              // keys per split (stream mode: fewest keys per run)
   int max_splits;         // partial slots per (row, position, head): splits, or pieces in stream mode
-  int stream_wgs;         // > 0: stream mode with this many workgroups per two KV heads; 0: splits
+  int stream_wgs;         // > 0: stream mode with this many workgroups per head group; 0: splits
   int pair_wgs;           // bf16 split mode: 1 = workgroups of two KV heads, one wave per SIMD; 0 = four
   int window;             // keys a row sees, its own included (kNoWindow: all earlier keys)
   float scale_log2;       // scale * log2(e)

@@ -39,9 +39,10 @@ __device__ __forceinline__ int split_origin(const DecodeArgs& a, int n_keys, int
   return first_visible(a, n_keys - ql + 1) & ~(kBlock - 1);
 }
 
-// ---- stream mode (bf16 decode) ----
+// ---- stream mode (decode over a bf16 or int8 cache) ----
 // The 16-key blocks that the rows' passes cover, concatenated in row order, are dealt out in equal
-// runs of L blocks to stream_wgs workgroups per two KV heads.  A run may end one row and begin the
+// runs of L blocks to stream_wgs workgroups per head group (bf16: two KV heads; int8: four KV heads
+// and one column group).  A run may end one row and begin the
 // next; each (row, run) piece is a partial softmax of the row, like a split, and a row's pieces
 // are merged as splits are.  Every workgroup reads the same number of blocks, so the launch has
 // no tail of workgroups still running while the rest of the chip idles.
@@ -102,6 +103,16 @@ struct BlockCursor {
     return true;
   }
 };
+
+// Lane i (lanes below count) loads block id p[i] and waits for it, in inline assembly: a load the
+// compiler sees inside a block loop makes it wait for every outstanding copy on every block after.
+__device__ __forceinline__ int load_ids_sync(const int32_t* p, int count) {
+  int v = 0;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int32_t* q = p + lane;
+  if (lane < count) asm volatile("global_load_dword %0, %1, off\n\ts_waitcnt vmcnt(0)" : "=v"(v) : "v"(q) : "memory");
+  return v;
+}
 
 // Index of the split partial of (row, position r, split, query head h).
 __device__ __forceinline__ int64_t partial_index(const DecodeArgs& a, int row, int r, int split, int h) {

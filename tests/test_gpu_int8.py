@@ -194,6 +194,9 @@ I8_VERIFY_CASES = [
     ([1030, 260, 90], [1, 3, 90], 24, 3, 128, 0),              # verify rows beside a prefill
     ([17, 300, 1000, 2049], [2, 8, 5, 1], 64, 32, 128, 0),     # whole-row staging, 2 heads per KV head
     ([3000, 777, 64], [4, 8, 2], 64, 32, 128, 100),
+    # stream runs of more than 64 blocks (block ids taken 64 at a time), whole-row and per-wave
+    ([9000, 8000], [8, 8], 256, 32, 128, 0),
+    ([20000, 14000], [8, 5], 128, 8, 128, 0),
 ]
 
 
