@@ -197,6 +197,10 @@ I8_VERIFY_CASES = [
     # stream runs of more than 64 blocks (block ids taken 64 at a time), whole-row and per-wave
     ([9000, 8000], [8, 8], 256, 32, 128, 0),
     ([20000, 14000], [8, 5], 128, 8, 128, 0),
+    # whole-row stream runs at d = 64, and with a last head group of two heads
+    ([33, 500, 1200], [3, 8, 5], 128, 64, 64, 0),
+    ([3000, 777, 40], [4, 8, 2], 128, 64, 64, 100),
+    ([17, 900, 2100], [8, 2, 6], 68, 34, 128, 0),
 ]
 
 
